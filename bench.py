@@ -1,0 +1,302 @@
+"""Benchmark of the packed low-bit weight-quantized matmul hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over one batch of synthetic
+input, every leg on the current stream, each leg captured once into a HIP
+graph and replayed between HIP events:
+  decode   : 1000 x q2_0_gemv_vec, qkvz n=12288 k=2048 (m=1), the weight
+             rotated through 80 copies (537 MB > the 256 MB Infinity Cache) so
+             that every call streams its weight from HBM;
+  verify   : q2_0_gemv_vec_batchm chain gate -> up -> silu_mul -> down,
+             FFN [17408, 5120] / [5120, 17408], m in {2, 3, 4, 8};
+  prefill  : quantize_act_q8_1 + q2_0_mmq_gemm, qkvz n=12288 k=2048, m in
+             {512, 2048}; and the bf16 fallback (dequant + dense GEMM) at m=512;
+  ffn      : m=4096 FFN prefill, Q2_0 and Q4_K: quantize, gate and up MMQ,
+             silu_mul, quantize, down MMQ.
+The JSON line reports the decode GEMV (the workload the headline metric is
+quoted on) as `value`, with its roofline and the CPU oracle beside it; the
+other legs are reported under "legs".  Inputs are resident in HBM before the
+timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q2_0 MMQ prefill int8 TOPS + GEMV decode HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5033.0      # MI355X dense int8 MFMA, published (no sparsity)
+BF16_PEAK_TFLOPS = 2516.0    # MI355X dense bf16 MFMA, published
+
+DECODE_CALLS = 1000
+DECODE_COPIES = 80
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--legs", default="decode,verify,prefill,ffn")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Leg:
+    """A captured HIP graph plus its event timings.
+
+    `keep` holds every tensor the captured kernels touch: the graph stores raw
+    device pointers, and torch.cuda.graph() empties the allocator cache when a
+    later capture begins, so a tensor without a live reference would be
+    unmapped under an earlier graph."""
+
+    def __init__(self, name, fn, keep, launches, work, unit, kernel, peak, bound):
+        import torch
+        self.name, self.fn, self.keep, self.launches = name, fn, list(keep), launches
+        self.work, self.unit, self.kernel, self.peak, self.bound = work, unit, kernel, peak, bound
+        log(f"capture {name}")
+        fn()  # eager run first: argument errors surface here, outside capture
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(self.graph):
+            fn()
+        torch.cuda.synchronize()
+        self.ms = []
+
+    def run(self, timed):
+        import torch
+        if timed:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            self.graph.replay()
+            b.record()
+            self._pending = (a, b)
+        else:
+            self.graph.replay()
+
+    def collect(self):
+        a, b = self._pending
+        self.ms.append(a.elapsed_time(b))
+
+    def summary(self):
+        ms = float(np.mean(self.ms))
+        per_launch_us = ms * 1e3 / self.launches
+        rate = self.work / (ms * 1e-3)  # units per second
+        scale = 1e9 if self.unit == "GB/s" else 1e12
+        achieved = rate / scale
+        return dict(name=self.name, ms=round(ms, 4), us_per_launch=round(per_launch_us, 3),
+                    value=round(achieved, 2), unit=self.unit, kernel=self.kernel,
+                    frac_of_peak=round(achieved / self.peak, 4), bound=self.bound)
+
+
+def decode_leg(bq, dev, d):
+    """1000 m=1 GEMV calls, weight rotated through DECODE_COPIES copies."""
+    import torch
+    n, k = d["n"], d["k"]
+    w0 = torch.from_numpy(d["w"]).to(dev)
+    wcopies = [w0] + [w0.clone() for _ in range(DECODE_COPIES - 1)]
+    x = torch.from_numpy(d["act"][0].copy().view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((n,), dtype=torch.bfloat16, device=dev)
+
+    def fn():
+        for i in range(DECODE_CALLS):
+            bq.q2_0_gemv_vec(x, wcopies[i % DECODE_COPIES], y, n, k)
+
+    bytes_per_call = w0.numel() + 2 * k + 2 * n
+    leg = Leg("decode_gemv_m1", fn, wcopies + [x, y], DECODE_CALLS, DECODE_CALLS * bytes_per_call, "GB/s",
+              "q2_0_gemv_kernel<1>", HBM_PEAK_GBS, "hbm")
+    return leg, bytes_per_call
+
+
+def verify_leg(bq, dev, W, act, m, H, I):
+    import torch
+    wg, wu, wd = W
+    x = torch.from_numpy(np.ascontiguousarray(act[:m]).view(np.int16)).to(dev).view(torch.bfloat16)
+    g_ = torch.empty((m, I), dtype=torch.bfloat16, device=dev)
+    u_ = torch.empty((m, I), dtype=torch.bfloat16, device=dev)
+    o_ = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
+
+    def fn():
+        bq.q2_0_gemv_vec_batchm(x, wg, g_, m, I, H)
+        bq.q2_0_gemv_vec_batchm(x, wu, u_, m, I, H)
+        bq.silu_mul_bf16(g_, u_, g_, m * I)
+        bq.q2_0_gemv_vec_batchm(g_, wd, o_, m, H, I)
+
+    work = wg.numel() + wu.numel() + wd.numel() + m * (6 * H + 12 * I)
+    return Leg(f"verify_ffn_m{m}", fn, [wg, wu, wd, x, g_, u_, o_], 4, work, "GB/s",
+               f"q2_0_gemv_kernel<{m}> x3 + silu_mul", HBM_PEAK_GBS, "hbm")
+
+
+def prefill_legs(bq, dev, p):
+    import torch
+    n, k = p["n"], p["k"]
+    w = torch.from_numpy(p["w"]).to(dev)
+    legs = []
+    for m in (512, 2048):
+        x = torch.from_numpy(np.ascontiguousarray(p["act"][:m]).view(np.int16)).to(dev).view(torch.bfloat16)
+        q8 = torch.empty((bq.q8_1_act_bytes(m, k),), dtype=torch.uint8, device=dev)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        bq.quantize_act_q8_1(x, q8, m, k)
+        legs.append(Leg(f"prefill_mmq_m{m}", lambda m=m, q8=q8, y=y: bq.q2_0_mmq_gemm(q8, w, y, m, n, k),
+                        [w, q8, y], 1, 2.0 * m * n * k, "TOPS", "q2_0_mmq_kernel", INT8_PEAK_TOPS, "mfma"))
+        legs.append(Leg(f"prefill_quantize_m{m}", lambda m=m, x=x, q8=q8: bq.quantize_act_q8_1(x, q8, m, k),
+                        [x, q8], 1, 2 * m * k + bq.q8_1_act_bytes(m, k), "GB/s", "quantize_q8_1_kernel",
+                        HBM_PEAK_GBS, "hbm"))
+    m = 512
+    x = torch.from_numpy(np.ascontiguousarray(p["act"][:m]).view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    scratch = torch.empty((n * k,), dtype=torch.bfloat16, device=dev)
+    legs.append(Leg("fallback_dequant", lambda: bq.dequant_q2_0_to_bf16(w, scratch, n, k, 128), [w, scratch],
+                    1, w.numel() + 2 * n * k, "GB/s", "dequant_q2_0_kernel", HBM_PEAK_GBS, "hbm"))
+    legs.append(Leg("fallback_dense_gemm_m512", lambda: bq.dense_gemm_bf16(x, scratch, y, m, n, k),
+                    [x, scratch, y], 1, 2.0 * m * n * k, "TOPS", "dense_gemm_bf16_kernel", BF16_PEAK_TFLOPS,
+                    "mfma"))
+    return legs
+
+
+def ffn_legs(bq, dev, F):
+    import torch
+    H, I, m = F["hidden"], F["inter"], 4096
+    x = torch.from_numpy(np.ascontiguousarray(F["act"]).view(np.int16)).to(dev).view(torch.bfloat16)
+    q8a = torch.empty((bq.q8_1_act_bytes(m, H),), dtype=torch.uint8, device=dev)
+    q8h = torch.empty((bq.q8_1_act_bytes(m, I),), dtype=torch.uint8, device=dev)
+    gate = torch.empty((m, I), dtype=torch.bfloat16, device=dev)
+    up = torch.empty((m, I), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
+    legs = []
+    for fmt, key, gemm, kname in (("q2_0", "q2", bq.q2_0_mmq_gemm, "q2_0_mmq_kernel"),
+                                  ("q4k", "q4k", bq.q4k_mmq_gemm, "q4k_mmq_kernel")):
+        wg, wu, wd = (torch.from_numpy(F[key][name]).to(dev) for name in ("wg", "wu", "wd"))
+
+        def ffn(wg=wg, wu=wu, wd=wd, gemm=gemm):
+            bq.quantize_act_q8_1(x, q8a, m, H)
+            gemm(q8a, wg, gate, m, I, H)
+            gemm(q8a, wu, up, m, I, H)
+            bq.silu_mul_bf16(gate, up, gate, m * I)
+            bq.quantize_act_q8_1(gate, q8h, m, I)
+            gemm(q8h, wd, out, m, H, I)
+
+        keep = [wg, wu, wd, x, q8a, q8h, gate, up, out]
+        legs.append(Leg(f"ffn_prefill_{fmt}_m4096", ffn, keep, 6, 3 * 2.0 * m * H * I, "TOPS",
+                        f"{kname} x3 + quantize x2 + silu_mul", INT8_PEAK_TOPS, "mfma"))
+        legs.append(Leg(f"ffn_gate_proj_{fmt}_m4096", lambda wg=wg, gemm=gemm: gemm(q8a, wg, gate, m, I, H),
+                        keep, 1, 2.0 * m * H * I, "TOPS", kname, INT8_PEAK_TOPS, "mfma"))
+    return legs
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the path has no inter-GPU "
+                          "sharding (--gpus must be 1)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import bit_quantized_matmul_quantize_amd as bq
+    import inputs
+
+    dev = torch.device("cuda:0")
+    legs_wanted = set(args.legs.split(","))
+    legs = []
+    decode_ctx = None
+    if "decode" in legs_wanted:
+        d = inputs.decode_gemv()
+        leg, bpc = decode_leg(bq, dev, d)
+        legs.append(leg)
+        decode_ctx = dict(d=d, bytes_per_call=bpc)
+    if "verify" in legs_wanted:
+        f = inputs.verify_ffn()
+        W = tuple(torch.from_numpy(f[key]).to(dev) for key in ("wg", "wu", "wd"))
+        for m in (2, 3, 4, 8):
+            legs.append(verify_leg(bq, dev, W, f["act"], m, f["hidden"], f["inter"]))
+    if "prefill" in legs_wanted:
+        legs += prefill_legs(bq, dev, inputs.prefill_qkvz())
+    if "ffn" in legs_wanted:
+        legs += ffn_legs(bq, dev, inputs.prefill_ffn())
+
+    # ---- timed region ----------------------------------------------------------
+    log(f"{len(legs)} legs captured; warmup {args.warmup}, steps {args.steps}")
+    for _ in range(args.warmup):
+        for leg in legs:
+            leg.run(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for step in range(args.steps):
+        for leg in legs:
+            leg.run(True)
+        torch.cuda.synchronize()
+        for leg in legs:
+            leg.collect()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    summaries = {leg.name: leg.summary() for leg in legs}
+    for s in summaries.values():
+        log(f"{s['name']:28s} {s['ms']:9.4f} ms  {s['value']:9.2f} {s['unit']:5s} "
+            f"({100 * s['frac_of_peak']:.1f}% of peak, {s['us_per_launch']:.2f} us/launch)")
+
+    result = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+              "config": {"workload": "decode GEMV m=1: Q2_0 qkvz n=12288 k=2048 group 128, 1000 calls per "
+                                     "step, weight rotated through 80 copies (537 MB) so each call reads HBM",
+                         "step": sorted(summaries)}}
+    if "decode_gemv_m1" in summaries:
+        s = summaries["decode_gemv_m1"]
+        result["value"] = s["value"]
+        result["roofline"] = {"bound": "hbm", "achieved": s["value"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": s["frac_of_peak"], "traffic": None,
+                              "kernel": s["kernel"], "us_per_launch": s["us_per_launch"],
+                              "bytes_per_launch": decode_ctx["bytes_per_call"]}
+    if "prefill_mmq_m2048" in summaries:
+        s = summaries["prefill_mmq_m2048"]
+        result["prefill"] = {"metric": "Q2_0 MMQ prefill int8 TOPS (2mnk / kernel time), m=2048 n=12288 k=2048",
+                             "value": s["value"], "unit": "TOPS", "dtype": "i8",
+                             "roofline": {"bound": "mfma", "achieved": s["value"], "peak": INT8_PEAK_TOPS,
+                                          "unit": "TOP/s", "frac": s["frac_of_peak"], "traffic": None}}
+    result["legs"] = summaries
+
+    # ---- CPU oracle baseline (rank 0, N = 1) -----------------------------------
+    if not args.no_cpu_baseline and "decode_gemv_m1" in summaries:
+        import oracle
+        d = decode_ctx["d"]
+        try:
+            os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+        except Exception:
+            pass
+        calls, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and calls < 200:
+            t1 = time.perf_counter()
+            oracle.q2_0_gemv(d["act"], d["w"], 1, d["n"], d["k"])
+            t_cpu += time.perf_counter() - t1
+            calls += 1
+        cpu_gbs = calls * decode_ctx["bytes_per_call"] / t_cpu / 1e9
+        result["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"{calls} decode GEMV calls (n=12288, k=2048) of the oracle, "
+                                            f"{t_cpu:.1f} s on one pinned host core of {os.cpu_count()}"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,66 @@
+"""Build libbqmm.so in-tree with hipcc for gfx950 only.
+
+    python -m bit_quantized_matmul_quantize_amd.build
+
+Each HIP source compiles to its own object (in parallel), then one shared
+library is linked next to this file.  Flags: -O3, IEEE-correct binary32
+division (the q8_1 codes depend on it), no fast-math, and packed-FP32
+instruction selection turned off.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libbqmm.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = ["quantize.hip", "elementwise.hip", "gemv.hip", "mmq_q2.hip", "mmq_q4k.hip",
+           "gemm_bf16.hip", "capi.cpp"]
+
+COMMON = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(HERE, "..", "include"),
+]
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *COMMON]
+        if src.endswith(".cpp"):
+            cmd += ["-x", "hip"]
+        cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
+    failed = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        text = "\n".join(l for l in out.decode(errors="replace").splitlines()
+                         if "packed-fp32-ops" not in l)
+        if p.returncode != 0:
+            failed.append(src)
+            sys.stderr.write(text + "\n")
+        elif verbose and text.strip():
+            print(text)
+    if failed:
+        raise RuntimeError("hipcc failed for: " + ", ".join(failed))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,57 @@
+// Internal declarations shared by the kernel sources and the C ABI layer.
+// gfx950 (CDNA4) only: wave64, int8/bf16 matrix cores, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bqmm {
+
+// ---- device helpers ------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// binary32 -> bfloat16 bits, round to nearest even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// binary32 -> binary16 bits, round to nearest even (v_cvt_f16_f32).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// ---- launchers (one per kernel source) ------------------------------------
+// Arguments are validated by the C ABI layer before these are called.
+
+hipError_t launch_quantize_act_q8_1(const void *act, void *out, uint32_t m, uint32_t k,
+                                    hipStream_t s);
+hipError_t launch_dequant_q2_0(const void *w, void *out, uint32_t n, uint32_t k, uint32_t group,
+                               hipStream_t s);
+hipError_t launch_silu_mul(const void *gate, const void *up, void *out, uint64_t count,
+                           hipStream_t s);
+hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
+                            uint32_t k, hipStream_t s);
+hipError_t launch_q2_0_mmq(const void *act_q8, const void *w, void *out, int32_t *dots,
+                           uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m,
+                           uint32_t n, uint32_t k, hipStream_t s);
+hipError_t launch_q4k_mmq(const void *act_q8, const void *w, void *out, int32_t *dots,
+                          uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m,
+                          uint32_t n, uint32_t k, hipStream_t s);
+hipError_t launch_dense_gemm_bf16(const void *a, const void *w, void *out, uint32_t m, uint32_t n,
+                                  uint32_t k, hipStream_t s);
+
+}  // namespace bqmm

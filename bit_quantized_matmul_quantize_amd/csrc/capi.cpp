@@ -1,0 +1,240 @@
+// The C ABI: argument checks, then one launch (or two, for the dispatcher) on
+// the caller's stream.  Every check runs before any HIP call.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/bqmm.h"
+#include "bqmm_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(BQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return BQ_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0u; }
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+constexpr uint32_t kMaxGridY = 65535u;
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *bq_last_error(void) { return g_last_error; }
+
+const char *bq_status_string(int status) {
+  switch (status) {
+    case BQ_OK: return "ok";
+    case BQ_EINVAL: return "invalid argument";
+    case BQ_EUNSUPPORTED: return "unsupported configuration";
+    case BQ_EALIGN: return "pointer not 16-byte aligned";
+    case BQ_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+uint64_t q8_1_act_bytes(uint32_t m, uint32_t k) {
+  const uint64_t kpad = ((uint64_t)k + 255u) / 256u * 256u;
+  return (uint64_t)m * kpad + (uint64_t)m * (kpad / 32u) * 4u;
+}
+
+uint64_t q2_0_weight_bytes(uint32_t n, uint32_t k, uint32_t group) {
+  if (group == 0 || group % 32u != 0 || k % group != 0) return 0;
+  return (uint64_t)n * k / 4u + 2u * (uint64_t)n * (k / group);
+}
+
+uint64_t q4k_weight_bytes(uint32_t n, uint32_t k) {
+  if (k % 256u != 0) return 0;
+  return (uint64_t)n * (k / 256u) * 144u;
+}
+
+int quantize_act_q8_1(const void *act_bf16, void *out_q8, uint32_t m, uint32_t k, void *stream) {
+  REQUIRE(act_bf16 && out_q8, BQ_EINVAL, "quantize_act_q8_1: null pointer");
+  REQUIRE(m >= 1 && k >= 1, BQ_EINVAL, "quantize_act_q8_1: m=%u k=%u must be >= 1", m, k);
+  REQUIRE(aligned16(act_bf16) && aligned16(out_q8), BQ_EALIGN, "quantize_act_q8_1: buffers must be 16-byte aligned");
+  const uint64_t kpad = ((uint64_t)k + 255u) / 256u * 256u;
+  const uint64_t blocks = (uint64_t)m * ((kpad + 2047u) / 2048u);
+  REQUIRE(blocks < (1ull << 31), BQ_EINVAL, "quantize_act_q8_1: m*k too large");
+  return hip_status(bqmm::launch_quantize_act_q8_1(act_bf16, out_q8, m, k, as_stream(stream)),
+                    "quantize_act_q8_1");
+}
+
+static int check_mmq(const char *name, const void *act_q8, const void *w, const void *out,
+                     uint32_t m, uint32_t n, uint32_t k, uint32_t kmult) {
+  REQUIRE(act_q8 && w && out, BQ_EINVAL, "%s: null pointer", name);
+  REQUIRE(m >= 1 && n >= 1 && k >= 1, BQ_EINVAL, "%s: m=%u n=%u k=%u must be >= 1", name, m, n, k);
+  REQUIRE(k % kmult == 0, BQ_EINVAL, "%s: k=%u must be a multiple of %u", name, k, kmult);
+  REQUIRE(aligned16(act_q8) && aligned16(w) && aligned16(out), BQ_EALIGN, "%s: buffers must be 16-byte aligned", name);
+  REQUIRE((m + 127u) / 128u <= kMaxGridY, BQ_EINVAL, "%s: m=%u too large", name, m);
+  return BQ_OK;
+}
+
+int q2_0_mmq_gemm(const void *act_q8, const void *w_q2, void *out_bf16, uint32_t m, uint32_t n,
+                  uint32_t k, void *stream) {
+  const int st = check_mmq("q2_0_mmq_gemm", act_q8, w_q2, out_bf16, m, n, k, 128u);
+  if (st != BQ_OK) return st;
+  return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, out_bf16, nullptr, 0, 0, 0, 0, m, n, k,
+                                          as_stream(stream)),
+                    "q2_0_mmq_gemm");
+}
+
+int q4k_mmq_gemm(const void *act_q8, const void *w_q4k, void *out_bf16, uint32_t m, uint32_t n,
+                 uint32_t k, void *stream) {
+  const int st = check_mmq("q4k_mmq_gemm", act_q8, w_q4k, out_bf16, m, n, k, 256u);
+  if (st != BQ_OK) return st;
+  return hip_status(bqmm::launch_q4k_mmq(act_q8, w_q4k, out_bf16, nullptr, 0, 0, 0, 0, m, n, k,
+                                         as_stream(stream)),
+                    "q4k_mmq_gemm");
+}
+
+static int check_blockdots(const char *name, const void *act_q8, const void *w, const int32_t *out,
+                           uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m, uint32_t n,
+                           uint32_t k, uint32_t kmult) {
+  const int st = check_mmq(name, act_q8, w, out, m, n, k, kmult);
+  if (st != BQ_OK) return st;
+  REQUIRE(mt >= 1 && nt >= 1, BQ_EINVAL, "%s: empty window", name);
+  REQUIRE((uint64_t)m0 + mt <= m && (uint64_t)n0 + nt <= n, BQ_EINVAL,
+          "%s: window [%u,+%u) x [%u,+%u) outside [0,%u) x [0,%u)", name, m0, mt, n0, nt, m, n);
+  return BQ_OK;
+}
+
+int q2_0_mmq_blockdots(const void *act_q8, const void *w_q2, int32_t *out, uint32_t m0, uint32_t mt,
+                       uint32_t n0, uint32_t nt, uint32_t m, uint32_t n, uint32_t k, void *stream) {
+  const int st = check_blockdots("q2_0_mmq_blockdots", act_q8, w_q2, out, m0, mt, n0, nt, m, n, k, 128u);
+  if (st != BQ_OK) return st;
+  return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, nullptr, out, m0, mt, n0, nt, m, n, k,
+                                          as_stream(stream)),
+                    "q2_0_mmq_blockdots");
+}
+
+int q4k_mmq_blockdots(const void *act_q8, const void *w_q4k, int32_t *out, uint32_t m0, uint32_t mt,
+                      uint32_t n0, uint32_t nt, uint32_t m, uint32_t n, uint32_t k, void *stream) {
+  const int st = check_blockdots("q4k_mmq_blockdots", act_q8, w_q4k, out, m0, mt, n0, nt, m, n, k, 256u);
+  if (st != BQ_OK) return st;
+  return hip_status(bqmm::launch_q4k_mmq(act_q8, w_q4k, nullptr, out, m0, mt, n0, nt, m, n, k,
+                                         as_stream(stream)),
+                    "q4k_mmq_blockdots");
+}
+
+static int check_gemv(const char *name, const void *act, const void *w, const void *out, uint32_t m,
+                      uint32_t n, uint32_t k) {
+  REQUIRE(act && w && out, BQ_EINVAL, "%s: null pointer", name);
+  REQUIRE(n >= 1 && k >= 1, BQ_EINVAL, "%s: n=%u k=%u must be >= 1", name, n, k);
+  REQUIRE(k % 128u == 0, BQ_EINVAL, "%s: k=%u must be a multiple of the group size 128", name, k);
+  REQUIRE(m >= 1, BQ_EINVAL, "%s: m must be >= 1", name);
+  REQUIRE(m <= 8, BQ_EUNSUPPORTED, "%s: m=%u > 8 (use the MMQ path)", name, m);
+  REQUIRE(aligned16(act) && aligned16(w) && aligned16(out), BQ_EALIGN, "%s: buffers must be 16-byte aligned", name);
+  return BQ_OK;
+}
+
+int q2_0_gemv_vec(const void *act_bf16, const void *w_q2, void *out_bf16, uint32_t n, uint32_t k,
+                  void *stream) {
+  const int st = check_gemv("q2_0_gemv_vec", act_bf16, w_q2, out_bf16, 1, n, k);
+  if (st != BQ_OK) return st;
+  return hip_status(bqmm::launch_q2_0_gemv(act_bf16, w_q2, out_bf16, 1, n, k, as_stream(stream)),
+                    "q2_0_gemv_vec");
+}
+
+int q2_0_gemv_vec_batchm(const void *act_bf16, const void *w_q2, void *out_bf16, uint32_t m,
+                         uint32_t n, uint32_t k, void *stream) {
+  const int st = check_gemv("q2_0_gemv_vec_batchm", act_bf16, w_q2, out_bf16, m, n, k);
+  if (st != BQ_OK) return st;
+  return hip_status(bqmm::launch_q2_0_gemv(act_bf16, w_q2, out_bf16, m, n, k, as_stream(stream)),
+                    "q2_0_gemv_vec_batchm");
+}
+
+static int check_dequant(const void *w, const void *out, uint32_t n, uint32_t k, uint32_t group) {
+  REQUIRE(w && out, BQ_EINVAL, "dequant_q2_0_to_bf16: null pointer");
+  REQUIRE(n >= 1 && k >= 1, BQ_EINVAL, "dequant_q2_0_to_bf16: n=%u k=%u must be >= 1", n, k);
+  REQUIRE(group >= 32u && group % 32u == 0, BQ_EUNSUPPORTED,
+          "dequant_q2_0_to_bf16: group=%u must be a positive multiple of 32", group);
+  REQUIRE(k % group == 0, BQ_EINVAL, "dequant_q2_0_to_bf16: k=%u not a multiple of group=%u", k, group);
+  REQUIRE(aligned16(w) && aligned16(out), BQ_EALIGN, "dequant_q2_0_to_bf16: buffers must be 16-byte aligned");
+  return BQ_OK;
+}
+
+int dequant_q2_0_to_bf16(const void *w_q2, void *out_bf16, uint32_t n, uint32_t k, uint32_t group,
+                         void *stream) {
+  const int st = check_dequant(w_q2, out_bf16, n, k, group);
+  if (st != BQ_OK) return st;
+  return hip_status(bqmm::launch_dequant_q2_0(w_q2, out_bf16, n, k, group, as_stream(stream)),
+                    "dequant_q2_0_to_bf16");
+}
+
+static int check_dense(const void *a, const void *w, const void *out, uint32_t m, uint32_t n, uint32_t k) {
+  REQUIRE(a && w && out, BQ_EINVAL, "dense_gemm_bf16: null pointer");
+  REQUIRE(m >= 1 && n >= 1 && k >= 1, BQ_EINVAL, "dense_gemm_bf16: m=%u n=%u k=%u must be >= 1", m, n, k);
+  REQUIRE(k % 64u == 0, BQ_EINVAL, "dense_gemm_bf16: k=%u must be a multiple of 64", k);
+  REQUIRE(aligned16(a) && aligned16(w) && aligned16(out), BQ_EALIGN, "dense_gemm_bf16: buffers must be 16-byte aligned");
+  REQUIRE((m + 127u) / 128u <= kMaxGridY, BQ_EINVAL, "dense_gemm_bf16: m=%u too large", m);
+  return BQ_OK;
+}
+
+int dense_gemm_bf16(const void *a_bf16, const void *w_bf16, void *out_bf16, uint32_t m, uint32_t n,
+                    uint32_t k, void *stream) {
+  const int st = check_dense(a_bf16, w_bf16, out_bf16, m, n, k);
+  if (st != BQ_OK) return st;
+  return hip_status(bqmm::launch_dense_gemm_bf16(a_bf16, w_bf16, out_bf16, m, n, k, as_stream(stream)),
+                    "dense_gemm_bf16");
+}
+
+int q2_0_prefill_gemm(const void *act_bf16, const void *w_q2, void *out_bf16, void *scratch_bf16,
+                      void *act_q8, uint32_t m, uint32_t n, uint32_t k, uint32_t group, int use_mmq,
+                      void *stream) {
+  REQUIRE(act_bf16 && w_q2 && out_bf16, BQ_EINVAL, "q2_0_prefill_gemm: null input, weight or output");
+  if (use_mmq && group == 128u) {
+    REQUIRE(act_q8, BQ_EINVAL, "q2_0_prefill_gemm: MMQ branch needs the act_q8 buffer");
+    REQUIRE(m >= 1 && k >= 1, BQ_EINVAL, "q2_0_prefill_gemm: m=%u k=%u must be >= 1", m, k);
+    REQUIRE(aligned16(act_bf16), BQ_EALIGN, "q2_0_prefill_gemm: input must be 16-byte aligned");
+    int st = check_mmq("q2_0_prefill_gemm", act_q8, w_q2, out_bf16, m, n, k, 128u);
+    if (st != BQ_OK) return st;
+    st = hip_status(bqmm::launch_quantize_act_q8_1(act_bf16, act_q8, m, k, as_stream(stream)),
+                    "q2_0_prefill_gemm (quantize)");
+    if (st != BQ_OK) return st;
+    return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, out_bf16, nullptr, 0, 0, 0, 0, m, n, k,
+                                            as_stream(stream)),
+                      "q2_0_prefill_gemm (mmq)");
+  }
+  REQUIRE(scratch_bf16, BQ_EINVAL, "q2_0_prefill_gemm: dequant branch needs the bf16 scratch buffer");
+  int st = check_dequant(w_q2, scratch_bf16, n, k, group);
+  if (st != BQ_OK) return st;
+  st = check_dense(act_bf16, scratch_bf16, out_bf16, m, n, k);
+  if (st != BQ_OK) return st;
+  st = hip_status(bqmm::launch_dequant_q2_0(w_q2, scratch_bf16, n, k, group, as_stream(stream)),
+                  "q2_0_prefill_gemm (dequant)");
+  if (st != BQ_OK) return st;
+  return hip_status(bqmm::launch_dense_gemm_bf16(act_bf16, scratch_bf16, out_bf16, m, n, k,
+                                                 as_stream(stream)),
+                    "q2_0_prefill_gemm (dense gemm)");
+}
+
+int silu_mul_bf16(const void *gate, const void *up, void *out, uint64_t count, void *stream) {
+  REQUIRE(gate && up && out, BQ_EINVAL, "silu_mul_bf16: null pointer");
+  REQUIRE(count >= 1, BQ_EINVAL, "silu_mul_bf16: count must be >= 1");
+  REQUIRE(((reinterpret_cast<uintptr_t>(gate) | reinterpret_cast<uintptr_t>(up) |
+            reinterpret_cast<uintptr_t>(out)) & 1u) == 0u,
+          BQ_EALIGN, "silu_mul_bf16: bf16 buffers must be 2-byte aligned");
+  return hip_status(bqmm::launch_silu_mul(gate, up, out, count, as_stream(stream)), "silu_mul_bf16");
+}
+
+}  // extern "C"

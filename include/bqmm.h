@@ -1,0 +1,183 @@
+/*
+ * bqmm -- packed low-bit weight-quantized matmul for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every entry point takes plain pointers and sizes; device pointers
+ * unless stated otherwise.  `stream` is a hipStream_t passed as void*; NULL
+ * means the legacy default stream.  Every call enqueues its kernels on that
+ * stream and returns without synchronizing: errors raised while the kernels
+ * run surface at the caller's next synchronization.  No call allocates,
+ * frees or synchronizes; all buffers belong to the caller (the reference
+ * dispatcher passes its scratch and q8_1 buffers in and "allocates nothing":
+ * page layers/qwen3_ssm/init_q2.rs, fn qkvz_q2_prefill_gemm).
+ *
+ * Errors are values, never aborts (the reference returns an error carrying a
+ * message when a kernel or weight is missing: page
+ * layers/dense_ffn_decode_batch.rs, fn forward_km_q2).  Every argument is
+ * checked before any HIP call, so a rejected call touches no device state.
+ * The message of the last failure on the calling thread is bq_last_error().
+ *
+ * Byte layouts (all little-endian; fp16 = IEEE binary16; bf16 = bfloat16):
+ *
+ *   q8_1 activations for [m][k], kpad = ceil(k/256)*256:
+ *     codes plane, int8 [m][kpad] at byte 0; then the (d, s) plane: for row r
+ *     and 32-value block b, fp16 d at byte m*kpad + 4*(r*kpad/32 + b) and
+ *     fp16 s at +2.  d = fp16(amax/127) (binary32 division), q =
+ *     clamp(roundf(x/d), -127, 127) using the stored d (binary32 division,
+ *     ties away from zero), s = fp16(d * sum q); padding values are zero.
+ *     Total q8_1_act_bytes(m, k) = 1.125*m*kpad bytes.
+ *
+ *   Q2_0 weight [n][k], group G (G = 128 for the matmul kernels):
+ *     codes plane, n*k/4 bytes at byte 0: row r, group g occupies bytes
+ *     [r*k/4 + g*G/4, +G/4); byte t of a group holds the 2-bit codes of
+ *     k-offsets t + j*G/4 in bits [2j, 2j+1], j = 0..3.  Then the scale
+ *     plane: fp16 d[r][g] at byte n*k/4 + 2*(r*k/G + g).  Weight value
+ *     w = d*(c - 2), c in {0,1,2,3}.  Total q2_0_weight_bytes(n, k, G).
+ *
+ *   Q4_K weight [n][k]: row-major [n][k/256] super-blocks of 144 bytes:
+ *     fp16 d (bytes 0-1), fp16 dmin (2-3), twelve bytes S of packed 6-bit
+ *     sub-scales/mins (4-15), 128 bytes of 4-bit codes (16-143).  Sub-block
+ *     j (32 weights): j < 4: sc = S[j] & 63, m = S[j+4] & 63; j >= 4:
+ *     sc = (S[j+4] & 15) | ((S[j-4] >> 6) << 4), m = (S[j+4] >> 4) | ((S[j] >> 6) << 4).
+ *     Byte 16 + 32t + i holds weight 64t+i (low nibble) and 64t+32+i (high
+ *     nibble).  w = d*sc_j*q - dmin*m_j.  256 weights in 144 bytes as on page
+ *     layers/ops/q4k_mmq.rs (consts QK_K, Q4K_BLOCK_BYTES).
+ *
+ * Alignment: weight, activation and q8_1 pointers must be 16-byte aligned
+ * (BQ_EALIGN otherwise); bf16 row lengths used by vector loads are noted per
+ * call.  Inputs and outputs must not overlap unless a call says so.
+ *
+ * Only a gfx950 code object is built; on other devices calls fail with
+ * BQ_EHIP.  The library keeps no mutable state besides the per-thread error
+ * message; calls from different threads are independent.
+ */
+#ifndef BQMM_H
+#define BQMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define BQ_OK 0
+#define BQ_EINVAL (-1)       /* null pointer, zero size, shape rule broken, overflow */
+#define BQ_EUNSUPPORTED (-2) /* valid in principle but not provided (group, m > 8) */
+#define BQ_EALIGN (-3)       /* pointer not 16-byte aligned */
+#define BQ_EHIP (-4)         /* a HIP launch failed; the HIP message is in bq_last_error() */
+
+/* Message of the last failing call on this thread ("" if none).  Host; the
+ * string stays valid until the next call on the same thread. */
+const char *bq_last_error(void);
+/* Fixed description of a status code.  Host. */
+const char *bq_status_string(int status);
+
+/* ---- sizes (host) ------------------------------------------------------- */
+
+/* Bytes of the q8_1 form of [m][k]: 1.125*m*kpad, kpad = ceil(k/256)*256.
+ * The reference sizes its q8_1 scratch with k rounded up to 256 (page
+ * layers/ops/q4k_mmq.rs, fn q8_1_scratch_bytes); its 4 bytes per value plus
+ * 1 MiB over-allocates this exact size and may still be passed.  0 on overflow. */
+uint64_t q8_1_act_bytes(uint32_t m, uint32_t k);
+
+/* Bytes of a Q2_0 weight [n][k] with group `group`: n*k/4 + 2*n*k/group.
+ * 0 if k % group != 0, group % 32 != 0 or on overflow. */
+uint64_t q2_0_weight_bytes(uint32_t n, uint32_t k, uint32_t group);
+
+/* Bytes of a Q4_K weight [n][k]: n*(k/256)*144 (page layers/ops/q4k_mmq.rs,
+ * fn q4k_weight_bytes).  0 if k % 256 != 0 or on overflow. */
+uint64_t q4k_weight_bytes(uint32_t n, uint32_t k);
+
+/* ---- the hot path -------------------------------------------------------- */
+
+/* bf16 activations [m][k] (row-major, contiguous) -> q8_1 in out_q8
+ * (q8_1_act_bytes(m, k) bytes, layout above).
+ * [page layers/ops/q4k_mmq.rs, fn quantize_act_q8_1: bf16 in, q8_1 out, k
+ *  padded to 256.]  m >= 1, k >= 1.  act_bf16 and out_q8 16-byte aligned. */
+int quantize_act_q8_1(const void *act_bf16, void *out_q8, uint32_t m, uint32_t k, void *stream);
+
+/* Q2_0 MMQ: out[m][n] (bf16, row-major, row stride n) =
+ *   sum_k deq(act_q8)[m][k] * deq(w_q2)[n][k],
+ * on int8 matrix cores with exact int32 block dot products; scales applied
+ * in fp32.  [page layers/qwen3_ssm/init_q2.rs, fn qkvz_q2_prefill_gemm:
+ *  out[m, n] = input[m, k] @ W^T via quantize_act_q8_1 then q2_0_mmq_gemm,
+ *  group 128 only.]
+ * act_q8: q8_1 of [m][k]; w_q2: Q2_0 [n][k] with group 128.  k % 128 == 0,
+ * m, n >= 1 (any n: tails handled inside). */
+int q2_0_mmq_gemm(const void *act_q8, const void *w_q2, void *out_bf16,
+                  uint32_t m, uint32_t n, uint32_t k, void *stream);
+
+/* Q2_0 decode GEMV, one row: out[n] (bf16) = sum_k act[k] * deq(w_q2)[n][k],
+ * on the unquantized bf16 activation, fp32 accumulation.
+ * [page layers/qwen3_ssm/init.rs, kernel q2_0_gemv_vec; page
+ *  layers/qwen3_ssm/init_q2.rs, fn set_packed_q2_qkvz: decode runs the GEMV
+ *  on the packed qkvz.]  Group 128; k % 128 == 0; n >= 1. */
+int q2_0_gemv_vec(const void *act_bf16, const void *w_q2, void *out_bf16,
+                  uint32_t n, uint32_t k, void *stream);
+
+/* Q2_0 GEMV for m = 1..8 rows (small verify batches): act [m][k] bf16,
+ * out [m][n] bf16.  [page layers/dense_ffn_decode_batch.rs, fn forward_km_q2:
+ *  q2_0_gemv_vec_batchm(inp, w, out, m).]  m > 8 -> BQ_EUNSUPPORTED.
+ * Group 128; k % 128 == 0. */
+int q2_0_gemv_vec_batchm(const void *act_bf16, const void *w_q2, void *out_bf16,
+                         uint32_t m, uint32_t n, uint32_t k, void *stream);
+
+/* Q2_0 weight -> bf16 [n][k]: bf16_rne(d*(c - 2)) (exact product, one
+ * rounding).  [page layers/qwen3_ssm/init_q2.rs, fn qkvz_q2_prefill_gemm,
+ *  fallback: dequant_q2_0_gn_to_bf16(w, scratch, n, k, group).]
+ * group % 32 == 0 and k % group == 0. */
+int dequant_q2_0_to_bf16(const void *w_q2, void *out_bf16, uint32_t n, uint32_t k,
+                         uint32_t group, void *stream);
+
+/* Dense bf16 GEMM: out[m][n] (bf16) = sum_k a[m][k] * w[n][k], fp32
+ * accumulation.  [page layers/qwen3_ssm/init_q2.rs, fn qkvz_q2_prefill_gemm,
+ *  fallback: dense_gemm_bf16_pipelined on the original bf16 input.]
+ * k % 64 == 0; m, n >= 1. */
+int dense_gemm_bf16(const void *a_bf16, const void *w_bf16, void *out_bf16,
+                    uint32_t m, uint32_t n, uint32_t k, void *stream);
+
+/* Prefill dispatcher.  With use_mmq != 0 and group == 128: quantize act_bf16
+ * into act_q8 (q8_1_act_bytes(m, k) bytes) and run q2_0_mmq_gemm.  Otherwise
+ * dequantize the weight into scratch_bf16 (n*k*2 bytes) and run
+ * dense_gemm_bf16 on the original bf16 input.  Both on `stream`.
+ * [page layers/qwen3_ssm/init_q2.rs, fn qkvz_q2_prefill_gemm.]  The buffer
+ * the chosen branch does not use may be NULL. */
+int q2_0_prefill_gemm(const void *act_bf16, const void *w_q2, void *out_bf16,
+                      void *scratch_bf16, void *act_q8, uint32_t m, uint32_t n, uint32_t k,
+                      uint32_t group, int use_mmq, void *stream);
+
+/* Q4_K MMQ: out[m][n] (bf16) = sum_k deq(act_q8)[m][k] * deq_q4k(w)[n][k].
+ * [page layers/ops/q4k_mmq.rs, fn q4k_mmq_gemm: C[m, n] = A[m, k] x W[n, k],
+ *  A in q8_1, W in block_q4_K, BF16 store; any n.]  k % 256 == 0. */
+int q4k_mmq_gemm(const void *act_q8, const void *w_q4k, void *out_bf16,
+                 uint32_t m, uint32_t n, uint32_t k, void *stream);
+
+/* out[i] = bf16_rne(silu(gate[i]) * up[i]) for i < count, silu(g) =
+ * g/(1+exp(-g)) in fp32.  out == gate is allowed (in place).
+ * [page layers/dense_ffn_decode_batch.rs, fn forward_km_q2: silu_mul over
+ *  m * intermediate elements with the output over the gate buffer.] */
+int silu_mul_bf16(const void *gate, const void *up, void *out, uint64_t count, void *stream);
+
+/* ---- test hooks: integer block dot products ---------------------------- */
+
+/* Runs the MMQ kernel's own unpack and matrix-core path over the window
+ * rows [m0, m0+mt) x columns [n0, n0+nt) and writes, instead of the scaled
+ * output, the int32 dot product of every 32-block:
+ *   out[(i*nt + j)*(k/32) + b] = sum_{t<32} (c - 2) * q     (Q2_0)
+ *   out[(i*nt + j)*(k/32) + b] = sum_{t<32} q4 * q          (Q4_K)
+ * for row m0+i, column n0+j, block b.  out holds mt*nt*(k/32) int32.
+ * Constraints as for the matching GEMM; mt, nt >= 1; the window must lie
+ * inside [0, m) x [0, n). */
+int q2_0_mmq_blockdots(const void *act_q8, const void *w_q2, int32_t *out,
+                       uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt,
+                       uint32_t m, uint32_t n, uint32_t k, void *stream);
+int q4k_mmq_blockdots(const void *act_q8, const void *w_q4k, int32_t *out,
+                      uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt,
+                      uint32_t m, uint32_t n, uint32_t k, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQMM_H */

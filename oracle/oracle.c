@@ -316,18 +316,21 @@ void oracle_q2_0_mmq(const uint8_t *q8, const uint8_t *w, double *R,
 void oracle_q2_0_gemv(const uint16_t *act, const uint8_t *w, double *R,
                       uint32_t m, uint32_t n, uint32_t k)
 {
+    double *a = (double *)malloc(sizeof(double) * (uint64_t)m * k);
     double *row = (double *)malloc(sizeof(double) * k);
+    for (uint64_t i = 0; i < (uint64_t)m * k; ++i) a[i] = oracle_bf16_to_f64(act[i]);
     for (uint64_t j = 0; j < n; ++j) {
         for (uint64_t kk = 0; kk < k; ++kk)
             row[kk] = q2_scale(w, n, k, 128u, j, kk / 128u) *
                       ((double)q2_code(w, k, 128u, j, kk) - 2.0);
         for (uint64_t i = 0; i < m; ++i) {
             double s = 0.0;
-            for (uint64_t kk = 0; kk < k; ++kk) s += oracle_bf16_to_f64(act[i * k + kk]) * row[kk];
+            for (uint64_t kk = 0; kk < k; ++kk) s += a[i * k + kk] * row[kk];
             R[i * n + j] = s;
         }
     }
     free(row);
+    free(a);
 }
 
 /* Dense GEMM on bf16 operands: R[i][j] = sum_k a[i][k] * w[j][k], fp64.

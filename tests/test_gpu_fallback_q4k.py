@@ -1,0 +1,128 @@
+"""GPU parity: the BF16 dequant fallback (dequant bit-exact; dense GEMM and
+the prefill dispatcher's fallback branch within relative Frobenius 2e-2), the
+dispatcher's MMQ branch, and the Q4_K MMQ (block dots bit-exact, floats within
+the row-L2 bound)."""
+import numpy as np
+import pytest
+import torch
+
+import inputs
+import oracle
+import bit_quantized_matmul_quantize_amd as bq
+from parity_helpers import (FROB_TOL, ROW_TOL, dev_bf16, dev_u8, empty_bf16, frob_error, host_bits,
+                            host_f64, rounded_row_ok, row_error)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("n,k,group,seed", [(256, 512, 128, 0), (7, 96, 32, 31), (33, 512, 64, 32),
+                                            (5, 1024, 256, 33), (12288, 2048, 128, 4)])
+def test_dequant_bit_exact(gpu, n, k, group, seed):
+    w = inputs.q2_0_weight(inputs.rng(seed), n, k, group)
+    out = empty_bf16((n, k), gpu)
+    bq.dequant_q2_0_to_bf16(dev_u8(w, gpu), out, n, k, group)
+    assert np.array_equal(host_bits(out), oracle.dequant_q2_0_to_bf16(w, n, k, group))
+
+
+@pytest.mark.parametrize("m,n,k,seed", [(4, 256, 512, 41), (130, 200, 192, 42), (1, 1, 64, 43)])
+def test_dense_gemm_bf16(gpu, m, n, k, seed):
+    g = inputs.rng(seed)
+    a = inputs.activations(g, m, k)
+    wb = inputs.activations(g, n, k)
+    out = empty_bf16((m, n), gpu)
+    bq.dense_gemm_bf16(dev_bf16(a, gpu), dev_bf16(wb, gpu), out, m, n, k)
+    R = oracle.dense_gemm_bf16(a, wb, m, n, k)
+    # fp32 accumulation and one bf16 rounding of each output
+    assert rounded_row_ok(host_f64(out), R)
+
+
+def _prefill(gpu, act, w, m, n, k, group, use_mmq):
+    out = empty_bf16((m, n), gpu)
+    scratch = torch.empty((n * k,), dtype=torch.bfloat16, device=gpu)
+    q8 = torch.empty((bq.q8_1_act_bytes(m, k),), dtype=torch.uint8, device=gpu)
+    bq.q2_0_prefill_gemm(dev_bf16(act, gpu), dev_u8(w, gpu), out, scratch, q8, m, n, k, group, use_mmq)
+    return host_f64(out), q8
+
+
+def test_prefill_dispatch_tiny(gpu):
+    d = inputs.tiny()
+    m, n, k = d["m"], d["n"], d["k"]
+    R_plain = oracle.q2_0_gemv(d["act"], d["w"], m, n, k)  # unquantized bf16 input
+    y_fb, _ = _prefill(gpu, d["act"], d["w"], m, n, k, 128, False)
+    assert frob_error(y_fb, R_plain) <= FROB_TOL
+    y_mmq, q8 = _prefill(gpu, d["act"], d["w"], m, n, k, 128, True)
+    q8_ref, _ = oracle.quantize_act_q8_1(d["act"], m, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(q8.cpu().numpy(), q8_ref)
+    assert row_error(y_mmq, oracle.q2_0_mmq(q8_ref, d["w"], m, n, k)) <= ROW_TOL
+
+
+def test_prefill_fallback_other_group(gpu):
+    # group 64 has no MMQ path: the dispatcher takes the dequant branch even with use_mmq
+    m, n, k = 9, 100, 512
+    g = inputs.rng(44)
+    w = inputs.q2_0_weight(g, n, k, 64)
+    act = inputs.activations(g, m, k, outliers=True)
+    y, _ = _prefill(gpu, act, w, m, n, k, 64, True)
+    W = oracle.q2_0_decode(w, n, k, 64)
+    R = inputs.bf16_bits_to_f32(act).astype(np.float64) @ W.T
+    assert frob_error(y, R) <= FROB_TOL
+
+
+@pytest.mark.parametrize("m", [512])
+def test_prefill_fallback_qkvz(gpu, m):
+    d = inputs.prefill_qkvz()
+    n, k = d["n"], d["k"]
+    act = d["act"][:m]
+    y, _ = _prefill(gpu, act, d["w"], m, n, k, 128, False)
+    rows = np.array([0, 1, 100, 255, 256, 511])
+    R = oracle.q2_0_gemv(np.ascontiguousarray(act[rows]), d["w"], len(rows), n, k)
+    assert frob_error(y[rows], R) <= FROB_TOL
+
+
+def _q4k_rows(w, n, k, r0, rt):
+    return w.reshape(n, k // 256 * 144)[r0:r0 + rt].reshape(-1)
+
+
+def _q8_rows(q8, m, k, rows):
+    kp = (k + 255) // 256 * 256
+    codes = q8[: m * kp].reshape(m, kp)[rows]
+    ds = q8[m * kp:].reshape(m, kp // 32 * 4)[rows]
+    return np.concatenate([codes.reshape(-1), ds.reshape(-1)])
+
+
+@pytest.mark.parametrize("m,n,k,seed", [(4, 256, 512, 51), (130, 200, 768, 52), (1, 3, 256, 53)])
+def test_q4k_small(gpu, m, n, k, seed):
+    g = inputs.rng(seed)
+    w = inputs.q4k_weight(g, n, k)
+    act = inputs.activations(g, m, k, outliers=True)
+    q8, _ = oracle.quantize_act_q8_1(act, m, k)
+    q8d, wd = dev_u8(q8, gpu), dev_u8(w, gpu)
+    out = empty_bf16((m, n), gpu)
+    bq.q4k_mmq_gemm(q8d, wd, out, m, n, k)
+    R = oracle.q4k_mmq(q8, w, m, n, k)
+    y = host_f64(out)
+    assert rounded_row_ok(y, R)
+    if n >= 256:
+        assert row_error(y, R) <= ROW_TOL
+    dots = torch.full((m * n * (k // 32),), -7, dtype=torch.int32, device=gpu)
+    bq.q4k_mmq_blockdots(q8d, wd, dots, 0, m, 0, n, m, n, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(dots.cpu().numpy().reshape(m, n, k // 32), oracle.q4k_blockdots(q8, w, m, n, k))
+
+
+def test_q4k_ffn_prefill_sampled(gpu):
+    # m = 4096 FFN gate projection [17408, 5120] in Q4_K: sampled rows, and
+    # the down projection [5120, 17408] on its own input
+    d = inputs.prefill_ffn(formats=("q4k",))
+    H, I = d["hidden"], d["inter"]
+    m = 4096
+    rows = np.array([0, 1, 1000, 2047, 2048, 4095])
+    for w, n, k, act in [(d["q4k"]["wg"], I, H, d["act"]),
+                         (d["q4k"]["wd"], H, I, inputs.activations(inputs.rng(54), m, I))]:
+        q8, _ = oracle.quantize_act_q8_1(act, m, k)
+        out = empty_bf16((m, n), gpu)
+        bq.q4k_mmq_gemm(dev_u8(q8, gpu), dev_u8(w, gpu), out, m, n, k)
+        y = host_f64(out)
+        R = oracle.q4k_mmq(_q8_rows(q8, m, k, rows), w, len(rows), n, k)
+        assert row_error(y[rows], R) <= ROW_TOL

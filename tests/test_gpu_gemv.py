@@ -1,0 +1,121 @@
+"""GPU parity: Q2_0 GEMV (m = 1), batched GEMV (m = 2..8), silu_mul and the
+verify-batch FFN chain gate -> up -> silu_mul -> down."""
+import numpy as np
+import pytest
+import torch
+
+import inputs
+import oracle
+import bit_quantized_matmul_quantize_amd as bq
+from parity_helpers import (ROW_TOL, bf16_ulp_distance, dev_bf16, dev_u8, empty_bf16, host_bits, host_f64,
+                            rounded_row_ok, row_error)
+
+pytestmark = pytest.mark.gpu
+
+
+def _gemv(gpu, act, w, m, n, k):
+    out = empty_bf16((m, n), gpu)
+    if m == 1:
+        bq.q2_0_gemv_vec(dev_bf16(act, gpu), dev_u8(w, gpu), out, n, k)
+    else:
+        bq.q2_0_gemv_vec_batchm(dev_bf16(act, gpu), dev_u8(w, gpu), out, m, n, k)
+    return host_f64(out)
+
+
+def test_tiny_row0(gpu):
+    d = inputs.tiny()
+    act = d["act"][:1]
+    R = oracle.q2_0_gemv(act, d["w"], 1, d["n"], d["k"])
+    assert row_error(_gemv(gpu, act, d["w"], 1, d["n"], d["k"]), R) <= ROW_TOL
+
+
+def test_decode_qkvz_full(gpu):
+    d = inputs.decode_gemv()
+    R = oracle.q2_0_gemv(d["act"], d["w"], 1, d["n"], d["k"])
+    assert row_error(_gemv(gpu, d["act"], d["w"], 1, d["n"], d["k"]), R) <= ROW_TOL
+
+
+@pytest.mark.parametrize("m,n,k,seed", [(1, 1, 128, 21), (1, 17, 384, 22), (3, 300, 1152, 23),
+                                        (8, 33, 5120, 24), (5, 7, 17408, 25)])
+def test_ragged(gpu, m, n, k, seed):
+    g = inputs.rng(seed)
+    w = inputs.q2_0_weight(g, n, k)
+    act = inputs.activations(g, m, k, outliers=True)
+    R = oracle.q2_0_gemv(act, w, m, n, k)
+    assert rounded_row_ok(_gemv(gpu, act, w, m, n, k), R)
+
+
+def test_closed_forms(gpu):
+    # codes 2 -> exactly 0; codes 3 with d = 1 -> row sums (exact for integer inputs)
+    n, k = 5, 256
+    g = inputs.rng(26)
+    x = g.integers(-4, 5, size=(2, k)).astype(np.float32)
+    act = inputs.f32_to_bf16_bits(x)
+    ones = np.frombuffer(np.ones(n * 2, np.float16).tobytes(), np.uint8)
+    w2 = np.concatenate([np.full(n * k // 4, 0xAA, np.uint8), ones])
+    w3 = np.concatenate([np.full(n * k // 4, 0xFF, np.uint8), ones])
+    assert not _gemv(gpu, act, w2, 2, n, k).any()
+    y = _gemv(gpu, act, w3, 2, n, k)
+    assert np.array_equal(y, np.repeat(x.sum(1, keepdims=True).astype(np.float64), n, axis=1))
+
+
+def test_batch_rows_independent(gpu):
+    # row r of the m = 8 run equals row r of the m = 2 run
+    n, k = 640, 2048
+    g = inputs.rng(27)
+    w = inputs.q2_0_weight(g, n, k)
+    act = inputs.activations(g, 8, k)
+    y8 = _gemv(gpu, act, w, 8, n, k)
+    y2 = _gemv(gpu, act[:2], w, 2, n, k)
+    assert np.array_equal(y8[:2], y2)
+
+
+def test_silu_mul(gpu):
+    g = inputs.rng(28)
+    for count in (1, 7, 8, 4097, 8 * 17408):
+        gate = inputs.activations(g, 1, count)[0]
+        up = inputs.activations(g, 1, count)[0]
+        ref = oracle.silu_mul_bf16(gate, up)
+        gd, ud = dev_bf16(gate, gpu), dev_bf16(up, gpu)
+        out = empty_bf16((count,), gpu)
+        bq.silu_mul_bf16(gd, ud, out)
+        got = host_bits(out)
+        # within one bf16 step (binary32 arithmetic on the device, fp64 in the oracle)
+        assert bf16_ulp_distance(got, ref).max() <= 1
+        # in place over the gate buffer gives the same bits
+        bq.silu_mul_bf16(gd, ud, gd)
+        assert np.array_equal(host_bits(gd), got)
+
+
+@pytest.fixture(scope="module")
+def ffn():
+    return inputs.verify_ffn()
+
+
+@pytest.mark.parametrize("m", [2, 3, 4, 8])
+def test_verify_ffn_chain(gpu, ffn, m):
+    H, I = ffn["hidden"], ffn["inter"]
+    x = ffn["act"][:m]
+    wg, wu, wdn = (dev_u8(ffn[key], gpu) for key in ("wg", "wu", "wd"))
+    xd = dev_bf16(x, gpu)
+    gate, up, out = empty_bf16((m, I), gpu), empty_bf16((m, I), gpu), empty_bf16((m, H), gpu)
+    bq.q2_0_gemv_vec_batchm(xd, wg, gate, m, I, H)
+    bq.q2_0_gemv_vec_batchm(xd, wu, up, m, I, H)
+    g_bits, u_bits = host_bits(gate), host_bits(up)
+    bq.silu_mul_bf16(gate, up, gate, m * I)
+    h_bits = host_bits(gate)
+    bq.q2_0_gemv_vec_batchm(gate, wdn, out, m, H, I)
+    y = host_f64(out)
+    # stage-wise: each stage against the oracle on the device's own previous output
+    Rg = oracle.q2_0_gemv(x, ffn["wg"], m, I, H)
+    Ru = oracle.q2_0_gemv(x, ffn["wu"], m, I, H)
+    assert row_error(inputs.bf16_bits_to_f32(g_bits).astype(np.float64), Rg) <= ROW_TOL
+    assert row_error(inputs.bf16_bits_to_f32(u_bits).astype(np.float64), Ru) <= ROW_TOL
+    Rh = oracle.silu_mul_bf16(g_bits, u_bits)
+    assert bf16_ulp_distance(h_bits, Rh).max() <= 1
+    Rd = oracle.q2_0_gemv(h_bits, ffn["wd"], m, H, I)
+    assert row_error(y, Rd) <= ROW_TOL
+    # end to end against the oracle's own chain (rounded to bf16 at the same points)
+    Rend = oracle.q2_0_gemv(oracle.silu_mul_bf16(oracle.round_bf16(Rg), oracle.round_bf16(Ru)),
+                            ffn["wd"], m, H, I)
+    assert row_error(y, Rend) <= ROW_TOL

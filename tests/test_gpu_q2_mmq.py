@@ -1,0 +1,148 @@
+"""GPU parity: Q2_0 MMQ.  Integer block dots bit-exact (through the same
+kernel path, dumped before the epilogue); bf16 outputs within the row-L2
+bound of the oracle's fp64 result."""
+import numpy as np
+import pytest
+import torch
+
+import inputs
+import oracle
+import bit_quantized_matmul_quantize_amd as bq
+from parity_helpers import ROW_TOL, dev_bf16, dev_u8, empty_bf16, host_f64, rounded_row_ok, row_error
+
+pytestmark = pytest.mark.gpu
+
+
+def _q8_dev(gpu, act, m, k):
+    q8, _ = oracle.quantize_act_q8_1(act, m, k)  # bit-exact with the device quantizer (tested)
+    return q8, dev_u8(q8, gpu)
+
+
+def _mmq(gpu, q8d, wd, m, n, k):
+    out = empty_bf16((m, n), gpu)
+    bq.q2_0_mmq_gemm(q8d, wd, out, m, n, k)
+    return host_f64(out)
+
+
+def _dots(gpu, q8d, wd, m0, mt, n0, nt, m, n, k):
+    out = torch.full((mt * nt * (k // 32),), -7, dtype=torch.int32, device=gpu)
+    bq.q2_0_mmq_blockdots(q8d, wd, out, m0, mt, n0, nt, m, n, k)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().reshape(mt, nt, k // 32)
+
+
+def test_tiny_full(gpu):
+    d = inputs.tiny()
+    m, n, k = d["m"], d["n"], d["k"]
+    q8, q8d = _q8_dev(gpu, d["act"], m, k)
+    wd = dev_u8(d["w"], gpu)
+    R = oracle.q2_0_mmq(q8, d["w"], m, n, k)
+    assert row_error(_mmq(gpu, q8d, wd, m, n, k), R) <= ROW_TOL
+    D = _dots(gpu, q8d, wd, 0, m, 0, n, m, n, k)
+    assert np.array_equal(D, oracle.q2_0_blockdots(q8, d["w"], m, n, k))
+
+
+@pytest.mark.parametrize("m,n,k,seed", [
+    (130, 200, 384, 11),   # ragged m and n over several tiles, 3 groups
+    (1, 1, 128, 12),       # degenerate single output
+    (257, 131, 1024, 13),  # tails on both sides, n % 4 != 0 (scalar stores)
+    (64, 384, 2048, 14),
+])
+def test_ragged_shapes(gpu, m, n, k, seed):
+    g = inputs.rng(seed)
+    w = inputs.q2_0_weight(g, n, k)
+    act = inputs.activations(g, m, k, outliers=True)
+    q8, q8d = _q8_dev(gpu, act, m, k)
+    wd = dev_u8(w, gpu)
+    R = oracle.q2_0_mmq(q8, w, m, n, k)
+    assert rounded_row_ok(_mmq(gpu, q8d, wd, m, n, k), R)
+    mt, nt = min(m, 40), min(n, 70)
+    m0, n0 = m - mt, n - nt
+    D = _dots(gpu, q8d, wd, m0, mt, n0, nt, m, n, k)
+    Dref = oracle.q2_0_blockdots(_rows_q8(q8, m, k, m0, mt), w, mt, n, k)
+    assert np.array_equal(D, Dref[:, n0:n0 + nt])
+
+
+def _rows_q8(q8, m, k, r0, rt):
+    """q8_1 buffer of rows [r0, r0+rt) of an m-row buffer (layout-level copy)."""
+    kp = (k + 255) // 256 * 256
+    codes = q8[: m * kp].reshape(m, kp)[r0:r0 + rt]
+    ds = q8[m * kp:].reshape(m, kp // 32 * 4)[r0:r0 + rt]
+    return np.concatenate([codes.reshape(-1), ds.reshape(-1)])
+
+
+def test_integer_case_exact(gpu):
+    # amax 127 per block -> d = 1, q = x; weight scales 1 -> exact small integers
+    m, n, k = 33, 65, 256
+    g = inputs.rng(15)
+    x = g.integers(-3, 4, size=(m, k)).astype(np.float32)
+    x[:, ::32] = 127
+    x[:, 1::32] = -127
+    act = inputs.f32_to_bf16_bits(x)
+    codes = inputs.q2_0_weight(g, n, k)
+    w = codes.copy()
+    w[n * k // 4:] = np.frombuffer(np.ones(n * k // 128, np.float16).tobytes(), np.uint8)
+    q8, q8d = _q8_dev(gpu, act, m, k)
+    R = oracle.q2_0_mmq(q8, w, m, n, k)
+    assert np.all(R == np.round(R))
+    y = _mmq(gpu, q8d, dev_u8(w, gpu), m, n, k)
+    small = np.abs(R) <= 256
+    assert np.array_equal(y[small], R[small])
+
+
+@pytest.mark.parametrize("m", [512, 2048])
+def test_prefill_qkvz_sampled(gpu, m):
+    d = inputs.prefill_qkvz()
+    n, k = d["n"], d["k"]
+    act = d["act"][:m]
+    q8, q8d = _q8_dev(gpu, act, m, k)
+    wd = dev_u8(d["w"], gpu)
+    y = _mmq(gpu, q8d, wd, m, n, k)
+    rows = np.unique(np.concatenate([[0, m - 1], inputs.rng(99).choice(m, 14, replace=False)]))
+    R = oracle.q2_0_mmq(_rows_sel(q8, m, k, rows), d["w"], len(rows), n, k)
+    assert row_error(y[rows], R) <= ROW_TOL
+    # block dots on two windows (first tile corner and the last rows/columns)
+    for (m0, n0) in [(0, 0), (m - 32, n - 32)]:
+        D = _dots(gpu, q8d, wd, m0, 32, n0, 32, m, n, k)
+        Dref = oracle.q2_0_blockdots(_rows_q8(q8, m, k, m0, 32), _w_rows(d["w"], n, k, n0, 32), 32, 32, k)
+        assert np.array_equal(D, Dref)
+
+
+def _w_rows(w, n, k, r0, rt):
+    """Q2_0 bytes of weight rows [r0, r0+rt) (layout-level copy, group 128)."""
+    codes = w[: n * k // 4].reshape(n, k // 4)[r0:r0 + rt]
+    sc = w[n * k // 4:].reshape(n, k // 128 * 2)[r0:r0 + rt]
+    return np.concatenate([codes.reshape(-1), sc.reshape(-1)])
+
+
+def _rows_sel(q8, m, k, rows):
+    kp = (k + 255) // 256 * 256
+    codes = q8[: m * kp].reshape(m, kp)[rows]
+    ds = q8[m * kp:].reshape(m, kp // 32 * 4)[rows]
+    return np.concatenate([codes.reshape(-1), ds.reshape(-1)])
+
+
+def test_batch_invariance(gpu):
+    # rows shared by the m = 512 and m = 2048 runs give identical outputs
+    d = inputs.prefill_qkvz()
+    n, k = d["n"], d["k"]
+    wd = dev_u8(d["w"], gpu)
+    q8a, q8ad = _q8_dev(gpu, d["act"][:512], 512, k)
+    q8b, q8bd = _q8_dev(gpu, d["act"], 2048, k)
+    ya = _mmq(gpu, q8ad, wd, 512, n, k)
+    yb = _mmq(gpu, q8bd, wd, 2048, n, k)
+    assert np.array_equal(ya, yb[:512])
+
+
+def test_ffn_prefill_q2_sampled(gpu):
+    # m = 4096 FFN prefill in Q2_0: gate [17408, 5120] and down [5120, 17408]
+    d = inputs.prefill_ffn(formats=("q2_0",))
+    H, I, m = d["hidden"], d["inter"], 4096
+    rows = np.array([0, 1, 1000, 2047, 2048, 4095])
+    for w, n, k, act in [(d["q2"]["wg"], I, H, d["act"]),
+                         (d["q2"]["wd"], H, I, inputs.activations(inputs.rng(55), m, I))]:
+        print(f"case n={n} k={k} m={m}", flush=True)
+        q8, q8d = _q8_dev(gpu, act, m, k)
+        y = _mmq(gpu, q8d, dev_u8(w, gpu), m, n, k)
+        R = oracle.q2_0_mmq(_rows_sel(q8, m, k, rows), w, len(rows), n, k)
+        assert row_error(y[rows], R) <= ROW_TOL

@@ -1,0 +1,64 @@
+"""GPU parity: quantize_act_q8_1 against the oracle, bit-exact over the whole
+q8_1 buffer (codes, d and s)."""
+import numpy as np
+import pytest
+import torch
+
+import inputs
+import oracle
+import bit_quantized_matmul_quantize_amd as bq
+from parity_helpers import dev_bf16, dev_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(gpu, act, m, k):
+    out = torch.full((bq.q8_1_act_bytes(m, k),), 0x5A, dtype=torch.uint8, device=gpu)
+    bq.quantize_act_q8_1(dev_bf16(act, gpu), out, m, k)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("m,k,outliers,seed", [
+    (4, 512, False, 0),        # tiny workload
+    (1, 1, False, 1),          # one value, padded to 256
+    (3, 300, True, 2),         # ragged k: scalar tail and padding
+    (5, 2056, True, 3),        # k % 8 == 0 but not % 256: vector path then padding
+    (7, 4100, False, 4),       # k % 8 != 0: scalar path
+    (130, 2048, True, 5),      # more than one 2048 chunk per row? no: exactly one; 130 rows
+    (2, 5120, False, 6),       # three 2048-chunks per row
+])
+def test_quantize_bit_exact(gpu, m, k, outliers, seed):
+    act = inputs.activations(inputs.rng(seed), m, k, outliers=outliers)
+    ref, flagged = oracle.quantize_act_q8_1(act, m, k)
+    assert flagged == 0
+    got = _run(gpu, act, m, k)
+    assert np.array_equal(got, ref)
+
+
+def test_quantize_edge_values(gpu):
+    # zero blocks, a ties block (amax 127 -> d = 1), tiny values (subnormal d)
+    m, k = 3, 256
+    x = np.zeros((m, k), np.float32)
+    x[1, :8] = [127.0, 2.5, -2.5, 0.5, -0.5, 126.5, -1.5, 3.5]
+    x[2] = np.linspace(-1e-6, 1e-6, k, dtype=np.float32)
+    x[2, 32:64] = 3e-5
+    act = inputs.f32_to_bf16_bits(x)
+    ref, _ = oracle.quantize_act_q8_1(act, m, k)
+    assert np.array_equal(_run(gpu, act, m, k), ref)
+
+
+def test_quantize_prefill_full_size(gpu):
+    # m = 2048, k = 2048 qkvz prefill input (with outlier channels), whole buffer
+    d = inputs.prefill_qkvz()
+    act = d["act"]
+    ref, _ = oracle.quantize_act_q8_1(act, 2048, 2048)
+    assert np.array_equal(_run(gpu, act, 2048, 2048), ref)
+
+
+def test_quantize_ffn_down_input_full_size(gpu):
+    # m = 4096, k = 17408: the largest activation the FFN prefill quantizes
+    g = inputs.rng(77)
+    act = inputs.activations(g, 4096, 17408)
+    ref, _ = oracle.quantize_act_q8_1(act, 4096, 17408)
+    assert np.array_equal(_run(gpu, act, 4096, 17408), ref)

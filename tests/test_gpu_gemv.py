@@ -36,7 +36,11 @@ def test_decode_qkvz_full(gpu):
 
 
 @pytest.mark.parametrize("m,n,k,seed", [(1, 1, 128, 21), (1, 17, 384, 22), (3, 300, 1152, 23),
-                                        (8, 33, 5120, 24), (5, 7, 17408, 25)])
+                                        (8, 33, 5120, 24), (5, 7, 17408, 25),
+                                        (1, 50, 5120, 29),      # m=1: three 32-chunk slices, ragged last
+                                        (1, 100, 17408, 30),    # m=1: prep loop over 1088 items
+                                        (1, 3, 33792, 31),      # m=1 beyond the LDS-staged kernel's k
+                                        (1, 4096 + 37, 2048, 32)])
 def test_ragged(gpu, m, n, k, seed):
     g = inputs.rng(seed)
     w = inputs.q2_0_weight(g, n, k)

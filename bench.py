@@ -65,13 +65,23 @@ class Leg:
     later capture begins, so a tensor without a live reference would be
     unmapped under an earlier graph."""
 
-    def __init__(self, name, fn, keep, launches, work, unit, kernel, peak, bound):
+    def __init__(self, name, fn, keep, launches, work, unit, kernel, peak, bound, min_ms=2.0):
         import torch
-        self.name, self.fn, self.keep, self.launches = name, fn, list(keep), launches
-        self.work, self.unit, self.kernel, self.peak, self.bound = work, unit, kernel, peak, bound
+        self.name, self.fn, self.keep = name, fn, list(keep)
+        self.unit, self.kernel, self.peak, self.bound = unit, kernel, peak, bound
         log(f"capture {name}")
         fn()  # eager run first: argument errors surface here, outside capture
         torch.cuda.synchronize()
+        # Repeat the leg inside one graph until a replay lasts >= min_ms, so the
+        # fixed cost of launching a graph is amortized over many kernels.
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        self.reps = max(1, min(200, int(np.ceil(min_ms / max(a.elapsed_time(b), 1e-3)))))
+        self.launches = launches * self.reps
+        self.work = work * self.reps
         self.graph = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -80,7 +90,8 @@ class Leg:
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         with torch.cuda.graph(self.graph):
-            fn()
+            for _ in range(self.reps):
+                fn()
         torch.cuda.synchronize()
         self.ms = []
 
@@ -106,7 +117,7 @@ class Leg:
         rate = self.work / (ms * 1e-3)  # units per second
         scale = 1e9 if self.unit == "GB/s" else 1e12
         achieved = rate / scale
-        return dict(name=self.name, ms=round(ms, 4), us_per_launch=round(per_launch_us, 3),
+        return dict(name=self.name, ms=round(ms, 4), reps=self.reps, us_per_launch=round(per_launch_us, 3),
                     value=round(achieved, 2), unit=self.unit, kernel=self.kernel,
                     frac_of_peak=round(achieved / self.peak, 4), bound=self.bound)
 
@@ -253,7 +264,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     summaries = {leg.name: leg.summary() for leg in legs}
     for s in summaries.values():
-        log(f"{s['name']:28s} {s['ms']:9.4f} ms  {s['value']:9.2f} {s['unit']:5s} "
+        log(f"{s['name']:28s} {s['ms']:9.4f} ms x{s['reps']:<3d} {s['value']:9.2f} {s['unit']:5s} "
             f"({100 * s['frac_of_peak']:.1f}% of peak, {s['us_per_launch']:.2f} us/launch)")
 
     result = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

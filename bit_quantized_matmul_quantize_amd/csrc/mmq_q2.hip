@@ -35,6 +35,10 @@ constexpr int BM = 128;       // activation rows per tile
 constexpr int KG = 128;       // k per stage (one Q2_0 group = four q8_1 blocks)
 constexpr int LDS_STRIDE = KG + 16;  // bytes per staged row; the pad spreads banks
 constexpr int kThreads = 256;
+// one LDS stage: activation codes, unpacked weight codes, weight scales, multipliers
+constexpr int kActBytes = BM * LDS_STRIDE;
+constexpr int kWBytes = BN * LDS_STRIDE;
+constexpr int kStageBytes = kActBytes + kWBytes + BN * 4 + BM * 16;
 
 __device__ __forceinline__ int mad_i24(int a, int b, int c) {
   // a, b fit in 24 bits (|D| <= 8128, mu < 2^16); one v_mad_i32_i24.
@@ -49,18 +53,17 @@ __device__ __forceinline__ uint32_t unpack_signed(uint32_t word, int j) {
 }
 
 template <bool kDump>
-__global__ __launch_bounds__(kThreads) void q2_0_mmq_kernel(
+__global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
     const uint8_t *__restrict__ act_q8, const uint8_t *__restrict__ w, uint16_t *__restrict__ out,
     int32_t *__restrict__ dots, uint32_t m, uint32_t n, uint32_t k, uint32_t m0, uint32_t mt,
     uint32_t n0, uint32_t nt, uint32_t tile_n0, uint32_t tile_m0) {
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint8_t w_lds[BN * LDS_STRIDE];
-  __shared__ float dw_lds[BN];
-  __shared__ int mu_lds[BM * 4];
+  // Two LDS stages (dynamic shared memory, kStageBytes each): group g is
+  // computed from stage g % 2 while group g + 1 is written into the other.
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int rowexp[BM];
 
   const uint32_t tid = threadIdx.x;
-  const uint32_t lane = tid & 63u;
+  const uint32_t lane = tid & 63u, l32 = lane & 31u, hi = lane >> 5;
   const uint32_t wave = tid >> 6;
   const uint32_t wn = wave & 1u, wm = wave >> 1;
   const uint32_t n_base = (blockIdx.x + tile_n0) * BN;
@@ -71,19 +74,42 @@ __global__ __launch_bounds__(kThreads) void q2_0_mmq_kernel(
   const uint8_t *ds = act_q8 + (uint64_t)m * kpad;
   const uint16_t *wscale = reinterpret_cast<const uint16_t *>(w + (uint64_t)n * k / 4u);
 
+  // Global -> register staging.  Rows past m or n read the last valid row
+  // (no branch around the loads); their results are never stored.
+  const uint32_t a_row[4] = {min(m_base + (tid >> 3), m - 1u), min(m_base + 32u + (tid >> 3), m - 1u),
+                             min(m_base + 64u + (tid >> 3), m - 1u), min(m_base + 96u + (tid >> 3), m - 1u)};
+  const uint32_t a_col = (tid & 7u) * 16u;
+  const uint32_t w_row = min(n_base + (tid >> 1), n - 1u), w_half = tid & 1u;
+  const uint32_t s_row = (tid < BN) ? min(n_base + tid, n - 1u) : min(m_base + tid - BN, m - 1u);
+
   // Row exponent: binary16 exponent field of the largest block scale of the row.
   {
     const uint32_t r = tid >> 1, part = tid & 1u;
+    const uint32_t *pairs =
+        reinterpret_cast<const uint32_t *>(ds) + (uint64_t)min(m_base + r, m - 1u) * nblk_pad;
+    const uint32_t nb = k / 32u;
     uint32_t mx = 0;
-    if (m_base + r < m) {
-      const uint32_t *pairs =
-          reinterpret_cast<const uint32_t *>(ds) + (uint64_t)(m_base + r) * nblk_pad;
-      const uint32_t nb = k / 32u;
-      for (uint32_t b = part; b < nb; b += 2) mx = max(mx, pairs[b] & 0x7FFFu);
-    }
+    for (uint32_t b = part; b < nb; b += 2) mx = max(mx, pairs[b] & 0x7FFFu);
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
     if (part == 0) rowexp[r] = (int)(mx >> 10);
   }
+
+  // Prefetch registers for one group (next group's data is in flight while
+  // the current group computes).
+  uint4 ra0, ra1, ra2, ra3, rw, rds = make_uint4(0, 0, 0, 0);
+  uint32_t rs16 = 0;
+#define BQMM_FETCH(g)                                                                                   \
+  do {                                                                                                  \
+    ra0 = *reinterpret_cast<const uint4 *>(act_q8 + (uint64_t)a_row[0] * kpad + (g) * KG + a_col);       \
+    ra1 = *reinterpret_cast<const uint4 *>(act_q8 + (uint64_t)a_row[1] * kpad + (g) * KG + a_col);       \
+    ra2 = *reinterpret_cast<const uint4 *>(act_q8 + (uint64_t)a_row[2] * kpad + (g) * KG + a_col);       \
+    ra3 = *reinterpret_cast<const uint4 *>(act_q8 + (uint64_t)a_row[3] * kpad + (g) * KG + a_col);       \
+    rw = *reinterpret_cast<const uint4 *>(w + (uint64_t)w_row * (k / 4u) + (g) * 32u + w_half * 16u);    \
+    if (tid < BN)                                                                                       \
+      rs16 = wscale[(uint64_t)s_row * ngroups + (g)];                                                   \
+    else                                                                                                \
+      rds = *reinterpret_cast<const uint4 *>(ds + 4ull * ((uint64_t)s_row * nblk_pad + 4u * (g)));     \
+  } while (0)
 
   float acc_out[2][2][16];
 #pragma unroll
@@ -95,119 +121,154 @@ __global__ __launch_bounds__(kThreads) void q2_0_mmq_kernel(
 
   const v16i zero16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
+  // Write the prefetched group into LDS stage `st`.
+#define BQMM_STAGE(st)                                                                                   \
+  do {                                                                                                   \
+    uint8_t *a_lds = lds + (st) * kStageBytes;                                                           \
+    uint8_t *w_lds = a_lds + kActBytes;                                                                  \
+    float *dw_lds = reinterpret_cast<float *>(w_lds + kWBytes);                                          \
+    int *mu_lds = reinterpret_cast<int *>(dw_lds + BN);                                                  \
+    *reinterpret_cast<uint4 *>(a_lds + (0 * 32 + (tid >> 3)) * LDS_STRIDE + a_col) = ra0;                \
+    *reinterpret_cast<uint4 *>(a_lds + (1 * 32 + (tid >> 3)) * LDS_STRIDE + a_col) = ra1;                \
+    *reinterpret_cast<uint4 *>(a_lds + (2 * 32 + (tid >> 3)) * LDS_STRIDE + a_col) = ra2;                \
+    *reinterpret_cast<uint4 *>(a_lds + (3 * 32 + (tid >> 3)) * LDS_STRIDE + a_col) = ra3;                \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                      \
+      const uint4 sv = make_uint4(unpack_signed(rw.x, j), unpack_signed(rw.y, j),                        \
+                                  unpack_signed(rw.z, j), unpack_signed(rw.w, j));                       \
+      *reinterpret_cast<uint4 *>(w_lds + (tid >> 1) * LDS_STRIDE + 32 * j + 16 * w_half) = sv;           \
+    }                                                                                                    \
+    if (tid < BN) {                                                                                      \
+      dw_lds[tid] = f16_bits_to_f32(rs16);                                                               \
+    } else {                                                                                             \
+      const int e = rowexp[tid - BN];                                                                    \
+      int4 mu;                                                                                           \
+      mu.x = (int)rintf(ldexpf(f16_bits_to_f32(rds.x & 0xFFFFu), 30 - e));                               \
+      mu.y = (int)rintf(ldexpf(f16_bits_to_f32(rds.y & 0xFFFFu), 30 - e));                               \
+      mu.z = (int)rintf(ldexpf(f16_bits_to_f32(rds.z & 0xFFFFu), 30 - e));                               \
+      mu.w = (int)rintf(ldexpf(f16_bits_to_f32(rds.w & 0xFFFFu), 30 - e));                               \
+      *reinterpret_cast<int4 *>(mu_lds + (tid - BN) * 4) = mu;                                           \
+    }                                                                                                    \
+  } while (0)
+
+  BQMM_FETCH(0u);
+  __syncthreads();  // rowexp visible
+  BQMM_STAGE(0);
+  if (ngroups > 1) BQMM_FETCH(1u);
+  // Loop body: one barrier, then stage group g + 1 into the other LDS stage and
+  // start the loads of group g + 2, then compute group g.  The barrier both
+  // publishes stage g and guarantees that every wave has finished reading the
+  // stage about to be overwritten (it held group g - 1).  The compute is last
+  // in the body: placed before a barrier, its epilogue gets sunk below it and
+  // all MFMA results of a group stay alive across the barrier.
   for (uint32_t g = 0; g < ngroups; ++g) {
-    __syncthreads();  // previous group fully consumed (and rowexp visible)
-    // activation codes: 128 rows x 128 bytes, 16 bytes per load
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t c = tid + kThreads * i;
-      const uint32_t r = c >> 3, col = (c & 7u) * 16u;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m_base + r < m)
-        v = *reinterpret_cast<const uint4 *>(act_q8 + (uint64_t)(m_base + r) * kpad + g * KG + col);
-      *reinterpret_cast<uint4 *>(a_lds + r * LDS_STRIDE + col) = v;
-    }
-    // weight codes: 128 rows x 32 bytes, unpacked to signed int8
-    {
-      const uint32_t r = tid >> 1, half = tid & 1u;
-      uint4 p = make_uint4(0xAAAAAAAAu, 0xAAAAAAAAu, 0xAAAAAAAAu, 0xAAAAAAAAu);  // codes 2 -> 0
-      if (n_base + r < n)
-        p = *reinterpret_cast<const uint4 *>(w + (uint64_t)(n_base + r) * (k / 4u) + g * 32u + half * 16u);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 s = make_uint4(unpack_signed(p.x, j), unpack_signed(p.y, j),
-                                   unpack_signed(p.z, j), unpack_signed(p.w, j));
-        *reinterpret_cast<uint4 *>(w_lds + r * LDS_STRIDE + 32 * j + 16 * half) = s;
-      }
-    }
-    if (tid < BN) {
-      const uint32_t r = tid;
-      dw_lds[r] = (n_base + r < n) ? f16_bits_to_f32(wscale[(uint64_t)(n_base + r) * ngroups + g]) : 0.0f;
-    } else {
-      const uint32_t r = tid - BN;
-      int mu[4] = {0, 0, 0, 0};
-      if (m_base + r < m) {
-        const uint4 pr = *reinterpret_cast<const uint4 *>(ds + 4ull * ((uint64_t)(m_base + r) * nblk_pad + 4u * g));
-        const uint32_t pv[4] = {pr.x, pr.y, pr.z, pr.w};
-        const int e = rowexp[r];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) mu[b] = (int)rintf(ldexpf(f16_bits_to_f32(pv[b] & 0xFFFFu), 30 - e));
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) mu_lds[r * 4 + b] = mu[b];
-    }
     __syncthreads();
-
-    int acc_int[2][2][16];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      v4i A[2], B[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        A[s] = *reinterpret_cast<const v4i *>(w_lds + (wn * 64 + s * 32 + (lane & 31)) * LDS_STRIDE + 32 * b + 16 * (lane >> 5));
-        B[s] = *reinterpret_cast<const v4i *>(a_lds + (wm * 64 + s * 32 + (lane & 31)) * LDS_STRIDE + 32 * b + 16 * (lane >> 5));
-      }
-#pragma unroll
-      for (int sn = 0; sn < 2; ++sn)
-#pragma unroll
-        for (int sm = 0; sm < 2; ++sm) {
-          const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[sn], B[sm], zero16, 0, 0, 0);
-          if constexpr (kDump) {
-            const uint32_t mm = m_base + wm * 64 + sm * 32 + (lane & 31);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const uint32_t nn = n_base + wn * 64 + sn * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-              if (mm >= m0 && mm < m0 + mt && nn >= n0 && nn < n0 + nt)
-                dots[((uint64_t)(mm - m0) * nt + (nn - n0)) * (k / 32u) + 4u * g + b] = D[r];
-            }
-          } else {
-            const int mu = mu_lds[(wm * 64 + sm * 32 + (lane & 31)) * 4 + b];
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              acc_int[sn][sm][r] = mad_i24(D[r], mu, b == 0 ? 0 : acc_int[sn][sm][r]);
-          }
-        }
+    if (g + 1 < ngroups) {
+      BQMM_STAGE((g + 1) & 1u);
+      if (g + 2 < ngroups) BQMM_FETCH(g + 2);
     }
-    if constexpr (!kDump) {
-#pragma unroll
-      for (int sn = 0; sn < 2; ++sn) {
-        float dwv[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 t = *reinterpret_cast<const float4 *>(dw_lds + wn * 64 + sn * 32 + 8 * q + 4 * (lane >> 5));
-          dwv[4 * q + 0] = t.x; dwv[4 * q + 1] = t.y; dwv[4 * q + 2] = t.z; dwv[4 * q + 3] = t.w;
-        }
-#pragma unroll
-        for (int sm = 0; sm < 2; ++sm)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            acc_out[sn][sm][r] = fmaf((float)acc_int[sn][sm][r], dwv[r], acc_out[sn][sm][r]);
-      }
-    }
-  }
+    const uint8_t *a_lds = lds + (g & 1u) * kStageBytes;
+    const uint8_t *w_lds = a_lds + kActBytes;
+    const float *dw_lds = reinterpret_cast<const float *>(w_lds + kWBytes);
+    const int *mu_lds = reinterpret_cast<const int *>(dw_lds + BN);
 
-  if constexpr (!kDump) {
-    const bool vec = (n % 4u) == 0u;
+    // Operands of the group: both n-subtiles (weights, A) and both m-subtiles
+    // (activations, B) for the four blocks, and the activation multipliers.
+    v4i A[2][4], B[2][4];
+    int mu[2][4];
 #pragma unroll
     for (int sm = 0; sm < 2; ++sm) {
-      const uint32_t mloc = wm * 64 + sm * 32 + (lane & 31);
+      const uint32_t ml = wm * 64 + sm * 32 + l32;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        B[sm][b] = *reinterpret_cast<const v4i *>(a_lds + ml * LDS_STRIDE + 32 * b + 16 * hi);
+      const int4 t = *reinterpret_cast<const int4 *>(mu_lds + ml * 4);
+      mu[sm][0] = t.x; mu[sm][1] = t.y; mu[sm][2] = t.z; mu[sm][3] = t.w;
+    }
+#pragma unroll
+    for (int sn = 0; sn < 2; ++sn) {
+      const uint32_t nl = wn * 64 + sn * 32 + l32;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        A[sn][b] = *reinterpret_cast<const v4i *>(w_lds + nl * LDS_STRIDE + 32 * b + 16 * hi);
+    }
+
+    // 16 steps (sn, sm, b), software-pipelined by one: the MFMA of step i + 1
+    // is issued before the epilogue of step i, so the matrix core runs while
+    // the VALU folds the previous block; two result registers alternate.  A
+    // scheduling barrier after each step keeps the compiler from clustering
+    // the MFMAs (which would keep all 16 results alive).
+    v16i D[2];
+    int acc[16];
+    float dwv[16];
+#pragma unroll
+    for (int i = 0; i <= 16; ++i) {
+      if (i < 16) {
+        const int sn = i >> 3, sm = (i >> 2) & 1, b = i & 3;
+        D[i & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[sn][b], B[sm][b], zero16, 0, 0, 0);
+      }
+      if (i > 0) {
+        const int p = i - 1;
+        const int sn = p >> 3, sm = (p >> 2) & 1, b = p & 3;
+        const v16i &Dp = D[p & 1];
+        if constexpr (kDump) {
+          const uint32_t mm = m_base + wm * 64 + sm * 32 + l32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t nn = n_base + wn * 64 + sn * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (mm >= m0 && mm < m0 + mt && nn >= n0 && nn < n0 + nt)
+              dots[((uint64_t)(mm - m0) * nt + (nn - n0)) * (k / 32u) + 4u * g + b] = Dp[r];
+          }
+        } else {
+          if ((p & 7) == 0) {
+            // weight scales of n-subtile sn: loaded at its first step, after the
+            // last flush of the previous n-subtile, three steps before first use
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 t = *reinterpret_cast<const float4 *>(dw_lds + wn * 64 + sn * 32 + 8 * q + 4 * hi);
+              dwv[4 * q + 0] = t.x; dwv[4 * q + 1] = t.y; dwv[4 * q + 2] = t.z; dwv[4 * q + 3] = t.w;
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = mad_i24(Dp[r], mu[sm][b], b == 0 ? 0 : acc[r]);
+          if (b == 3) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              acc_out[sn][sm][r] = fmaf((float)acc[r], dwv[r], acc_out[sn][sm][r]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#undef BQMM_FETCH
+#undef BQMM_STAGE
+
+  if constexpr (!kDump) {
+    const bool full = (m_base + BM <= m) && (n_base + BN <= n) && (n % 4u) == 0u;
+#pragma unroll
+    for (int sm = 0; sm < 2; ++sm) {
+      const uint32_t mloc = wm * 64 + sm * 32 + l32;
       const uint32_t mm = m_base + mloc;
-      if (mm >= m) continue;
       const float scale = ldexpf(1.0f, rowexp[mloc] - 30);
-      uint16_t *orow = out + (uint64_t)mm * n;
+      uint16_t *orow = out + (uint64_t)min(mm, m - 1u) * n;
 #pragma unroll
       for (int sn = 0; sn < 2; ++sn)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t nn = n_base + wn * 64 + sn * 32 + 8 * q + 4 * (lane >> 5);
+          const uint32_t nn = n_base + wn * 64 + sn * 32 + 8 * q + 4 * hi;
           const float *v = &acc_out[sn][sm][4 * q];
-          if (vec && nn + 4 <= n) {
+          if (full) {
             *reinterpret_cast<uint2 *>(orow + nn) =
                 make_uint2(pack_bf16x2(v[0] * scale, v[1] * scale), pack_bf16x2(v[2] * scale, v[3] * scale));
-          } else {
+          } else if (mm < m) {
+            if ((n % 4u) == 0u && nn + 4 <= n) {
+              *reinterpret_cast<uint2 *>(orow + nn) =
+                  make_uint2(pack_bf16x2(v[0] * scale, v[1] * scale), pack_bf16x2(v[2] * scale, v[3] * scale));
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (nn + e < n) orow[nn + e] = (uint16_t)f32_to_bf16_rne(v[e] * scale);
+              for (int e = 0; e < 4; ++e)
+                if (nn + e < n) orow[nn + e] = (uint16_t)f32_to_bf16_rne(v[e] * scale);
+            }
           }
         }
     }
@@ -219,16 +280,26 @@ __global__ __launch_bounds__(kThreads) void q2_0_mmq_kernel(
 hipError_t launch_q2_0_mmq(const void *act_q8, const void *w, void *out, int32_t *dots,
                            uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m,
                            uint32_t n, uint32_t k, hipStream_t s) {
+  // Two stages exceed the 64 KB default dynamic-LDS limit; gfx950 allows 160 KB.
+  static const hipError_t attr_err = [] {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(q2_0_mmq_kernel<false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(q2_0_mmq_kernel<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
+    return e;
+  }();
+  if (attr_err != hipSuccess) return attr_err;
   if (dots == nullptr) {
     const dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);
-    hipLaunchKernelGGL(q2_0_mmq_kernel<false>, grid, dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(q2_0_mmq_kernel<false>, grid, dim3(kThreads), 2 * kStageBytes, s,
                        static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
                        static_cast<uint16_t *>(out), nullptr, m, n, k, 0u, 0u, 0u, 0u, 0u, 0u);
   } else {
     const uint32_t tn0 = n0 / BN, tn1 = (n0 + nt - 1) / BN;
     const uint32_t tm0 = m0 / BM, tm1 = (m0 + mt - 1) / BM;
     const dim3 grid(tn1 - tn0 + 1, tm1 - tm0 + 1);
-    hipLaunchKernelGGL(q2_0_mmq_kernel<true>, grid, dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(q2_0_mmq_kernel<true>, grid, dim3(kThreads), 2 * kStageBytes, s,
                        static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
                        nullptr, dots, m, n, k, m0, mt, n0, nt, tn0, tm0);
   }

@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbqmm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["quantize.hip", "elementwise.hip", "gemv.hip", "mmq_q2.hip", "mmq_q4k.hip",
+SOURCES = ["quantize.hip", "elementwise.hip", "gemv.hip", "gemv_mfma.hip", "mmq_q2.hip", "mmq_q4k.hip",
            "gemm_bf16.hip", "capi.cpp"]
 
 COMMON = [

@@ -45,6 +45,8 @@ hipError_t launch_silu_mul(const void *gate, const void *up, void *out, uint64_t
                            hipStream_t s);
 hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
                             uint32_t k, hipStream_t s);
+hipError_t launch_q2_0_gemv_mfma(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
+                                 uint32_t k, hipStream_t s);
 hipError_t launch_q2_0_mmq(const void *act_q8, const void *w, void *out, int32_t *dots,
                            uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m,
                            uint32_t n, uint32_t k, hipStream_t s);

@@ -5,117 +5,33 @@
 //  the bf16 activations, output bf16.]
 //
 // out[i][r] = sum_k a[i][k] * d[r][g] * (c - 2), accumulated in fp32.
-// A bandwidth kernel: the packed weight (2.125 bits per weight) is streamed
-// once with 16-byte loads; no matrix cores.  16 lanes share one weight row;
-// lane L owns the 16-byte half-groups L, L+16, ... of the row, i.e. 64 codes
-// per load: for field j of byte t the code belongs to k = 128g + 32j + 16h + t.
+// Bandwidth kernels: the packed weight (2.125 bits per weight) is streamed
+// once with 16-byte loads, row sums are wavefront reductions, no matrix cores.
+//
+// Shared arithmetic.  A 16-byte chunk c = 2g + h of a weight row holds 64
+// codes: field j (bits 2j..2j+1) of byte t is the code of
+// k = 128g + 32j + 16h + t.  Codes become bf16 without a conversion: OR-ing
+// the masked field into the mantissa of bf16 2^e gives exactly 2^e + c, with
+// e = 7, 5, 3 for j = 0..2 (field at mantissa bits 0, 2, 4) and e = 2 for
+// j = 3 (field shifted down one bit to mantissa bits 5..6).  One v_and_or_b32
+// builds two such values: bytes 0 and 2 of a 32-bit word land in the low and
+// high halves, bytes 1 and 3 after a shift by 8.  The activations are stored
+// permuted into the matching pairs (t, t+2), (t+1, t+3), so one
+// v_dot2_f32_bf16 adds (2^e + c_t) a_t + (2^e + c_t') a_t'.  Per field the
+// partial bias sum_t (2^e + 2) a_t is subtracted once per chunk, leaving
+// sum_t (c_t - 2) a_t; then the group scale is applied with one fma.
+// Activations are used as given (zeros stay exact zeros).
 #include "bqmm_internal.h"
 
 namespace bqmm {
 namespace {
 
-constexpr int kLanesPerRow = 16;
 constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = kThreads / kLanesPerRow;
-
-template <int M>
-__global__ __launch_bounds__(kThreads) void q2_0_gemv_kernel(const uint16_t *__restrict__ act,
-                                                             const uint8_t *__restrict__ w,
-                                                             uint16_t *__restrict__ out,
-                                                             uint32_t n, uint32_t k) {
-  const uint32_t sub = threadIdx.x % kLanesPerRow;
-  const uint32_t row = blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
-  const uint32_t chunks = k / 64u;  // 16-byte half-groups per row
-  const uint16_t *scales = reinterpret_cast<const uint16_t *>(w + (uint64_t)n * k / 4u);
-
-  float acc[M];
-#pragma unroll
-  for (int i = 0; i < M; ++i) acc[i] = 0.0f;
-
-  if (row < n) {
-    const uint8_t *wrow = w + (uint64_t)row * (k / 4u);
-    for (uint32_t c = sub; c < chunks; c += kLanesPerRow) {
-      const uint32_t g = c >> 1, h = c & 1u;
-      const uint4 q = *reinterpret_cast<const uint4 *>(wrow + 16u * c);
-      const float d = f16_bits_to_f32(scales[(uint64_t)row * (k / 128u) + g]);
-      const uint32_t words[4] = {q.x, q.y, q.z, q.w};
-      float part[M];
-#pragma unroll
-      for (int i = 0; i < M; ++i) part[i] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t kbase = 128u * g + 32u * j + 16u * h;
-#pragma unroll
-        for (int i = 0; i < M; ++i) {
-          const uint4 a0 = *reinterpret_cast<const uint4 *>(act + (uint64_t)i * k + kbase);
-          const uint4 a1 = *reinterpret_cast<const uint4 *>(act + (uint64_t)i * k + kbase + 8);
-          const uint32_t av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const uint32_t code = (words[t / 4] >> (8 * (t % 4) + 2 * j)) & 3u;
-            const float wv = (float)((int)code - 2);
-            const float av_f = (t & 1) ? __uint_as_float(av[t / 2] & 0xFFFF0000u)
-                                       : __uint_as_float(av[t / 2] << 16);
-            part[i] = fmaf(wv, av_f, part[i]);
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < M; ++i) acc[i] = fmaf(d, part[i], acc[i]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < M; ++i) {
-#pragma unroll
-    for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off);
-  }
-  if (row < n && sub == 0) {
-#pragma unroll
-    for (int i = 0; i < M; ++i) out[(uint64_t)i * n + row] = (uint16_t)f32_to_bf16_rne(acc[i]);
-  }
-}
-
-// ---- m = 1 decode kernel ---------------------------------------------------
-//
-// Each lane keeps one fixed 16-byte chunk position c of the weight rows (64
-// codes: half of a 128-group) and serves kRowsPerLane rows; a half-wave (32
-// lanes) covers 32 consecutive chunks of a row.  The activation slice of every
-// chunk is prepared once per workgroup in LDS:
-//   * pairs: for the 16-byte word i of a chunk and field j, the codes of bytes
-//     (0, 2) and (1, 3) of the word pair with activations (t, t+2), so the
-//     activations are permuted into those pairs;
-//   * the code field j sits at bits 2j of each byte; OR-ing a masked field into
-//     the mantissa of bf16 1.0 gives 1 + c * 2^-e_j (e = 7, 5, 3 for j = 0..2;
-//     field 3 is shifted down one bit, e = 2), exact in bf16, with one
-//     v_and_or_b32 per pair of codes;
-//   * the activation of field j is stored with its exponent raised by e_j
-//     (a' = a * 2^e_j, a packed 16-bit add; exact), so every product
-//     (1 + c 2^-e) * a' = a' + c * a and one v_dot2_f32_bf16 handles two codes;
-//   * four partial biases per chunk, sum a' (1 + 2 * 2^-e) over each field, so
-//     that sum_k (c - 2) a = dot - bias.
-// Per row and chunk: 12 bit ops + 32 dot2 + 1 fma for 64 codes.  The weight
-// loads of the first slice are issued before the activation prep, which is
-// spread over one lane per (chunk, field) and runs while they are in flight.
-// Row sums over the 32 lanes of a half-wave use DPP adds (no LDS round trip).
-// Activations are assumed below 2^120 in magnitude (the exponent add must not
-// overflow).
-
-#ifndef BQMM_GEMV_ROWS
-#define BQMM_GEMV_ROWS 3
-#endif
-constexpr int kRowsPerLane = BQMM_GEMV_ROWS;
-constexpr int kChunkStride = 36;  // dwords per chunk in LDS: 32 pairs, 4 partial biases
-constexpr uint32_t kMaxK1 = 32768;
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a), __builtin_bit_cast(v2bf, b), c, false);
-}
-
-__device__ __forceinline__ uint32_t add_u16x2(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2u16, a) + __builtin_bit_cast(v2u16, b));
 }
 
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
@@ -132,6 +48,60 @@ __device__ __forceinline__ uint32_t vconst(uint32_t c) {
   return r;
 }
 
+// bf16 2^e for the four fields, in both halves
+constexpr uint32_t kMagic[4] = {0x43004300u, 0x42004200u, 0x41004100u, 0x40804080u};
+
+struct CodeConsts {
+  uint32_t m0, m1, m2, m3, g0, g1, g2, g3;
+};
+
+__device__ __forceinline__ CodeConsts code_consts() {
+  return {vconst(0x00030003u), vconst(0x000C000Cu), vconst(0x00300030u), vconst(0x00600060u),
+          vconst(kMagic[0]),   vconst(kMagic[1]),   vconst(kMagic[2]),   vconst(kMagic[3])};
+}
+
+// The eight bf16 pairs of one 32-bit code word, in the order
+// (field 0: bytes 0/2, bytes 1/3), (field 1: ...), (field 2: ...), (field 3: ...).
+__device__ __forceinline__ void word_pairs(uint32_t x, const CodeConsts &K, uint32_t p[8]) {
+  const uint32_t x8 = x >> 8, x1 = x >> 1, x9 = x >> 9;
+  p[0] = and_or(x, K.m0, K.g0);
+  p[1] = and_or(x8, K.m0, K.g0);
+  p[2] = and_or(x, K.m1, K.g1);
+  p[3] = and_or(x8, K.m1, K.g1);
+  p[4] = and_or(x, K.m2, K.g2);
+  p[5] = and_or(x8, K.m2, K.g2);
+  p[6] = and_or(x1, K.m3, K.g3);
+  p[7] = and_or(x9, K.m3, K.g3);
+}
+
+// Activation pairs of 16 consecutive values a[0..15] (eight bf16x2 words D):
+// word i of the chunk pairs (4i, 4i+2) and (4i+1, 4i+3).
+__device__ __forceinline__ void act_pairs(const uint32_t D[8], uint32_t p[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[2 * i] = __builtin_amdgcn_perm(D[2 * i + 1], D[2 * i], 0x05040100u);
+    p[2 * i + 1] = __builtin_amdgcn_perm(D[2 * i + 1], D[2 * i], 0x07060302u);
+  }
+}
+
+// bf16 pair of 2^e_j + 2 for a field index j that is not a compile-time
+// constant (e = 7, 5, 3, 2): exponent 127 + e, one mantissa bit at 8 - e.
+// Integer arithmetic rather than a table or a select chain, which the compiler
+// turns into divergent branches.
+__device__ __forceinline__ uint32_t bias_weight(uint32_t j) {
+  const uint32_t e = 7u - 2u * j + ((j >> 1) & j & 1u);
+  const uint32_t b = ((127u + e) << 7) | (1u << (8u - e));
+  return b | (b << 16);
+}
+
+// sum_t (2^e_j + 2) a_t over 16 values
+__device__ __forceinline__ float field_bias(const uint32_t D[8], uint32_t bw) {
+  float b = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b = dot2(D[i], bw, b);
+  return b;
+}
+
 // x plus the value DPP moves into this lane (rows not in row_mask add 0).
 template <int kCtrl, int kRowMask>
 __device__ __forceinline__ float dpp_add(float x) {
@@ -139,16 +109,45 @@ __device__ __forceinline__ float dpp_add(float x) {
   return x + __int_as_float(moved);
 }
 
-// Sum over each half-wave (lanes 0..31, 32..63); the total lands in lanes
-// 16..31 and 48..63.
-__device__ __forceinline__ float half_wave_sum(float x) {
+// Sum over each group of 16 lanes; every lane of the group gets the total.
+__device__ __forceinline__ float row16_sum(float x) {
   x = dpp_add<0xB1, 0xF>(x);   // quad_perm [1,0,3,2]: xor 1
   x = dpp_add<0x4E, 0xF>(x);   // quad_perm [2,3,0,1]: xor 2
   x = dpp_add<0x124, 0xF>(x);  // row_ror:4
-  x = dpp_add<0x128, 0xF>(x);  // row_ror:8 -> every lane holds its 16-lane row sum
+  x = dpp_add<0x128, 0xF>(x);  // row_ror:8
+  return x;
+}
+
+// Sum over each half-wave (lanes 0..31, 32..63); the total lands in lanes
+// 16..31 and 48..63.
+__device__ __forceinline__ float half_wave_sum(float x) {
+  x = row16_sum(x);
   x = dpp_add<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
   return x;
 }
+
+// ---- m = 1 decode kernel ---------------------------------------------------
+//
+// Each lane keeps one fixed chunk position c of the weight rows and serves
+// kRowsPerLane rows; a half-wave (32 lanes) covers 32 consecutive chunks of a
+// row per slice.  The whole activation vector is prepared once per workgroup
+// in LDS (pairs field-major: dword 8j + 2i + b of a chunk, then the four
+// partial biases), one lane per (chunk, field).  The weight loads of the first
+// slice are issued right after the first prep item's activation loads and
+// stay in flight during the prep.  Per row and chunk: 12 shifts,
+// 32 v_and_or_b32, 32 v_dot2 and one fma for 64 codes.
+
+#ifndef BQMM_GEMV_ROWS
+#define BQMM_GEMV_ROWS 3
+#endif
+constexpr int kRowsPerLane = BQMM_GEMV_ROWS;
+constexpr int kChunkStride = 36;  // dwords per chunk in LDS: 32 pairs, 4 partial biases
+constexpr uint32_t kMaxK1 = 32768;
+constexpr uint32_t kMaxKMfma = 65536;
+#ifndef BQMM_GEMV_MIN_M_MFMA
+#define BQMM_GEMV_MIN_M_MFMA 6
+#endif
+constexpr uint32_t kMinMMfma = BQMM_GEMV_MIN_M_MFMA;
 
 __global__ __launch_bounds__(kThreads) void q2_0_gemv1_kernel(const uint16_t *__restrict__ act,
                                                               const uint8_t *__restrict__ w,
@@ -190,19 +189,9 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemv1_kernel(const uint16_t *__
   auto prep = [&](uint32_t item, uint4 av0, uint4 av1) {
     const uint32_t c = item >> 2, j = item & 3u;
     const uint32_t D[8] = {av0.x, av0.y, av0.z, av0.w, av1.x, av1.y, av1.z, av1.w};
-    const uint32_t e = (j == 0) ? 7u : (j == 1) ? 5u : (j == 2) ? 3u : 2u;
-    const uint32_t add = (e << 7) | (e << 23);
-    // bf16 of 1 + 2 * 2^-e: 1 + 2^-6, 1 + 2^-4, 1 + 2^-2, 1.5
-    const uint32_t onep = (j == 0) ? 0x3F823F82u : (j == 1) ? 0x3F883F88u : (j == 2) ? 0x3FA03FA0u : 0x3FC03FC0u;
     uint32_t p[8];
-    float b = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[2 * i] = add_u16x2(__builtin_amdgcn_perm(D[2 * i + 1], D[2 * i], 0x05040100u), add);
-      p[2 * i + 1] = add_u16x2(__builtin_amdgcn_perm(D[2 * i + 1], D[2 * i], 0x07060302u), add);
-      b = dot2(p[2 * i], onep, b);
-      b = dot2(p[2 * i + 1], onep, b);
-    }
+    act_pairs(D, p);
+    const float b = field_bias(D, bias_weight(j));
     uint32_t *dst = smem + c * kChunkStride;
     *reinterpret_cast<uint4 *>(dst + 8 * j) = make_uint4(p[0], p[1], p[2], p[3]);
     *reinterpret_cast<uint4 *>(dst + 8 * j + 4) = make_uint4(p[4], p[5], p[6], p[7]);
@@ -224,9 +213,7 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemv1_kernel(const uint16_t *__
          *reinterpret_cast<const uint4 *>(act_src(item) + 8));
   __syncthreads();
 
-  const uint32_t MAGIC = vconst(0x3F803F80u);  // bf16 1.0 in both halves
-  const uint32_t M0 = vconst(0x00030003u), M1 = vconst(0x000C000Cu), M2 = vconst(0x00300030u),
-                 M3 = vconst(0x00600060u);
+  const CodeConsts K = code_consts();
   float acc_out[kRowsPerLane];
 #pragma unroll
   for (int r = 0; r < kRowsPerLane; ++r) acc_out[r] = 0.0f;
@@ -251,15 +238,13 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemv1_kernel(const uint16_t *__
         float acc = -bias;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t x = words[i], x8 = x >> 8, x1 = x >> 1, x9 = x >> 9;
-          acc = dot2(and_or(x, M0, MAGIC), P[2 * i], acc);
-          acc = dot2(and_or(x8, M0, MAGIC), P[2 * i + 1], acc);
-          acc = dot2(and_or(x, M1, MAGIC), P[8 + 2 * i], acc);
-          acc = dot2(and_or(x8, M1, MAGIC), P[8 + 2 * i + 1], acc);
-          acc = dot2(and_or(x, M2, MAGIC), P[16 + 2 * i], acc);
-          acc = dot2(and_or(x8, M2, MAGIC), P[16 + 2 * i + 1], acc);
-          acc = dot2(and_or(x1, M3, MAGIC), P[24 + 2 * i], acc);
-          acc = dot2(and_or(x9, M3, MAGIC), P[24 + 2 * i + 1], acc);
+          uint32_t wp[8];
+          word_pairs(words[i], K, wp);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc = dot2(wp[2 * j], P[8 * j + 2 * i], acc);
+            acc = dot2(wp[2 * j + 1], P[8 * j + 2 * i + 1], acc);
+          }
         }
         acc_out[r] = fmaf(f16_bits_to_f32(sc[r]), acc, acc_out[r]);
       }
@@ -276,14 +261,286 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemv1_kernel(const uint16_t *__
   }
 }
 
-template <int M>
-hipError_t launch_m(const void *act, const void *w, void *out, uint32_t n, uint32_t k,
-                    hipStream_t s) {
-  const uint32_t blocks = (n + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(q2_0_gemv_kernel<M>, dim3(blocks), dim3(kThreads), 0, s,
+// ---- batched kernel, m = 1..8 ---------------------------------------------
+//
+// Used for the verify batches, and for m = 1 when k is beyond the decode
+// kernel's whole-vector LDS staging.  A group of L lanes serves R weight rows;
+// lane li of the group takes chunk li of every slice of L chunks.  The
+// workgroup (256 / L groups, 256 R / L rows) walks k slice by slice: the
+// activation slice of all M rows is prepared into LDS once per workgroup and
+// read by every group, so the prep is amortized over the workgroup's rows and
+// each activation pair read from LDS feeds R rows.
+//
+// LDS per chunk and activation row (kRowDw dwords): 32 pairs word-major
+// (dword 8i + 2j + b for word i, field j, byte pair b), then the four partial
+// biases; chunks are padded so that the 16 chunks read by one instruction hit
+// distinct bank quads.  Two LDS buffers and D register slots of weights:
+// iteration s computes slice s, prepares slice s+1 from activations loaded in
+// the previous iteration, loads the activations of slice s+2 and then the
+// weights of slice s+D, and ends with the only barrier.  Issuing activation
+// loads ahead of weight loads matters because vector-memory counters retire
+// in order: the prep of slice s+1 then never waits for HBM.
+//
+// Chunks past k (a ragged last slice) get zero activations and zero biases,
+// so their (clamped, valid) weight loads add exactly 0.
+
+constexpr int kRowDw = 36;
+
+__host__ __device__ constexpr int gemvm_chunk_dwords(int M) {
+  return ((kRowDw * M / 4) % 2 == 1) ? kRowDw * M : kRowDw * M + 4;
+}
+
+template <int M, int R, int L, int D>
+__global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__restrict__ act,
+                                                              const uint8_t *__restrict__ w,
+                                                              uint16_t *__restrict__ out, uint32_t n,
+                                                              uint32_t k) {
+  static_assert(L == 16 || L == 32, "lane group of 16 or 32");
+  static_assert(D == 2 || D == 3, "the load-free tail covers at most two slices");
+  constexpr int CS = gemvm_chunk_dwords(M);
+  constexpr int kGroups = kThreads / L;
+  constexpr int kItems = 4 * L * M;  // prep items per slice: (chunk, field, activation row)
+  constexpr int kPrep = (kItems + kThreads - 1) / kThreads;
+  static_assert(kItems % 64 == 0, "prep items fill whole waves");
+  constexpr int kBuf = L * CS;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[2 * kBuf];
+
+  const uint32_t C = k >> 6, G = k >> 7;
+  const uint32_t tid = threadIdx.x, li = tid % L, grp = tid / L;
+  const uint32_t row_base = (blockIdx.x * kGroups + grp) * R;
+  const uint32_t ns = (C + L - 1) / L;
+  const uint16_t *scales = reinterpret_cast<const uint16_t *>(w + (uint64_t)n * k / 4u);
+
+  // rows past n compute on row n-1 and are not stored
+  const uint8_t *wrow[R];
+  const uint16_t *srow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t row = min(row_base + r, n - 1u);
+    wrow[r] = w + (uint64_t)row * (k >> 2);
+    srow[r] = scales + (uint64_t)row * G;
+  }
+
+  // This thread's prep items.  Item order (m, group, field, half) makes
+  // consecutive threads read consecutive 32-byte activation runs.  Threads
+  // past the last item load that item's activations again (their loads stay
+  // unconditional) but write nothing.
+  uint32_t it_m[kPrep], it_cl[kPrep], it_j[kPrep], it_src[kPrep];
+#pragma unroll
+  for (int q = 0; q < kPrep; ++q) {
+    const uint32_t it = min(tid + (uint32_t)(kThreads * q), (uint32_t)kItems - 1u);
+    const uint32_t m = it / (4u * L), rr = it % (4u * L);
+    const uint32_t h = rr & 1u, j = (rr >> 1) & 3u, gl = rr >> 3;
+    it_m[q] = m;
+    it_cl[q] = 2u * gl + h;
+    it_j[q] = j;
+    it_src[q] = m * k + 32u * j + 16u * h;  // element offset of the run within its 128-group
+  }
+
+  uint4 wq[D][R];
+  uint32_t sc[D][R];
+  uint4 av[kPrep][2];
+
+#define BQMM_LOAD_W(slot, sl)                                                      \
+  do {                                                                             \
+    const uint32_t c_ = min((uint32_t)(sl) * L + li, C - 1u);                      \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) {                                \
+      wq[slot][r] = *reinterpret_cast<const uint4 *>(wrow[r] + 16u * c_);          \
+      sc[slot][r] = srow[r][c_ >> 1];                                              \
+    }                                                                              \
+  } while (0)
+
+#define BQMM_LOAD_A(regs, sl)                                                      \
+  do {                                                                             \
+    _Pragma("unroll") for (int q = 0; q < kPrep; ++q) {                            \
+      const uint32_t c_ = min((uint32_t)(sl) * L + it_cl[q], C - 1u);              \
+      const uint16_t *p_ = act + it_src[q] + 128u * (c_ >> 1);                     \
+      regs[q][0] = *reinterpret_cast<const uint4 *>(p_);                           \
+      regs[q][1] = *reinterpret_cast<const uint4 *>(p_ + 8);                       \
+    }                                                                              \
+  } while (0)
+
+#define BQMM_PREP(regs, sl, buf)                                                   \
+  do {                                                                             \
+    _Pragma("unroll") for (int q = 0; q < kPrep; ++q) {                            \
+      /* whole waves past the last item skip (kItems is a multiple of 64) */       \
+      if (kItems % kThreads != 0 && tid + (uint32_t)(kThreads * q) >= (uint32_t)kItems) continue; \
+      const bool live_ = (uint32_t)(sl) * L + it_cl[q] < C;                        \
+      uint32_t Dw_[8] = {regs[q][0].x, regs[q][0].y, regs[q][0].z, regs[q][0].w,  \
+                         regs[q][1].x, regs[q][1].y, regs[q][1].z, regs[q][1].w};  \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i) Dw_[i] = live_ ? Dw_[i] : 0u;  \
+      uint32_t p_[8];                                                              \
+      act_pairs(Dw_, p_);                                                          \
+      const uint32_t j_ = it_j[q];                                                 \
+      const float b_ = field_bias(Dw_, bias_weight(j_));                           \
+      uint32_t *dst_ = lds + (buf) * kBuf + it_cl[q] * CS + it_m[q] * kRowDw;      \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                \
+        *reinterpret_cast<uint2 *>(dst_ + 8 * i + 2 * j_) =                        \
+            make_uint2(p_[2 * i], p_[2 * i + 1]);                                  \
+      dst_[32 + j_] = __float_as_uint(b_);                                         \
+    }                                                                              \
+  } while (0)
+
+  const CodeConsts K = code_consts();
+  float oacc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) oacc[r][m] = 0.0f;
+
+// One (word i, activation row m) unit: 8 activation pairs from LDS feed
+// 8 R dot2.  The next unit's LDS reads are issued before this unit's dot2s.
+// After each unit its accumulators pass through an empty asm that also
+// redefines the LDS offset, so the reads of unit u + 2 cannot be hoisted above
+// the dot2s of unit u: without it the compiler issues every read of the chunk
+// up front (32 M registers).
+#define BQMM_COMPUTE(slot, buf)                                                    \
+  do {                                                                             \
+    uint32_t off_ = (buf) * kBuf + li * CS;                                        \
+    float acc_[R][M];                                                              \
+    _Pragma("unroll") for (int m = 0; m < M; ++m) {                                \
+      const uint4 bq_ = *reinterpret_cast<const uint4 *>(lds + off_ + m * kRowDw + 32); \
+      const float nb_ = -((__uint_as_float(bq_.x) + __uint_as_float(bq_.y)) +      \
+                          (__uint_as_float(bq_.z) + __uint_as_float(bq_.w)));      \
+      _Pragma("unroll") for (int r = 0; r < R; ++r) acc_[r][m] = nb_;              \
+    }                                                                              \
+    uint4 pa_ = *reinterpret_cast<const uint4 *>(lds + off_);                      \
+    uint4 pb_ = *reinterpret_cast<const uint4 *>(lds + off_ + 4);                  \
+    uint32_t wp_[R][8];                                                            \
+    _Pragma("unroll") for (int u_ = 0; u_ < 4 * M; ++u_) {                         \
+      const int i = u_ / M, m = u_ % M;                                            \
+      if (m == 0) {                                                                \
+        _Pragma("unroll") for (int r = 0; r < R; ++r) {                            \
+          const uint32_t x_ = (i == 0) ? wq[slot][r].x : (i == 1) ? wq[slot][r].y  \
+                            : (i == 2) ? wq[slot][r].z : wq[slot][r].w;            \
+          word_pairs(x_, K, wp_[r]);                                               \
+        }                                                                          \
+      }                                                                            \
+      const uint32_t P_[8] = {pa_.x, pa_.y, pa_.z, pa_.w, pb_.x, pb_.y, pb_.z, pb_.w}; \
+      if (u_ + 1 < 4 * M) {                                                        \
+        const int i2 = (u_ + 1) / M, m2 = (u_ + 1) % M;                            \
+        pa_ = *reinterpret_cast<const uint4 *>(lds + off_ + m2 * kRowDw + 8 * i2);     \
+        pb_ = *reinterpret_cast<const uint4 *>(lds + off_ + m2 * kRowDw + 8 * i2 + 4); \
+      }                                                                            \
+      _Pragma("unroll") for (int r = 0; r < R; ++r)                                \
+        _Pragma("unroll") for (int qq = 0; qq < 8; ++qq)                           \
+          acc_[r][m] = dot2(wp_[r][qq], P_[qq], acc_[r][m]);                       \
+      _Pragma("unroll") for (int r = 0; r < R; ++r)                                \
+        asm volatile("" : "+v"(off_) : "v"(acc_[r][m]));                           \
+    }                                                                              \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) {                                \
+      const float d_ = f16_bits_to_f32(sc[slot][r]);                               \
+      _Pragma("unroll") for (int m = 0; m < M; ++m)                                \
+        oacc[r][m] = fmaf(d_, acc_[r][m], oacc[r][m]);                             \
+    }                                                                              \
+  } while (0)
+
+  // Prologue: activations of slices 0 and 1, then D slices of weights, so
+  // that the loads pending at the loop entry are in the same order (the
+  // activations of the next prep ahead of the weights) as at its back edge.
+  {
+    uint4 av0[kPrep][2];
+    BQMM_LOAD_A(av0, 0);
+    BQMM_LOAD_A(av, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < D; ++u) BQMM_LOAD_W(u, u);
+    BQMM_PREP(av0, 0, 0);
+  }
+  __syncthreads();
+
+  // Full groups of D slices.  Every load is unconditional (clamped past the
+  // end): a load under a branch would be merged into its slot registers at
+  // the join with a copy that waits for it, draining the prefetch.
+  uint32_t s0 = 0;
+  for (; s0 + D <= ns; s0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const uint32_t sl = s0 + u;
+      BQMM_COMPUTE(u, sl & 1u);
+      BQMM_PREP(av, sl + 1u, (sl + 1u) & 1u);
+      BQMM_LOAD_A(av, sl + 2u);
+      __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead
+      BQMM_LOAD_W(u, sl + D);
+      __syncthreads();
+    }
+  }
+  // The last ns - s0 < D slices: their weights and activations are already
+  // loaded, so these steps issue no loads.
+#pragma unroll
+  for (int u = 0; u < D - 1; ++u) {
+    const uint32_t sl = s0 + u;
+    if (sl < ns) {
+      BQMM_COMPUTE(u, sl & 1u);
+      if (sl + 1u < ns) {
+        BQMM_PREP(av, sl + 1u, (sl + 1u) & 1u);
+        __syncthreads();
+      }
+    }
+  }
+#undef BQMM_LOAD_W
+#undef BQMM_LOAD_A
+#undef BQMM_PREP
+#undef BQMM_COMPUTE
+
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      oacc[r][m] = (L == 16) ? row16_sum(oacc[r][m]) : half_wave_sum(oacc[r][m]);
+  if (li == (uint32_t)L - 1u) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t row = row_base + r;
+      if (row < n) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) out[(uint64_t)m * n + row] = (uint16_t)f32_to_bf16_rne(oacc[r][m]);
+      }
+    }
+  }
+}
+
+// Launch shapes (measured): wide outputs (gate/up, n = 17408) take 16-lane
+// groups of three rows (48 rows per workgroup, one slice = 1024 k); narrow
+// outputs with a long k (down, n = 5120, k = 17408) take 32-lane groups of four
+// rows (32 rows per workgroup).  More rows per lane amortize the activation
+// prep and the LDS reads over more weight bytes.
+#ifndef BQMM_GEMVM_WIDE_R
+#define BQMM_GEMVM_WIDE_R 3
+#endif
+#ifndef BQMM_GEMVM_WIDE_L
+#define BQMM_GEMVM_WIDE_L 16
+#endif
+#ifndef BQMM_GEMVM_NARROW_R
+#define BQMM_GEMVM_NARROW_R 4
+#endif
+#ifndef BQMM_GEMVM_NARROW_L
+#define BQMM_GEMVM_NARROW_L 32
+#endif
+#ifndef BQMM_GEMVM_SLOTS
+#define BQMM_GEMVM_SLOTS 3
+#endif
+#ifndef BQMM_GEMVM_WIDE_N
+#define BQMM_GEMVM_WIDE_N 8192
+#endif
+
+template <int M, int R, int L>
+hipError_t launch_gemvm_shape(const void *act, const void *w, void *out, uint32_t n, uint32_t k,
+                              hipStream_t s) {
+  constexpr uint32_t rows = (kThreads / L) * R;
+  const uint32_t blocks = (n + rows - 1) / rows;
+  hipLaunchKernelGGL((q2_0_gemvm_kernel<M, R, L, BQMM_GEMVM_SLOTS>), dim3(blocks), dim3(kThreads), 0, s,
                      static_cast<const uint16_t *>(act), static_cast<const uint8_t *>(w),
                      static_cast<uint16_t *>(out), n, k);
   return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_gemvm(const void *act, const void *w, void *out, uint32_t n, uint32_t k,
+                        hipStream_t s) {
+  if (n >= BQMM_GEMVM_WIDE_N)
+    return launch_gemvm_shape<M, BQMM_GEMVM_WIDE_R, BQMM_GEMVM_WIDE_L>(act, w, out, n, k, s);
+  return launch_gemvm_shape<M, BQMM_GEMVM_NARROW_R, BQMM_GEMVM_NARROW_L>(act, w, out, n, k, s);
 }
 
 }  // namespace
@@ -298,15 +555,18 @@ hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t 
                        static_cast<uint16_t *>(out), n, k);
     return hipGetLastError();
   }
+  // From m = 6 on the per-code multiply-adds outweigh the code unpacking and
+  // the matrix-core kernel is faster (its staged scales bound k).
+  if (m >= kMinMMfma && k <= kMaxKMfma) return launch_q2_0_gemv_mfma(act, w, out, m, n, k, s);
   switch (m) {
-    case 1: return launch_m<1>(act, w, out, n, k, s);
-    case 2: return launch_m<2>(act, w, out, n, k, s);
-    case 3: return launch_m<3>(act, w, out, n, k, s);
-    case 4: return launch_m<4>(act, w, out, n, k, s);
-    case 5: return launch_m<5>(act, w, out, n, k, s);
-    case 6: return launch_m<6>(act, w, out, n, k, s);
-    case 7: return launch_m<7>(act, w, out, n, k, s);
-    case 8: return launch_m<8>(act, w, out, n, k, s);
+    case 1: return launch_gemvm<1>(act, w, out, n, k, s);
+    case 2: return launch_gemvm<2>(act, w, out, n, k, s);
+    case 3: return launch_gemvm<3>(act, w, out, n, k, s);
+    case 4: return launch_gemvm<4>(act, w, out, n, k, s);
+    case 5: return launch_gemvm<5>(act, w, out, n, k, s);
+    case 6: return launch_gemvm<6>(act, w, out, n, k, s);
+    case 7: return launch_gemvm<7>(act, w, out, n, k, s);
+    case 8: return launch_gemvm<8>(act, w, out, n, k, s);
     default: return hipErrorInvalidValue;
   }
 }

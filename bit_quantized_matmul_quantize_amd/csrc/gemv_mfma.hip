@@ -1,0 +1,243 @@
+// Q2_0 GEMV for small verify batches (m = 2..8) on bf16 matrix cores.
+//
+// [page layers/dense_ffn_decode_batch.rs, fn forward_km_q2:
+//  q2_0_gemv_vec_batchm on the bf16 activations, output bf16.]
+//
+// out[i][r] = sum_k a[i][k] * d[r][g] * (c - 2), fp32 accumulation.
+//
+// With m activation rows every code feeds m multiply-adds.  On the vector
+// ALU that work grows with m (two per v_dot2), so this kernel moves the
+// products to v_mfma_f32_16x16x32_bf16 and keeps the VALU for the
+// m-independent part: turning codes into bf16 (about 0.75 ops per code).
+// Its weight loads cover 32 bytes of each of 16 rows per instruction, which
+// streams at about half the rate of row-contiguous loads, so the dispatcher
+// uses it only where the per-code ALU work of the vector kernel is larger.
+//
+// Operands of one MFMA (field j of a 128-group, i.e. the 32 k of block j):
+//   A = 16 weight rows x 32 k; lane l holds row l % 16 and the 8 consecutive
+//       k = 8 (l / 16) .. +7, i.e. bytes 8 (l / 16) .. +7 of the row's group,
+//       code field j, as bf16 2^e_j + c (mantissa OR, exact; e = 7, 5, 3, 2);
+//   B = the same 32 k x 16 columns; column j' < m is activation row j',
+//       loaded as 8 consecutive bf16 straight from memory (columns >= m
+//       repeat row m - 1 and their outputs are dropped);
+//   D = 16 x 16 fp32; lane l holds column l % 16, rows 4 (l / 16) .. +3.
+// The constant part of the codes is removed by four more MFMAs per group with
+// A = -(2^e_j + 2) everywhere: their sum, -sum_k (2^e + 2) a_k for every row,
+// is the accumulator the weight MFMAs start from, so each group's result is
+// sum_k (c_k - 2) a_k exactly as the four weight MFMAs see it.  It is shared
+// by the T row tiles a wave processes.  The group scale is applied once per
+// group and output with an fma.
+//
+// Work split (at most 128 VGPRs, so that two 8-wave workgroups share a CU):
+// a wave owns T tiles of 16 rows and a contiguous range of the
+// 128-groups; the W waves of a workgroup split k between them and add their
+// partial sums through LDS at the end.  There is no barrier in the main loop.
+// A wave's weight scales are staged once in LDS ([group][row], so one 8-byte
+// read gives the four rows of a lane's outputs).  Loads run P groups ahead,
+// unconditionally from clamped addresses.
+#include "bqmm_internal.h"
+
+namespace bqmm {
+namespace {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t vconst_(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t and_or_(uint32_t x, uint32_t mask, uint32_t bits) {
+  return (x & mask) | bits;
+}
+
+__device__ __forceinline__ v8bf as_bf8(v4u x) { return __builtin_bit_cast(v8bf, x); }
+
+__device__ __forceinline__ v4f mfma(v4u a, v4u b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b), c, 0, 0, 0);
+}
+
+#ifndef BQMM_GEMVX_WIDE_N
+#define BQMM_GEMVX_WIDE_N 8192
+#endif
+#ifndef BQMM_GEMVX_MINW
+#define BQMM_GEMVX_MINW 2
+#endif
+#ifndef BQMM_GEMVX_P
+#define BQMM_GEMVX_P 2
+#endif
+
+template <int M, int T, int W, int P>
+__global__ __launch_bounds__(64 * W, W >= 8 ? BQMM_GEMVX_MINW : 1) void q2_0_gemv_mfma_kernel(const uint16_t *__restrict__ act,
+                                                                const uint8_t *__restrict__ w,
+                                                                uint16_t *__restrict__ out,
+                                                                uint32_t n, uint32_t k) {
+  static_assert(M >= 1 && M <= 16, "one MFMA column per activation row");
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+  constexpr uint32_t kRows = 16 * T;
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  const uint32_t lr = lane & 15u, lg = lane >> 4;
+  const uint32_t G = k >> 7;
+  const uint32_t gmax = (G + W - 1) / W;  // groups of the widest wave
+  const uint32_t gb = wave * G / W, ng = (wave + 1) * G / W - gb;  // >= 1 since G >= W
+  const uint32_t row0 = blockIdx.x * kRows;
+  const uint16_t *scales = reinterpret_cast<const uint16_t *>(w + (uint64_t)n * k / 4u);
+
+  // weight bytes 8 lg .. +7 of each 128-group of this lane's rows (rows past n
+  // read row n - 1 and are not stored)
+  const uint8_t *wp[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const uint32_t row = min(row0 + 16u * t + lr, n - 1u);
+    wp[t] = w + (uint64_t)row * (k >> 2) + 8u * lg;
+  }
+  const uint16_t *ap = act + (uint64_t)min(lr, (uint32_t)M - 1u) * k + 8u * lg;
+
+  uint2 cq[P][T];
+  uint4 aq[P][4];
+#define BQMM_LOADX(slot, gi)                                                        \
+  do {                                                                              \
+    const uint32_t g_ = gb + min((uint32_t)(gi), ng - 1u);                          \
+    _Pragma("unroll") for (int t = 0; t < T; ++t)                                   \
+      cq[slot][t] = *reinterpret_cast<const uint2 *>(wp[t] + 32u * g_);             \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                   \
+      aq[slot][j] = *reinterpret_cast<const uint4 *>(ap + 128u * g_ + 32u * j);     \
+  } while (0)
+
+#pragma unroll
+  for (int p = 0; p < P; ++p) BQMM_LOADX(p, p);
+
+  // stage this wave's scales: [group][row] fp16
+  uint16_t *sc = reinterpret_cast<uint16_t *>(smem) + wave * (kRows * gmax);
+  for (uint32_t i = lane; i < kRows * ng; i += 64u) {
+    const uint32_t r = i / ng, gi = i - r * ng;
+    const uint32_t row = min(row0 + r, n - 1u);
+    sc[gi * kRows + r] = scales[(uint64_t)row * G + gb + gi];
+  }
+
+  const uint32_t M0 = vconst_(0x00030003u), M1 = vconst_(0x000C000Cu), M2 = vconst_(0x00300030u),
+                 M3 = vconst_(0x00600060u);
+  const uint32_t G0 = vconst_(0x43004300u), G1 = vconst_(0x42004200u), G2 = vconst_(0x41004100u),
+                 G3 = vconst_(0x40804080u);
+  // -(2^e_j + 2) = -130, -34, -10, -6 in bf16, eight per lane
+  const v4u NK[4] = {v4u{0xC302C302u, 0xC302C302u, 0xC302C302u, 0xC302C302u},
+                     v4u{0xC208C208u, 0xC208C208u, 0xC208C208u, 0xC208C208u},
+                     v4u{0xC120C120u, 0xC120C120u, 0xC120C120u, 0xC120C120u},
+                     v4u{0xC0C0C0C0u, 0xC0C0C0C0u, 0xC0C0C0C0u, 0xC0C0C0C0u}};
+
+  v4f acc_out[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc_out[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // bytes of a code word reordered to (b0, b2, b1, b3): b0/b1 then sit in the
+  // low bytes of the two halves (fields at bits 2j, 16 + 2j), b2/b3 after >> 8
+#define BQMM_COMPUTEX(slot, gi)                                                     \
+  do {                                                                              \
+    v4f nb_ = v4f{0.f, 0.f, 0.f, 0.f};                                              \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                 \
+      const v4u b_ = {aq[slot][j].x, aq[slot][j].y, aq[slot][j].z, aq[slot][j].w};  \
+      nb_ = mfma(NK[j], b_, nb_);                                                   \
+    }                                                                               \
+    const uint16_t *srow_ = sc + (uint32_t)(gi) * kRows + 4u * lg;                  \
+    _Pragma("unroll") for (int t = 0; t < T; ++t) {                                 \
+      const uint32_t x0_ = __builtin_amdgcn_perm(cq[slot][t].x, cq[slot][t].x, 0x03010200u); \
+      const uint32_t x1_ = __builtin_amdgcn_perm(cq[slot][t].y, cq[slot][t].y, 0x03010200u); \
+      const uint32_t y0_ = x0_ >> 8, y1_ = x1_ >> 8;                                \
+      const v4u a0_ = {and_or_(x0_, M0, G0), and_or_(y0_, M0, G0), and_or_(x1_, M0, G0), and_or_(y1_, M0, G0)}; \
+      const v4u a1_ = {and_or_(x0_, M1, G1), and_or_(y0_, M1, G1), and_or_(x1_, M1, G1), and_or_(y1_, M1, G1)}; \
+      const v4u a2_ = {and_or_(x0_, M2, G2), and_or_(y0_, M2, G2), and_or_(x1_, M2, G2), and_or_(y1_, M2, G2)}; \
+      const v4u a3_ = {and_or_(x0_ >> 1, M3, G3), and_or_(y0_ >> 1, M3, G3),        \
+                       and_or_(x1_ >> 1, M3, G3), and_or_(y1_ >> 1, M3, G3)};       \
+      v4f s_ = mfma(a0_, v4u{aq[slot][0].x, aq[slot][0].y, aq[slot][0].z, aq[slot][0].w}, nb_); \
+      s_ = mfma(a1_, v4u{aq[slot][1].x, aq[slot][1].y, aq[slot][1].z, aq[slot][1].w}, s_);      \
+      s_ = mfma(a2_, v4u{aq[slot][2].x, aq[slot][2].y, aq[slot][2].z, aq[slot][2].w}, s_);      \
+      s_ = mfma(a3_, v4u{aq[slot][3].x, aq[slot][3].y, aq[slot][3].z, aq[slot][3].w}, s_);      \
+      const uint2 dv_ = *reinterpret_cast<const uint2 *>(srow_ + 16u * t);          \
+      acc_out[t][0] = fmaf(f16_bits_to_f32(dv_.x & 0xFFFFu), s_[0], acc_out[t][0]); \
+      acc_out[t][1] = fmaf(f16_bits_to_f32(dv_.x >> 16), s_[1], acc_out[t][1]);     \
+      acc_out[t][2] = fmaf(f16_bits_to_f32(dv_.y & 0xFFFFu), s_[2], acc_out[t][2]); \
+      acc_out[t][3] = fmaf(f16_bits_to_f32(dv_.y >> 16), s_[3], acc_out[t][3]);     \
+    }                                                                               \
+  } while (0)
+
+  uint32_t gi0 = 0;
+  for (; gi0 + P <= ng; gi0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      BQMM_COMPUTEX(u, gi0 + u);
+      BQMM_LOADX(u, gi0 + u + P);
+    }
+  }
+  // the last ng - gi0 < P groups are already loaded
+#pragma unroll
+  for (int u = 0; u < P - 1; ++u)
+    if (gi0 + u < ng) BQMM_COMPUTEX(u, gi0 + u);
+#undef BQMM_LOADX
+#undef BQMM_COMPUTEX
+
+  // add the W waves' partial sums: red[wave][t][i][lane]
+  __syncthreads();  // every wave is done with its scales (the same LDS)
+  float *red = reinterpret_cast<float *>(smem);
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[((wave * T + t) * 4 + i) * 64 + lane] = acc_out[t][i];
+  __syncthreads();
+  for (uint32_t o = tid; o < kRows * M; o += 64u * W) {
+    const uint32_t col = o / kRows, r = o - col * kRows;
+    const uint32_t t = r >> 4, rr = r & 15u;
+    const uint32_t src = ((t * 4 + (rr & 3u)) * 64) + (rr >> 2) * 16 + col;
+    float s = 0.0f;
+#pragma unroll
+    for (int v = 0; v < W; ++v) s += red[v * T * 256 + src];
+    if (row0 + r < n) out[(uint64_t)col * n + row0 + r] = (uint16_t)f32_to_bf16_rne(s);
+  }
+}
+
+template <int M, int W, int T>
+hipError_t launch_w(const void *act, const void *w, void *out, uint32_t n, uint32_t k,
+                    hipStream_t s) {
+  constexpr int P = BQMM_GEMVX_P;
+  const uint32_t G = k >> 7;
+  const uint32_t gmax = (G + W - 1) / W;
+  const size_t sc_bytes = (size_t)W * 16 * T * gmax * 2;
+  const size_t red_bytes = (size_t)W * T * 4 * 64 * 4;
+  const size_t lds = sc_bytes > red_bytes ? sc_bytes : red_bytes;
+  if (lds > 65536) return hipErrorInvalidValue;  // k too large for the staged scales
+  const uint32_t blocks = (n + 16 * T - 1) / (16 * T);
+  hipLaunchKernelGGL((q2_0_gemv_mfma_kernel<M, T, W, P>), dim3(blocks), dim3(64 * W), lds, s,
+                     static_cast<const uint16_t *>(act), static_cast<const uint8_t *>(w),
+                     static_cast<uint16_t *>(out), n, k);
+  return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_m(const void *act, const void *w, void *out, uint32_t n, uint32_t k,
+                    hipStream_t s) {
+  const uint32_t G = k >> 7;
+  // Eight waves split k when it has at least eight groups (W <= G is
+  // required); narrow outputs take one 16-row tile per wave so that the grid
+  // still has a few waves per SIMD.
+  if (G >= 8) {
+    if (n >= BQMM_GEMVX_WIDE_N) return launch_w<M, 8, 2>(act, w, out, n, k, s);
+    return launch_w<M, 8, 1>(act, w, out, n, k, s);
+  }
+  return launch_w<M, 1, 2>(act, w, out, n, k, s);
+}
+
+}  // namespace
+
+hipError_t launch_q2_0_gemv_mfma(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
+                                 uint32_t k, hipStream_t s) {
+  switch (m) {
+    case 6: return launch_m<6>(act, w, out, n, k, s);
+    case 7: return launch_m<7>(act, w, out, n, k, s);
+    case 8: return launch_m<8>(act, w, out, n, k, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace bqmm

@@ -40,7 +40,14 @@ def test_decode_qkvz_full(gpu):
                                         (1, 50, 5120, 29),      # m=1: three 32-chunk slices, ragged last
                                         (1, 100, 17408, 30),    # m=1: prep loop over 1088 items
                                         (1, 3, 33792, 31),      # m=1 beyond the LDS-staged kernel's k
-                                        (1, 4096 + 37, 2048, 32)])
+                                        (1, 4096 + 37, 2048, 32),
+                                        # batched kernel, wide launch shape (n >= 8192):
+                                        (2, 8192 + 45, 1152, 33),   # two slices, the second ragged
+                                        (4, 9000, 384, 34),         # one slice, fewer than the prefetch depth
+                                        (7, 8192, 4096, 35),        # one full prefetch round plus one slice
+                                        (1, 8192 + 5, 36864, 36),   # m=1 beyond the decode kernel's k
+                                        # matrix-core kernel (m >= 6): one wave per group range
+                                        (6, 100, 512, 39), (6, 8192 + 16, 2048, 40)])
 def test_ragged(gpu, m, n, k, seed):
     g = inputs.rng(seed)
     w = inputs.q2_0_weight(g, n, k)
@@ -63,15 +70,39 @@ def test_closed_forms(gpu):
     assert np.array_equal(y, np.repeat(x.sum(1, keepdims=True).astype(np.float64), n, axis=1))
 
 
-def test_batch_rows_independent(gpu):
-    # row r of the m = 8 run equals row r of the m = 2 run
+@pytest.mark.parametrize("m,n,k", [(1, 300, 2048), (1, 64, 33792), (3, 640, 5120), (8, 8200, 1024)])
+def test_zero_activations(gpu, m, n, k):
+    # zero activations give exactly zero outputs (no bias residue)
+    w = inputs.q2_0_weight(inputs.rng(37), n, k)
+    act = np.zeros((m, k), np.uint16)
+    assert not _gemv(gpu, act, w, m, n, k).any()
+
+
+def test_sparse_activations(gpu):
+    # a mostly-zero activation row (every 7th value kept) against the oracle
+    m, n, k = 3, 700, 5120
+    g = inputs.rng(38)
+    w = inputs.q2_0_weight(g, n, k)
+    act = inputs.activations(g, m, k)
+    act[:, np.arange(k) % 7 != 0] = 0
+    R = oracle.q2_0_gemv(act, w, m, n, k)
+    assert row_error(_gemv(gpu, act, w, m, n, k), R) <= ROW_TOL
+
+
+@pytest.mark.parametrize("m", [2, 5, 8])
+def test_batch_rows_independent(gpu, m):
+    # a row's output does not depend on the other rows of the batch: replacing
+    # rows 1.. leaves row 0 bit-identical (same m, same kernel)
     n, k = 640, 2048
     g = inputs.rng(27)
     w = inputs.q2_0_weight(g, n, k)
-    act = inputs.activations(g, 8, k)
-    y8 = _gemv(gpu, act, w, 8, n, k)
-    y2 = _gemv(gpu, act[:2], w, 2, n, k)
-    assert np.array_equal(y8[:2], y2)
+    act = inputs.activations(g, m, k)
+    other = act.copy()
+    other[1:] = inputs.activations(g, m - 1, k)
+    y = _gemv(gpu, act, w, m, n, k)
+    y_other = _gemv(gpu, other, w, m, n, k)
+    assert np.array_equal(y[0], y_other[0])
+    assert row_error(y, oracle.q2_0_gemv(act, w, m, n, k)) <= ROW_TOL
 
 
 def test_silu_mul(gpu):

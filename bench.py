@@ -13,7 +13,9 @@ graph and replayed between HIP events:
   prefill  : quantize_act_q8_1 + q2_0_mmq_gemm, qkvz n=12288 k=2048, m in
              {512, 2048}; and the bf16 fallback (dequant + dense GEMM) at m=512;
   ffn      : m=4096 FFN prefill, Q2_0 and Q4_K: quantize, gate and up MMQ,
-             silu_mul, quantize, down MMQ.
+             silu_mul, quantize, down MMQ;
+  copy     : (not in the default set) a plain 256 MiB device-to-device copy,
+             the known-size reference for the HBM byte counters.
 The JSON line reports the decode GEMV (the workload the headline metric is
 quoted on) as `value`, with its roofline and the CPU oracle beside it; the
 other legs are reported under "legs".  Inputs are resident in HBM before the
@@ -39,6 +41,13 @@ BF16_PEAK_TFLOPS = 2516.0    # MI355X dense bf16 MFMA, published
 
 DECODE_CALLS = 1000
 DECODE_COPIES = 80
+COPY_BYTES = 256 << 20
+# Per-dispatch HBM traffic of the decode GEMV, measured with rocprofv3 counters
+# (FETCH_SIZE + WRITE_SIZE, scaled by the same counters on the copy leg).  The
+# figure is reported only while the kernel source still matches the hash the
+# counters were taken with.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_gemv_n12288_k2048.txt")
+GEMV_SOURCE = os.path.join(ROOT, "bit_quantized_matmul_quantize_amd", "csrc", "gemv.hip")
 
 
 def parse():
@@ -137,7 +146,7 @@ def decode_leg(bq, dev, d):
 
     bytes_per_call = w0.numel() + 2 * k + 2 * n
     leg = Leg("decode_gemv_m1", fn, wcopies + [x, y], DECODE_CALLS, DECODE_CALLS * bytes_per_call, "GB/s",
-              "q2_0_gemv_kernel<1>", HBM_PEAK_GBS, "hbm")
+              "q2_0_gemv1_kernel", HBM_PEAK_GBS, "hbm")
     return leg, bytes_per_call
 
 
@@ -156,8 +165,32 @@ def verify_leg(bq, dev, W, act, m, H, I):
         bq.q2_0_gemv_vec_batchm(g_, wd, o_, m, H, I)
 
     work = wg.numel() + wu.numel() + wd.numel() + m * (6 * H + 12 * I)
+    kname = "q2_0_gemv_mfma_kernel" if m >= 6 else "q2_0_gemvm_kernel"
     return Leg(f"verify_ffn_m{m}", fn, [wg, wu, wd, x, g_, u_, o_], 4, work, "GB/s",
-               f"q2_0_gemv_kernel<{m}> x3 + silu_mul", HBM_PEAK_GBS, "hbm")
+               f"{kname}<{m}> x3 + silu_mul", HBM_PEAK_GBS, "hbm")
+
+
+def copy_leg(dev):
+    """Known-size reference for the byte counters: one 256 MiB device copy."""
+    import torch
+    src = torch.randint(0, 255, (COPY_BYTES,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    return Leg("copy_256MiB", lambda: dst.copy_(src), [src, dst], 1, 2 * COPY_BYTES, "GB/s",
+               "device copy", HBM_PEAK_GBS, "hbm")
+
+
+def measured_traffic():
+    """Bytes per decode GEMV dispatch from the committed counter summary, or
+    None when it is missing or was taken on another version of the kernel."""
+    import hashlib
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
+        digest = hashlib.sha256(open(GEMV_SOURCE, "rb").read()).hexdigest()
+        if fields.get("kernel_source_sha256", "").strip() != digest:
+            return None
+        return int(fields["traffic_bytes_per_launch"].strip())
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def prefill_legs(bq, dev, p):
@@ -245,6 +278,8 @@ def main():
         legs += prefill_legs(bq, dev, inputs.prefill_qkvz())
     if "ffn" in legs_wanted:
         legs += ffn_legs(bq, dev, inputs.prefill_ffn())
+    if "copy" in legs_wanted:
+        legs.append(copy_leg(dev))
 
     # ---- timed region ----------------------------------------------------------
     log(f"{len(legs)} legs captured; warmup {args.warmup}, steps {args.steps}")
@@ -277,7 +312,9 @@ def main():
         s = summaries["decode_gemv_m1"]
         result["value"] = s["value"]
         result["roofline"] = {"bound": "hbm", "achieved": s["value"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": s["frac_of_peak"], "traffic": None,
+                              "frac": s["frac_of_peak"], "traffic": measured_traffic(),
+                              "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                              "copy-calibrated)",
                               "kernel": s["kernel"], "us_per_launch": s["us_per_launch"],
                               "bytes_per_launch": decode_ctx["bytes_per_call"]}
     if "prefill_mmq_m2048" in summaries:

@@ -9,7 +9,8 @@ graph and replayed between HIP events:
              rotated through 80 copies (537 MB > the 256 MB Infinity Cache) so
              that every call streams its weight from HBM;
   verify   : q2_0_gemv_vec_batchm chain gate -> up -> silu_mul -> down,
-             FFN [17408, 5120] / [5120, 17408], m in {2, 3, 4, 8};
+             FFN [17408, 5120] / [5120, 17408], m in {2, 3, 4, 8}; and the same
+             step with q2_0_gemv_gate_up_silu in place of the first three calls;
   prefill  : quantize_act_q8_1 + q2_0_mmq_gemm, qkvz n=12288 k=2048, m in
              {512, 2048}; and the bf16 fallback (dequant + dense GEMM) at m=512;
   ffn      : m=4096 FFN prefill, Q2_0 and Q4_K: quantize, gate and up MMQ,
@@ -170,6 +171,24 @@ def verify_leg(bq, dev, W, act, m, H, I):
                f"{kname}<{m}> x3 + silu_mul", HBM_PEAK_GBS, "hbm")
 
 
+def verify_fused_leg(bq, dev, W, act, m, H, I):
+    """The same FFN step with gate, up and silu_mul fused into one launch."""
+    import torch
+    wg, wu, wd = W
+    x = torch.from_numpy(np.ascontiguousarray(act[:m]).view(np.int16)).to(dev).view(torch.bfloat16)
+    h_ = torch.empty((m, I), dtype=torch.bfloat16, device=dev)
+    o_ = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
+
+    def fn():
+        bq.q2_0_gemv_gate_up_silu(x, wg, wu, h_, m, I, H)
+        bq.q2_0_gemv_vec_batchm(h_, wd, o_, m, H, I)
+
+    work = wg.numel() + wu.numel() + wd.numel() + m * (2 * H + 4 * I)
+    kname = "q2_0_gemv_mfma_kernel" if m >= 6 else "q2_0_gemvm_kernel"
+    return Leg(f"verify_ffn_fused_m{m}", fn, [wg, wu, wd, x, h_, o_], 2, work, "GB/s",
+               f"{kname}<{m}> gate+up+silu, {kname}<{m}> down", HBM_PEAK_GBS, "hbm")
+
+
 def copy_leg(dev):
     """Known-size reference for the byte counters: one 256 MiB device copy."""
     import torch
@@ -274,6 +293,8 @@ def main():
         W = tuple(torch.from_numpy(f[key]).to(dev) for key in ("wg", "wu", "wd"))
         for m in (2, 3, 4, 8):
             legs.append(verify_leg(bq, dev, W, f["act"], m, f["hidden"], f["inter"]))
+        for m in (2, 3, 4, 8):
+            legs.append(verify_fused_leg(bq, dev, W, f["act"], m, f["hidden"], f["inter"]))
     if "prefill" in legs_wanted:
         legs += prefill_legs(bq, dev, inputs.prefill_qkvz())
     if "ffn" in legs_wanted:

@@ -32,6 +32,7 @@ EXPORTS = {
     "q2_0_mmq_gemm": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
     "q2_0_gemv_vec": (_I, [_P, _P, _P, _U32, _U32, _P]),
     "q2_0_gemv_vec_batchm": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
+    "q2_0_gemv_gate_up_silu": (_I, [_P, _P, _P, _P, _U32, _U32, _U32, _P]),
     "dequant_q2_0_to_bf16": (_I, [_P, _P, _U32, _U32, _U32, _P]),
     "dense_gemm_bf16": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
     "q2_0_prefill_gemm": (_I, [_P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _I, _P]),
@@ -135,6 +136,12 @@ def q2_0_gemv_vec(act, w_q2, out, n: int, k: int, stream=None):
 def q2_0_gemv_vec_batchm(act, w_q2, out, m: int, n: int, k: int, stream=None):
     _check(lib().q2_0_gemv_vec_batchm(_ptr(_bf16(act, "act")), _ptr(_u8(w_q2, "w_q2")),
                                       _ptr(_bf16(out, "out")), m, n, k, _stream(stream)))
+
+
+def q2_0_gemv_gate_up_silu(act, w_gate, w_up, out, m: int, n: int, k: int, stream=None):
+    _check(lib().q2_0_gemv_gate_up_silu(_ptr(_bf16(act, "act")), _ptr(_u8(w_gate, "w_gate")),
+                                        _ptr(_u8(w_up, "w_up")), _ptr(_bf16(out, "out")), m, n, k,
+                                        _stream(stream)))
 
 
 def dequant_q2_0_to_bf16(w_q2, out, n: int, k: int, group: int = 128, stream=None):

@@ -34,6 +34,12 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// silu(g) * u = g / (1 + exp(-g)) * u in binary32: the silu_mul kernel and the
+// fused gate/up GEMV epilogue share it, so both round the same value.
+__device__ __forceinline__ float silu_mul_f32(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
 // ---- launchers (one per kernel source) ------------------------------------
 // Arguments are validated by the C ABI layer before these are called.
 
@@ -45,8 +51,14 @@ hipError_t launch_silu_mul(const void *gate, const void *up, void *out, uint64_t
                            hipStream_t s);
 hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
                             uint32_t k, hipStream_t s);
+hipError_t launch_q2_0_gemv_gate_up_silu(const void *act, const void *w_gate, const void *w_up,
+                                         void *out, uint32_t m, uint32_t n, uint32_t k,
+                                         hipStream_t s);
 hipError_t launch_q2_0_gemv_mfma(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
                                  uint32_t k, hipStream_t s);
+hipError_t launch_q2_0_gemv_mfma_gate_up(const void *act, const void *w_gate, const void *w_up,
+                                         void *out, uint32_t m, uint32_t n, uint32_t k,
+                                         hipStream_t s);
 hipError_t launch_q2_0_mmq(const void *act_q8, const void *w, void *out, int32_t *dots,
                            uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m,
                            uint32_t n, uint32_t k, hipStream_t s);

@@ -163,6 +163,18 @@ int q2_0_gemv_vec_batchm(const void *act_bf16, const void *w_q2, void *out_bf16,
                     "q2_0_gemv_vec_batchm");
 }
 
+int q2_0_gemv_gate_up_silu(const void *act_bf16, const void *w_gate_q2, const void *w_up_q2,
+                           void *out_bf16, uint32_t m, uint32_t n, uint32_t k, void *stream) {
+  int st = check_gemv("q2_0_gemv_gate_up_silu", act_bf16, w_gate_q2, out_bf16, m, n, k);
+  if (st != BQ_OK) return st;
+  REQUIRE(w_up_q2, BQ_EINVAL, "q2_0_gemv_gate_up_silu: null pointer");
+  REQUIRE(aligned16(w_up_q2), BQ_EALIGN, "q2_0_gemv_gate_up_silu: buffers must be 16-byte aligned");
+  REQUIRE(out_bf16 != act_bf16, BQ_EINVAL, "q2_0_gemv_gate_up_silu: out must not alias act");
+  return hip_status(bqmm::launch_q2_0_gemv_gate_up_silu(act_bf16, w_gate_q2, w_up_q2, out_bf16, m, n, k,
+                                                        as_stream(stream)),
+                    "q2_0_gemv_gate_up_silu");
+}
+
 static int check_dequant(const void *w, const void *out, uint32_t n, uint32_t k, uint32_t group) {
   REQUIRE(w && out, BQ_EINVAL, "dequant_q2_0_to_bf16: null pointer");
   REQUIRE(n >= 1 && k >= 1, BQ_EINVAL, "dequant_q2_0_to_bf16: n=%u k=%u must be >= 1", n, k);

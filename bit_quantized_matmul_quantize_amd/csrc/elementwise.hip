@@ -47,10 +47,6 @@ __global__ __launch_bounds__(256) void dequant_q2_0_kernel(const uint8_t *__rest
   }
 }
 
-__device__ __forceinline__ float silu_mul_f32(float g, float u) {
-  return g / (1.0f + expf(-g)) * u;
-}
-
 // out = bf16(silu(gate) * up), silu(g) = g / (1 + exp(-g)) in binary32.
 // [page layers/dense_ffn_decode_batch.rs, fn forward_km_q2: silu_mul over
 //  m * intermediate elements, output over the gate buffer.]  Eight elements

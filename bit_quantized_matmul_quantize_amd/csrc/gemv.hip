@@ -290,13 +290,16 @@ __host__ __device__ constexpr int gemvm_chunk_dwords(int M) {
   return ((kRowDw * M / 4) % 2 == 1) ? kRowDw * M : kRowDw * M + 4;
 }
 
-template <int M, int R, int L, int D>
+template <int M, int R, int L, int D, int NW>
 __global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__restrict__ act,
                                                               const uint8_t *__restrict__ w,
+                                                              const uint8_t *__restrict__ w2,
                                                               uint16_t *__restrict__ out, uint32_t n,
                                                               uint32_t k) {
   static_assert(L == 16 || L == 32, "lane group of 16 or 32");
   static_assert(D == 2 || D == 3, "the load-free tail covers at most two slices");
+  static_assert(NW == 1 || NW == 2, "one weight, or gate and up");
+  constexpr int RR = NW * R;  // weight rows per lane: R rows of each weight
   constexpr int CS = gemvm_chunk_dwords(M);
   constexpr int kGroups = kThreads / L;
   constexpr int kItems = 4 * L * M;  // prep items per slice: (chunk, field, activation row)
@@ -309,16 +312,21 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__
   const uint32_t tid = threadIdx.x, li = tid % L, grp = tid / L;
   const uint32_t row_base = (blockIdx.x * kGroups + grp) * R;
   const uint32_t ns = (C + L - 1) / L;
-  const uint16_t *scales = reinterpret_cast<const uint16_t *>(w + (uint64_t)n * k / 4u);
 
-  // rows past n compute on row n-1 and are not stored
-  const uint8_t *wrow[R];
-  const uint16_t *srow[R];
+  // rows past n compute on row n-1 and are not stored; with two weights, lane
+  // rows R .. 2R-1 are the up rows matching gate rows 0 .. R-1
+  const uint8_t *wrow[RR];
+  const uint16_t *srow[RR];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint32_t row = min(row_base + r, n - 1u);
-    wrow[r] = w + (uint64_t)row * (k >> 2);
-    srow[r] = scales + (uint64_t)row * G;
+  for (int v = 0; v < NW; ++v) {
+    const uint8_t *wv = v == 0 ? w : w2;
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(wv + (uint64_t)n * k / 4u);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t row = min(row_base + r, n - 1u);
+      wrow[v * R + r] = wv + (uint64_t)row * (k >> 2);
+      srow[v * R + r] = scales + (uint64_t)row * G;
+    }
   }
 
   // This thread's prep items.  Item order (m, group, field, half) makes
@@ -337,14 +345,14 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__
     it_src[q] = m * k + 32u * j + 16u * h;  // element offset of the run within its 128-group
   }
 
-  uint4 wq[D][R];
-  uint32_t sc[D][R];
+  uint4 wq[D][RR];
+  uint32_t sc[D][RR];
   uint4 av[kPrep][2];
 
 #define BQMM_LOAD_W(slot, sl)                                                      \
   do {                                                                             \
     const uint32_t c_ = min((uint32_t)(sl) * L + li, C - 1u);                      \
-    _Pragma("unroll") for (int r = 0; r < R; ++r) {                                \
+    _Pragma("unroll") for (int r = 0; r < RR; ++r) {                               \
       wq[slot][r] = *reinterpret_cast<const uint4 *>(wrow[r] + 16u * c_);          \
       sc[slot][r] = srow[r][c_ >> 1];                                              \
     }                                                                              \
@@ -382,9 +390,9 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__
   } while (0)
 
   const CodeConsts K = code_consts();
-  float oacc[R][M];
+  float oacc[RR][M];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < RR; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) oacc[r][m] = 0.0f;
 
@@ -397,20 +405,20 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__
 #define BQMM_COMPUTE(slot, buf)                                                    \
   do {                                                                             \
     uint32_t off_ = (buf) * kBuf + li * CS;                                        \
-    float acc_[R][M];                                                              \
+    float acc_[RR][M];                                                              \
     _Pragma("unroll") for (int m = 0; m < M; ++m) {                                \
       const uint4 bq_ = *reinterpret_cast<const uint4 *>(lds + off_ + m * kRowDw + 32); \
       const float nb_ = -((__uint_as_float(bq_.x) + __uint_as_float(bq_.y)) +      \
                           (__uint_as_float(bq_.z) + __uint_as_float(bq_.w)));      \
-      _Pragma("unroll") for (int r = 0; r < R; ++r) acc_[r][m] = nb_;              \
+      _Pragma("unroll") for (int r = 0; r < RR; ++r) acc_[r][m] = nb_;              \
     }                                                                              \
     uint4 pa_ = *reinterpret_cast<const uint4 *>(lds + off_);                      \
     uint4 pb_ = *reinterpret_cast<const uint4 *>(lds + off_ + 4);                  \
-    uint32_t wp_[R][8];                                                            \
+    uint32_t wp_[RR][8];                                                            \
     _Pragma("unroll") for (int u_ = 0; u_ < 4 * M; ++u_) {                         \
       const int i = u_ / M, m = u_ % M;                                            \
       if (m == 0) {                                                                \
-        _Pragma("unroll") for (int r = 0; r < R; ++r) {                            \
+        _Pragma("unroll") for (int r = 0; r < RR; ++r) {                            \
           const uint32_t x_ = (i == 0) ? wq[slot][r].x : (i == 1) ? wq[slot][r].y  \
                             : (i == 2) ? wq[slot][r].z : wq[slot][r].w;            \
           word_pairs(x_, K, wp_[r]);                                               \
@@ -422,13 +430,13 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__
         pa_ = *reinterpret_cast<const uint4 *>(lds + off_ + m2 * kRowDw + 8 * i2);     \
         pb_ = *reinterpret_cast<const uint4 *>(lds + off_ + m2 * kRowDw + 8 * i2 + 4); \
       }                                                                            \
-      _Pragma("unroll") for (int r = 0; r < R; ++r)                                \
+      _Pragma("unroll") for (int r = 0; r < RR; ++r)                                \
         _Pragma("unroll") for (int qq = 0; qq < 8; ++qq)                           \
           acc_[r][m] = dot2(wp_[r][qq], P_[qq], acc_[r][m]);                       \
-      _Pragma("unroll") for (int r = 0; r < R; ++r)                                \
+      _Pragma("unroll") for (int r = 0; r < RR; ++r)                                \
         asm volatile("" : "+v"(off_) : "v"(acc_[r][m]));                           \
     }                                                                              \
-    _Pragma("unroll") for (int r = 0; r < R; ++r) {                                \
+    _Pragma("unroll") for (int r = 0; r < RR; ++r) {                                \
       const float d_ = f16_bits_to_f32(sc[slot][r]);                               \
       _Pragma("unroll") for (int m = 0; m < M; ++m)                                \
         oacc[r][m] = fmaf(d_, acc_[r][m], oacc[r][m]);                             \
@@ -484,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__
 #undef BQMM_COMPUTE
 
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < RR; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m)
       oacc[r][m] = (L == 16) ? row16_sum(oacc[r][m]) : half_wave_sum(oacc[r][m]);
@@ -494,7 +502,15 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__
       const uint32_t row = row_base + r;
       if (row < n) {
 #pragma unroll
-        for (int m = 0; m < M; ++m) out[(uint64_t)m * n + row] = (uint16_t)f32_to_bf16_rne(oacc[r][m]);
+        for (int m = 0; m < M; ++m) {
+          uint32_t h = f32_to_bf16_rne(oacc[r][m]);
+          if (NW == 2) {
+            // gate and up rounded to bf16 as separate GEMV outputs would be
+            const float g = bf16_to_f32(h), u = bf16_to_f32(f32_to_bf16_rne(oacc[R + r][m]));
+            h = f32_to_bf16_rne(silu_mul_f32(g, u));
+          }
+          out[(uint64_t)m * n + row] = (uint16_t)h;
+        }
       }
     }
   }
@@ -517,6 +533,9 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__
 #ifndef BQMM_GEMVM_NARROW_L
 #define BQMM_GEMVM_NARROW_L 32
 #endif
+#ifndef BQMM_GEMVM_FUSED_R
+#define BQMM_GEMVM_FUSED_R 2
+#endif
 #ifndef BQMM_GEMVM_SLOTS
 #define BQMM_GEMVM_SLOTS 3
 #endif
@@ -524,23 +543,37 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__
 #define BQMM_GEMVM_WIDE_N 8192
 #endif
 
-template <int M, int R, int L>
-hipError_t launch_gemvm_shape(const void *act, const void *w, void *out, uint32_t n, uint32_t k,
-                              hipStream_t s) {
+template <int M, int R, int L, int NW>
+hipError_t launch_gemvm_shape(const void *act, const void *w, const void *w2, void *out, uint32_t n,
+                              uint32_t k, hipStream_t s) {
   constexpr uint32_t rows = (kThreads / L) * R;
   const uint32_t blocks = (n + rows - 1) / rows;
-  hipLaunchKernelGGL((q2_0_gemvm_kernel<M, R, L, BQMM_GEMVM_SLOTS>), dim3(blocks), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((q2_0_gemvm_kernel<M, R, L, BQMM_GEMVM_SLOTS, NW>), dim3(blocks), dim3(kThreads), 0, s,
                      static_cast<const uint16_t *>(act), static_cast<const uint8_t *>(w),
-                     static_cast<uint16_t *>(out), n, k);
+                     static_cast<const uint8_t *>(w2), static_cast<uint16_t *>(out), n, k);
   return hipGetLastError();
 }
 
+// The lane-group width L follows n in the same way for the single and the
+// fused (gate + up) kernel, so that each output row is summed in the same
+// order by both and the fused result equals GEMV, GEMV, silu_mul bit for bit.
 template <int M>
 hipError_t launch_gemvm(const void *act, const void *w, void *out, uint32_t n, uint32_t k,
                         hipStream_t s) {
   if (n >= BQMM_GEMVM_WIDE_N)
-    return launch_gemvm_shape<M, BQMM_GEMVM_WIDE_R, BQMM_GEMVM_WIDE_L>(act, w, out, n, k, s);
-  return launch_gemvm_shape<M, BQMM_GEMVM_NARROW_R, BQMM_GEMVM_NARROW_L>(act, w, out, n, k, s);
+    return launch_gemvm_shape<M, BQMM_GEMVM_WIDE_R, BQMM_GEMVM_WIDE_L, 1>(act, w, nullptr, out, n, k, s);
+  return launch_gemvm_shape<M, BQMM_GEMVM_NARROW_R, BQMM_GEMVM_NARROW_L, 1>(act, w, nullptr, out, n, k, s);
+}
+
+// Two rows of each weight per lane up to m = 5; one from m = 6 on, where the
+// accumulators of 4 rows x m columns would crowd out the weight prefetch.
+template <int M>
+hipError_t launch_gemvm_gate_up(const void *act, const void *wg, const void *wu, void *out, uint32_t n,
+                                uint32_t k, hipStream_t s) {
+  constexpr int R = M >= 6 ? 1 : BQMM_GEMVM_FUSED_R;
+  if (n >= BQMM_GEMVM_WIDE_N)
+    return launch_gemvm_shape<M, R, BQMM_GEMVM_WIDE_L, 2>(act, wg, wu, out, n, k, s);
+  return launch_gemvm_shape<M, R, BQMM_GEMVM_NARROW_L, 2>(act, wg, wu, out, n, k, s);
 }
 
 }  // namespace
@@ -567,6 +600,26 @@ hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t 
     case 6: return launch_gemvm<6>(act, w, out, n, k, s);
     case 7: return launch_gemvm<7>(act, w, out, n, k, s);
     case 8: return launch_gemvm<8>(act, w, out, n, k, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_q2_0_gemv_gate_up_silu(const void *act, const void *w_gate, const void *w_up,
+                                         void *out, uint32_t m, uint32_t n, uint32_t k,
+                                         hipStream_t s) {
+  // One launch for every m, on the kernel the single GEMV uses for that m, so
+  // the result equals GEMV, GEMV, silu_mul.
+  if (m >= kMinMMfma && k <= kMaxKMfma)
+    return launch_q2_0_gemv_mfma_gate_up(act, w_gate, w_up, out, m, n, k, s);
+  switch (m) {
+    case 1: return launch_gemvm_gate_up<1>(act, w_gate, w_up, out, n, k, s);
+    case 2: return launch_gemvm_gate_up<2>(act, w_gate, w_up, out, n, k, s);
+    case 3: return launch_gemvm_gate_up<3>(act, w_gate, w_up, out, n, k, s);
+    case 4: return launch_gemvm_gate_up<4>(act, w_gate, w_up, out, n, k, s);
+    case 5: return launch_gemvm_gate_up<5>(act, w_gate, w_up, out, n, k, s);
+    case 6: return launch_gemvm_gate_up<6>(act, w_gate, w_up, out, n, k, s);
+    case 7: return launch_gemvm_gate_up<7>(act, w_gate, w_up, out, n, k, s);
+    case 8: return launch_gemvm_gate_up<8>(act, w_gate, w_up, out, n, k, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -70,38 +70,40 @@ __device__ __forceinline__ v4f mfma(v4u a, v4u b, v4f c) {
 #define BQMM_GEMVX_P 2
 #endif
 
-template <int M, int T, int W, int P>
+template <int M, int T, int W, int P, int NW>
 __global__ __launch_bounds__(64 * W, W >= 8 ? BQMM_GEMVX_MINW : 1) void q2_0_gemv_mfma_kernel(const uint16_t *__restrict__ act,
                                                                 const uint8_t *__restrict__ w,
+                                                                const uint8_t *__restrict__ w2,
                                                                 uint16_t *__restrict__ out,
                                                                 uint32_t n, uint32_t k) {
   static_assert(M >= 1 && M <= 16, "one MFMA column per activation row");
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+  static_assert(NW == 1 || NW == 2, "one weight, or gate and up");
   constexpr uint32_t kRows = 16 * T;
+  constexpr int TT = NW * T;  // tile slots: T of each weight (same rows)
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint32_t lr = lane & 15u, lg = lane >> 4;
   const uint32_t G = k >> 7;
   const uint32_t gmax = (G + W - 1) / W;  // groups of the widest wave
   const uint32_t gb = wave * G / W, ng = (wave + 1) * G / W - gb;  // >= 1 since G >= W
   const uint32_t row0 = blockIdx.x * kRows;
-  const uint16_t *scales = reinterpret_cast<const uint16_t *>(w + (uint64_t)n * k / 4u);
 
   // weight bytes 8 lg .. +7 of each 128-group of this lane's rows (rows past n
-  // read row n - 1 and are not stored)
-  const uint8_t *wp[T];
+  // read row n - 1 and are not stored); slots T .. 2T-1 are the up rows
+  const uint8_t *wp[TT];
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const uint32_t row = min(row0 + 16u * t + lr, n - 1u);
-    wp[t] = w + (uint64_t)row * (k >> 2) + 8u * lg;
+  for (int t = 0; t < TT; ++t) {
+    const uint32_t row = min(row0 + 16u * (t % T) + lr, n - 1u);
+    wp[t] = (t < T ? w : w2) + (uint64_t)row * (k >> 2) + 8u * lg;
   }
   const uint16_t *ap = act + (uint64_t)min(lr, (uint32_t)M - 1u) * k + 8u * lg;
 
-  uint2 cq[P][T];
+  uint2 cq[P][TT];
   uint4 aq[P][4];
 #define BQMM_LOADX(slot, gi)                                                        \
   do {                                                                              \
     const uint32_t g_ = gb + min((uint32_t)(gi), ng - 1u);                          \
-    _Pragma("unroll") for (int t = 0; t < T; ++t)                                   \
+    _Pragma("unroll") for (int t = 0; t < TT; ++t)                                  \
       cq[slot][t] = *reinterpret_cast<const uint2 *>(wp[t] + 32u * g_);             \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                   \
       aq[slot][j] = *reinterpret_cast<const uint4 *>(ap + 128u * g_ + 32u * j);     \
@@ -110,12 +112,16 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? BQMM_GEMVX_MINW : 1) void q2_0_gem
 #pragma unroll
   for (int p = 0; p < P; ++p) BQMM_LOADX(p, p);
 
-  // stage this wave's scales: [group][row] fp16
-  uint16_t *sc = reinterpret_cast<uint16_t *>(smem) + wave * (kRows * gmax);
-  for (uint32_t i = lane; i < kRows * ng; i += 64u) {
-    const uint32_t r = i / ng, gi = i - r * ng;
-    const uint32_t row = min(row0 + r, n - 1u);
-    sc[gi * kRows + r] = scales[(uint64_t)row * G + gb + gi];
+  // stage this wave's scales: [weight][group][row] fp16
+  uint16_t *sc = reinterpret_cast<uint16_t *>(smem) + wave * (NW * kRows * gmax);
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>((v == 0 ? w : w2) + (uint64_t)n * k / 4u);
+    for (uint32_t i = lane; i < kRows * ng; i += 64u) {
+      const uint32_t r = i / ng, gi = i - r * ng;
+      const uint32_t row = min(row0 + r, n - 1u);
+      sc[(v * gmax + gi) * kRows + r] = scales[(uint64_t)row * G + gb + gi];
+    }
   }
 
   const uint32_t M0 = vconst_(0x00030003u), M1 = vconst_(0x000C000Cu), M2 = vconst_(0x00300030u),
@@ -128,9 +134,9 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? BQMM_GEMVX_MINW : 1) void q2_0_gem
                      v4u{0xC120C120u, 0xC120C120u, 0xC120C120u, 0xC120C120u},
                      v4u{0xC0C0C0C0u, 0xC0C0C0C0u, 0xC0C0C0C0u, 0xC0C0C0C0u}};
 
-  v4f acc_out[T];
+  v4f acc_out[TT];
 #pragma unroll
-  for (int t = 0; t < T; ++t) acc_out[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TT; ++t) acc_out[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // bytes of a code word reordered to (b0, b2, b1, b3): b0/b1 then sit in the
   // low bytes of the two halves (fields at bits 2j, 16 + 2j), b2/b3 after >> 8
@@ -141,8 +147,8 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? BQMM_GEMVX_MINW : 1) void q2_0_gem
       const v4u b_ = {aq[slot][j].x, aq[slot][j].y, aq[slot][j].z, aq[slot][j].w};  \
       nb_ = mfma(NK[j], b_, nb_);                                                   \
     }                                                                               \
-    const uint16_t *srow_ = sc + (uint32_t)(gi) * kRows + 4u * lg;                  \
-    _Pragma("unroll") for (int t = 0; t < T; ++t) {                                 \
+    _Pragma("unroll") for (int t = 0; t < TT; ++t) {                                \
+      const uint16_t *srow_ = sc + ((t / T) * gmax + (uint32_t)(gi)) * kRows + 4u * lg; \
       const uint32_t x0_ = __builtin_amdgcn_perm(cq[slot][t].x, cq[slot][t].x, 0x03010200u); \
       const uint32_t x1_ = __builtin_amdgcn_perm(cq[slot][t].y, cq[slot][t].y, 0x03010200u); \
       const uint32_t y0_ = x0_ >> 8, y1_ = x1_ >> 8;                                \
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? BQMM_GEMVX_MINW : 1) void q2_0_gem
       s_ = mfma(a1_, v4u{aq[slot][1].x, aq[slot][1].y, aq[slot][1].z, aq[slot][1].w}, s_);      \
       s_ = mfma(a2_, v4u{aq[slot][2].x, aq[slot][2].y, aq[slot][2].z, aq[slot][2].w}, s_);      \
       s_ = mfma(a3_, v4u{aq[slot][3].x, aq[slot][3].y, aq[slot][3].z, aq[slot][3].w}, s_);      \
-      const uint2 dv_ = *reinterpret_cast<const uint2 *>(srow_ + 16u * t);          \
+      const uint2 dv_ = *reinterpret_cast<const uint2 *>(srow_ + 16u * (t % T));    \
       acc_out[t][0] = fmaf(f16_bits_to_f32(dv_.x & 0xFFFFu), s_[0], acc_out[t][0]); \
       acc_out[t][1] = fmaf(f16_bits_to_f32(dv_.x >> 16), s_[1], acc_out[t][1]);     \
       acc_out[t][2] = fmaf(f16_bits_to_f32(dv_.y & 0xFFFFu), s_[2], acc_out[t][2]); \
@@ -182,9 +188,9 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? BQMM_GEMVX_MINW : 1) void q2_0_gem
   __syncthreads();  // every wave is done with its scales (the same LDS)
   float *red = reinterpret_cast<float *>(smem);
 #pragma unroll
-  for (int t = 0; t < T; ++t)
+  for (int t = 0; t < TT; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[((wave * T + t) * 4 + i) * 64 + lane] = acc_out[t][i];
+    for (int i = 0; i < 4; ++i) red[((wave * TT + t) * 4 + i) * 64 + lane] = acc_out[t][i];
   __syncthreads();
   for (uint32_t o = tid; o < kRows * M; o += 64u * W) {
     const uint32_t col = o / kRows, r = o - col * kRows;
@@ -192,40 +198,49 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? BQMM_GEMVX_MINW : 1) void q2_0_gem
     const uint32_t src = ((t * 4 + (rr & 3u)) * 64) + (rr >> 2) * 16 + col;
     float s = 0.0f;
 #pragma unroll
-    for (int v = 0; v < W; ++v) s += red[v * T * 256 + src];
-    if (row0 + r < n) out[(uint64_t)col * n + row0 + r] = (uint16_t)f32_to_bf16_rne(s);
+    for (int v = 0; v < W; ++v) s += red[v * TT * 256 + src];
+    uint32_t h = f32_to_bf16_rne(s);
+    if (NW == 2) {
+      // the up row's sum, then silu(gate) * up on both values rounded to bf16
+      float su = 0.0f;
+#pragma unroll
+      for (int v = 0; v < W; ++v) su += red[v * TT * 256 + T * 256 + src];
+      h = f32_to_bf16_rne(silu_mul_f32(bf16_to_f32(h), bf16_to_f32(f32_to_bf16_rne(su))));
+    }
+    if (row0 + r < n) out[(uint64_t)col * n + row0 + r] = (uint16_t)h;
   }
 }
 
-template <int M, int W, int T>
-hipError_t launch_w(const void *act, const void *w, void *out, uint32_t n, uint32_t k,
+template <int M, int W, int T, int NW>
+hipError_t launch_w(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
                     hipStream_t s) {
   constexpr int P = BQMM_GEMVX_P;
   const uint32_t G = k >> 7;
   const uint32_t gmax = (G + W - 1) / W;
-  const size_t sc_bytes = (size_t)W * 16 * T * gmax * 2;
-  const size_t red_bytes = (size_t)W * T * 4 * 64 * 4;
+  const size_t sc_bytes = (size_t)W * NW * 16 * T * gmax * 2;
+  const size_t red_bytes = (size_t)W * NW * T * 4 * 64 * 4;
   const size_t lds = sc_bytes > red_bytes ? sc_bytes : red_bytes;
   if (lds > 65536) return hipErrorInvalidValue;  // k too large for the staged scales
   const uint32_t blocks = (n + 16 * T - 1) / (16 * T);
-  hipLaunchKernelGGL((q2_0_gemv_mfma_kernel<M, T, W, P>), dim3(blocks), dim3(64 * W), lds, s,
+  hipLaunchKernelGGL((q2_0_gemv_mfma_kernel<M, T, W, P, NW>), dim3(blocks), dim3(64 * W), lds, s,
                      static_cast<const uint16_t *>(act), static_cast<const uint8_t *>(w),
-                     static_cast<uint16_t *>(out), n, k);
+                     static_cast<const uint8_t *>(w2), static_cast<uint16_t *>(out), n, k);
   return hipGetLastError();
 }
 
-template <int M>
-hipError_t launch_m(const void *act, const void *w, void *out, uint32_t n, uint32_t k,
+// Eight waves split k when it has at least eight groups (W <= G is required);
+// narrow outputs take one 16-row tile per wave so that the grid still has a
+// few waves per SIMD.  The fused gate/up kernel takes one tile of each weight
+// (the same rows), so per-row sums are identical to the single kernel's.
+template <int M, int NW>
+hipError_t launch_m(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
                     hipStream_t s) {
   const uint32_t G = k >> 7;
-  // Eight waves split k when it has at least eight groups (W <= G is
-  // required); narrow outputs take one 16-row tile per wave so that the grid
-  // still has a few waves per SIMD.
   if (G >= 8) {
-    if (n >= BQMM_GEMVX_WIDE_N) return launch_w<M, 8, 2>(act, w, out, n, k, s);
-    return launch_w<M, 8, 1>(act, w, out, n, k, s);
+    if (NW == 1 && n >= BQMM_GEMVX_WIDE_N) return launch_w<M, 8, 2, NW>(act, w, w2, out, n, k, s);
+    return launch_w<M, 8, 1, NW>(act, w, w2, out, n, k, s);
   }
-  return launch_w<M, 1, 2>(act, w, out, n, k, s);
+  return launch_w<M, 1, 2, NW>(act, w, w2, out, n, k, s);
 }
 
 }  // namespace
@@ -233,9 +248,20 @@ hipError_t launch_m(const void *act, const void *w, void *out, uint32_t n, uint3
 hipError_t launch_q2_0_gemv_mfma(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
                                  uint32_t k, hipStream_t s) {
   switch (m) {
-    case 6: return launch_m<6>(act, w, out, n, k, s);
-    case 7: return launch_m<7>(act, w, out, n, k, s);
-    case 8: return launch_m<8>(act, w, out, n, k, s);
+    case 6: return launch_m<6, 1>(act, w, nullptr, out, n, k, s);
+    case 7: return launch_m<7, 1>(act, w, nullptr, out, n, k, s);
+    case 8: return launch_m<8, 1>(act, w, nullptr, out, n, k, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_q2_0_gemv_mfma_gate_up(const void *act, const void *w_gate, const void *w_up,
+                                         void *out, uint32_t m, uint32_t n, uint32_t k,
+                                         hipStream_t s) {
+  switch (m) {
+    case 6: return launch_m<6, 2>(act, w_gate, w_up, out, n, k, s);
+    case 7: return launch_m<7, 2>(act, w_gate, w_up, out, n, k, s);
+    case 8: return launch_m<8, 2>(act, w_gate, w_up, out, n, k, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -123,6 +123,19 @@ int q2_0_gemv_vec(const void *act_bf16, const void *w_q2, void *out_bf16,
 int q2_0_gemv_vec_batchm(const void *act_bf16, const void *w_q2, void *out_bf16,
                          uint32_t m, uint32_t n, uint32_t k, void *stream);
 
+/* Fused FFN gate/up GEMV with the SiLU-gated product, m = 1..8 rows:
+ *   out[i][r] = bf16_rne(silu(g) * u),  g = bf16_rne(sum_k act[i][k] * deq(w_gate)[r][k]),
+ *                                       u = bf16_rne(sum_k act[i][k] * deq(w_up)[r][k]),
+ * i.e. q2_0_gemv_vec_batchm on both weights followed by silu_mul_bf16, in one
+ * launch that reads the activations once.  For m = 2..8 the result equals
+ * that three-call chain bit for bit (same kernels, same summation order).
+ * [page layers/dense_ffn_decode_batch.rs, fn forward_km_q2: gate and up
+ *  GEMVs, then silu_mul into the gate buffer.]
+ * act [m][k] bf16; w_gate, w_up: Q2_0 [n][k] group 128; out [m][n] bf16 and
+ * must not alias act.  k % 128 == 0, n >= 1, m > 8 -> BQ_EUNSUPPORTED. */
+int q2_0_gemv_gate_up_silu(const void *act_bf16, const void *w_gate_q2, const void *w_up_q2,
+                           void *out_bf16, uint32_t m, uint32_t n, uint32_t k, void *stream);
+
 /* Q2_0 weight -> bf16 [n][k]: bf16_rne(d*(c - 2)) (exact product, one
  * rounding).  [page layers/qwen3_ssm/init_q2.rs, fn qkvz_q2_prefill_gemm,
  *  fallback: dequant_q2_0_gn_to_bf16(w, scratch, n, k, group).]

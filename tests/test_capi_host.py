@@ -52,6 +52,7 @@ P = ctypes.c_void_p
 A = P(0x10000)          # aligned fake device addresses: never dereferenced,
 B = P(0x20000)          # every case below fails validation first
 C = P(0x30000)
+D = P(0x40000)
 MIS = P(0x30008)        # misaligned
 
 
@@ -71,6 +72,11 @@ def _err(bq):
     (lambda l: l.q2_0_gemv_vec(A, B, None, 256, 512, None), -1, "null"),
     (lambda l: l.q2_0_gemv_vec_batchm(A, B, C, 9, 256, 512, None), -2, "m=9"),
     (lambda l: l.q2_0_gemv_vec_batchm(A, B, C, 0, 256, 512, None), -1, "m must"),
+    (lambda l: l.q2_0_gemv_gate_up_silu(A, B, C, D, 9, 256, 512, None), -2, "m=9"),
+    (lambda l: l.q2_0_gemv_gate_up_silu(A, B, None, D, 2, 256, 512, None), -1, "null"),
+    (lambda l: l.q2_0_gemv_gate_up_silu(A, B, MIS, D, 2, 256, 512, None), -3, "aligned"),
+    (lambda l: l.q2_0_gemv_gate_up_silu(A, B, C, A, 2, 256, 512, None), -1, "alias"),
+    (lambda l: l.q2_0_gemv_gate_up_silu(A, B, C, D, 2, 256, 300, None), -1, "group size 128"),
     (lambda l: l.dequant_q2_0_to_bf16(A, B, 4, 512, 48, None), -2, "multiple of 32"),
     (lambda l: l.dequant_q2_0_to_bf16(A, B, 4, 480, 128, None), -1, "not a multiple"),
     (lambda l: l.dense_gemm_bf16(A, B, C, 4, 4, 96, None), -1, "multiple of 64"),

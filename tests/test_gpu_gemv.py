@@ -154,3 +154,66 @@ def test_verify_ffn_chain(gpu, ffn, m):
     Rend = oracle.q2_0_gemv(oracle.silu_mul_bf16(oracle.round_bf16(Rg), oracle.round_bf16(Ru)),
                             ffn["wd"], m, H, I)
     assert row_error(y, Rend) <= ROW_TOL
+
+
+# ---- fused gate/up GEMV with the SiLU-gated product ---------------------------
+
+def _fused(gpu, act, wg, wu, m, n, k):
+    out = empty_bf16((m, n), gpu)
+    bq.q2_0_gemv_gate_up_silu(dev_bf16(act, gpu), dev_u8(wg, gpu), dev_u8(wu, gpu), out, m, n, k)
+    return host_bits(out)
+
+
+def _chain_bits(gpu, act, wg, wu, m, n, k):
+    """GEMV, GEMV, silu_mul on the device: the calls the fused entry replaces."""
+    x = dev_bf16(act, gpu)
+    g, u = empty_bf16((m, n), gpu), empty_bf16((m, n), gpu)
+    if m == 1:
+        bq.q2_0_gemv_vec(x, dev_u8(wg, gpu), g, n, k)
+        bq.q2_0_gemv_vec(x, dev_u8(wu, gpu), u, n, k)
+    else:
+        bq.q2_0_gemv_vec_batchm(x, dev_u8(wg, gpu), g, m, n, k)
+        bq.q2_0_gemv_vec_batchm(x, dev_u8(wu, gpu), u, m, n, k)
+    bq.silu_mul_bf16(g, u, g, m * n)
+    return host_bits(g)
+
+
+@pytest.mark.parametrize("m,n,k,seed", [(2, 17408, 5120, 41), (3, 300, 1152, 42), (5, 8192 + 45, 2048, 43),
+                                        (4, 33, 17408, 44), (8, 17408, 5120, 46), (6, 300, 1152, 47),
+                                        (7, 40, 512, 48)])
+def test_fused_gate_up_equals_chain(gpu, m, n, k, seed):
+    # m >= 2: the fused kernel sums every row exactly as the single GEMV does
+    g = inputs.rng(seed)
+    wg, wu = inputs.q2_0_weight(g, n, k), inputs.q2_0_weight(g, n, k)
+    act = inputs.activations(g, m, k, outliers=True)
+    assert np.array_equal(_fused(gpu, act, wg, wu, m, n, k), _chain_bits(gpu, act, wg, wu, m, n, k))
+
+
+@pytest.mark.parametrize("m", [1, 2, 6, 8])
+def test_fused_gate_up_ffn_chain(gpu, ffn, m):
+    # the verify FFN with the fused first stage, end to end against the oracle's
+    # chain (bf16 roundings at the same points)
+    H, I = ffn["hidden"], ffn["inter"]
+    x = ffn["act"][:m]
+    h_bits = _fused(gpu, x, ffn["wg"], ffn["wu"], m, I, H)
+    out = empty_bf16((m, H), gpu)
+    bq.q2_0_gemv_vec_batchm(dev_bf16(h_bits, gpu), dev_u8(ffn["wd"], gpu), out, m, H, I) if m > 1 else \
+        bq.q2_0_gemv_vec(dev_bf16(h_bits, gpu), dev_u8(ffn["wd"], gpu), out, H, I)
+    y = host_f64(out)
+    Rg = oracle.q2_0_gemv(x, ffn["wg"], m, I, H)
+    Ru = oracle.q2_0_gemv(x, ffn["wu"], m, I, H)
+    Rend = oracle.q2_0_gemv(oracle.silu_mul_bf16(oracle.round_bf16(Rg), oracle.round_bf16(Ru)),
+                            ffn["wd"], m, H, I)
+    assert row_error(y, Rend) <= ROW_TOL
+    # the fused output itself: each value within one bf16 step of silu(g)*u taken
+    # on the oracle's bf16-rounded gate and up, except where gate or up
+    # themselves rounded to a neighbouring bf16 value (a small fraction)
+    Rh = oracle.silu_mul_bf16(oracle.round_bf16(Rg), oracle.round_bf16(Ru))
+    assert np.mean(bf16_ulp_distance(h_bits, Rh) <= 1) > 0.99
+
+
+def test_fused_gate_up_zero_and_ragged(gpu):
+    n, k = 37, 384
+    g = inputs.rng(45)
+    wg, wu = inputs.q2_0_weight(g, n, k), inputs.q2_0_weight(g, n, k)
+    assert not inputs.bf16_bits_to_f32(_fused(gpu, np.zeros((3, k), np.uint16), wg, wu, 3, n, k)).any()

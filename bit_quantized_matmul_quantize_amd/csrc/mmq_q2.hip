@@ -205,6 +205,10 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
       if (i < 16) {
         const int sn = i >> 3, sm = (i >> 2) & 1, b = i & 3;
         D[i & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[sn][b], B[sm][b], zero16, 0, 0, 0);
+        // issue the MFMA ahead of the previous step's epilogue: left to itself
+        // the scheduler can sink it below, and the next step then waits for
+        // the result (a run of s_nop hazard padding at every such step)
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (i > 0) {
         const int p = i - 1;

@@ -199,6 +199,8 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
       if (i < 16) {
         const int sn = i >> 3, sm = (i >> 2) & 1, b = i & 3;
         D[i & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[sn][b], B[sm][b], zero16, 0, 0, 0);
+        // keep the MFMA ahead of the previous step's epilogue (see mmq_q2.hip)
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (i > 0) {
         const int p = i - 1;

@@ -198,7 +198,7 @@ static int check_dense(const void *a, const void *w, const void *out, uint32_t m
   REQUIRE(m >= 1 && n >= 1 && k >= 1, BQ_EINVAL, "dense_gemm_bf16: m=%u n=%u k=%u must be >= 1", m, n, k);
   REQUIRE(k % 64u == 0, BQ_EINVAL, "dense_gemm_bf16: k=%u must be a multiple of 64", k);
   REQUIRE(aligned16(a) && aligned16(w) && aligned16(out), BQ_EALIGN, "dense_gemm_bf16: buffers must be 16-byte aligned");
-  REQUIRE((m + 127u) / 128u <= kMaxGridY, BQ_EINVAL, "dense_gemm_bf16: m=%u too large", m);
+  REQUIRE((n + 127u) / 128u <= kMaxGridY, BQ_EINVAL, "dense_gemm_bf16: n=%u too large", n);
   return BQ_OK;
 }
 

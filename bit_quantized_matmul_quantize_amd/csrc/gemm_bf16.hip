@@ -5,9 +5,13 @@
 //  dense_gemm_bf16_pipelined runs on the original bf16 input.]
 //
 // bf16 matrix cores (v_mfma_f32_32x32x16_bf16), fp32 accumulation, bf16 out.
-// Tile 128 (n) x 128 (m), 4 waves of 64 x 64, k staged 64 at a time through
-// LDS.  The weight is the A operand so that a lane's 16 accumulators share
-// one output row and are stored as four 8-byte runs.
+// Tile 128 (n) x 128 (m), 4 waves of 64 x 64, k staged KS = 64 at a time
+// through two LDS stages: while stage s is multiplied, the registers holding
+// the global loads of step s + 1 are written into the other stage and the
+// loads of step s + 2 are already in flight, so one barrier per step and no
+// exposed load latency.  The weight is the A operand so that a lane's 16
+// accumulators share one output row and are stored as four 8-byte runs.
+// Rows past m or n load the last valid row and are not stored.
 #include "bqmm_internal.h"
 
 namespace bqmm {
@@ -17,17 +21,65 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BN = 128, BM = 128, KS = 64;
-constexpr int LDS_STRIDE = KS * 2 + 16;  // bytes per staged row
+constexpr int LDS_STRIDE = KS * 2 + 16;  // bytes per staged row; the pad spreads banks
 constexpr int kThreads = 256;
+constexpr int kTileBytes = BM * LDS_STRIDE;      // one operand tile (128 rows)
+constexpr int kStageBytes = 2 * kTileBytes;      // activation tile + weight tile
+constexpr int kLoads = BM * KS * 2 / 16 / kThreads;  // 16-byte loads per thread per operand (4)
 
-__global__ __launch_bounds__(kThreads) void dense_gemm_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 2) void dense_gemm_bf16_kernel(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ w, uint16_t *__restrict__ out,
     uint32_t m, uint32_t n, uint32_t k) {
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint8_t w_lds[BN * LDS_STRIDE];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
   const uint32_t wn = wave & 1u, wm = wave >> 1;
-  const uint32_t n_base = blockIdx.x * BN, m_base = blockIdx.y * BM;
+  // m tiles run consecutively (grid x), so the workgroups that share a weight
+  // tile are co-resident and read it from L2 rather than from memory
+  const uint32_t n_base = blockIdx.y * BN, m_base = blockIdx.x * BM;
+  const uint32_t nsteps = k / KS;
+
+  // This thread's rows and 16-byte column of each operand tile.  The staging
+  // registers are named scalars: as arrays, indexed inside the macros' loops,
+  // they were kept in scratch memory.
+  static_assert(kLoads == 4, "four 16-byte loads per operand and thread");
+  const uint32_t r0 = tid >> 3, col = (tid & 7u) * 8u;  // 8 bf16 = 16 bytes
+  const uint16_t *ap = a + (uint64_t)min(m_base + r0, m - 1u) * k + col;
+  const uint16_t *wp = w + (uint64_t)min(n_base + r0, n - 1u) * k + col;
+  // rows r0 + 32 i; rows past m (n) read the last valid row
+  const uint64_t ast[4] = {0, (uint64_t)(min(m_base + r0 + 32u, m - 1u) - min(m_base + r0, m - 1u)) * k,
+                           (uint64_t)(min(m_base + r0 + 64u, m - 1u) - min(m_base + r0, m - 1u)) * k,
+                           (uint64_t)(min(m_base + r0 + 96u, m - 1u) - min(m_base + r0, m - 1u)) * k};
+  const uint64_t wst[4] = {0, (uint64_t)(min(n_base + r0 + 32u, n - 1u) - min(n_base + r0, n - 1u)) * k,
+                           (uint64_t)(min(n_base + r0 + 64u, n - 1u) - min(n_base + r0, n - 1u)) * k,
+                           (uint64_t)(min(n_base + r0 + 96u, n - 1u) - min(n_base + r0, n - 1u)) * k};
+  const uint32_t soff = r0 * LDS_STRIDE + col * 2;
+  constexpr uint32_t kRowStep = 32 * LDS_STRIDE;
+
+  uint4 ra0, ra1, ra2, ra3, rw0, rw1, rw2, rw3;
+#define BQMM_GLOAD(step)                                                              \
+  do {                                                                                \
+    const uint64_t o_ = (uint64_t)(step) * KS;                                        \
+    ra0 = *reinterpret_cast<const uint4 *>(ap + ast[0] + o_);                         \
+    ra1 = *reinterpret_cast<const uint4 *>(ap + ast[1] + o_);                         \
+    ra2 = *reinterpret_cast<const uint4 *>(ap + ast[2] + o_);                         \
+    ra3 = *reinterpret_cast<const uint4 *>(ap + ast[3] + o_);                         \
+    rw0 = *reinterpret_cast<const uint4 *>(wp + wst[0] + o_);                         \
+    rw1 = *reinterpret_cast<const uint4 *>(wp + wst[1] + o_);                         \
+    rw2 = *reinterpret_cast<const uint4 *>(wp + wst[2] + o_);                         \
+    rw3 = *reinterpret_cast<const uint4 *>(wp + wst[3] + o_);                         \
+  } while (0)
+#define BQMM_STORE(st)                                                                \
+  do {                                                                                \
+    uint8_t *a_l = lds + (st) * kStageBytes + soff, *w_l = a_l + kTileBytes;          \
+    *reinterpret_cast<uint4 *>(a_l) = ra0;                                            \
+    *reinterpret_cast<uint4 *>(a_l + kRowStep) = ra1;                                 \
+    *reinterpret_cast<uint4 *>(a_l + 2 * kRowStep) = ra2;                             \
+    *reinterpret_cast<uint4 *>(a_l + 3 * kRowStep) = ra3;                             \
+    *reinterpret_cast<uint4 *>(w_l) = rw0;                                            \
+    *reinterpret_cast<uint4 *>(w_l + kRowStep) = rw1;                                 \
+    *reinterpret_cast<uint4 *>(w_l + 2 * kRowStep) = rw2;                             \
+    *reinterpret_cast<uint4 *>(w_l + 3 * kRowStep) = rw3;                             \
+  } while (0)
 
   v16f acc[2][2];
 #pragma unroll
@@ -37,26 +89,23 @@ __global__ __launch_bounds__(kThreads) void dense_gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  for (uint32_t k0 = 0; k0 < k; k0 += KS) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t c = tid + kThreads * i;
-      const uint32_t r = c >> 3, col = (c & 7u) * 8u;  // 8 bf16 = 16 bytes
-      uint4 va = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
-      if (m_base + r < m) va = *reinterpret_cast<const uint4 *>(a + (uint64_t)(m_base + r) * k + k0 + col);
-      if (n_base + r < n) vw = *reinterpret_cast<const uint4 *>(w + (uint64_t)(n_base + r) * k + k0 + col);
-      *reinterpret_cast<uint4 *>(a_lds + r * LDS_STRIDE + col * 2) = va;
-      *reinterpret_cast<uint4 *>(w_lds + r * LDS_STRIDE + col * 2) = vw;
+  BQMM_GLOAD(0u);
+  BQMM_STORE(0);
+  if (nsteps > 1) BQMM_GLOAD(1u);
+  for (uint32_t s = 0; s < nsteps; ++s) {
+    __syncthreads();  // stage s is complete; nobody still reads stage s + 1's buffer
+    if (s + 1 < nsteps) {
+      BQMM_STORE((s + 1) & 1u);
+      if (s + 2 < nsteps) BQMM_GLOAD(s + 2);
     }
-    __syncthreads();
+    const uint8_t *a_l = lds + (s & 1u) * kStageBytes, *w_l = a_l + kTileBytes;
 #pragma unroll
     for (int kk = 0; kk < KS / 16; ++kk) {
       v8bf A[2], B[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        A[s] = *reinterpret_cast<const v8bf *>(w_lds + (wn * 64 + s * 32 + (lane & 31)) * LDS_STRIDE + 32 * kk + 16 * (lane >> 5));
-        B[s] = *reinterpret_cast<const v8bf *>(a_lds + (wm * 64 + s * 32 + (lane & 31)) * LDS_STRIDE + 32 * kk + 16 * (lane >> 5));
+      for (int t = 0; t < 2; ++t) {
+        A[t] = *reinterpret_cast<const v8bf *>(w_l + (wn * 64 + t * 32 + (lane & 31)) * LDS_STRIDE + 32 * kk + 16 * (lane >> 5));
+        B[t] = *reinterpret_cast<const v8bf *>(a_l + (wm * 64 + t * 32 + (lane & 31)) * LDS_STRIDE + 32 * kk + 16 * (lane >> 5));
       }
 #pragma unroll
       for (int sn = 0; sn < 2; ++sn)
@@ -65,6 +114,8 @@ __global__ __launch_bounds__(kThreads) void dense_gemm_bf16_kernel(
           acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[sn], B[sm], acc[sn][sm], 0, 0, 0);
     }
   }
+#undef BQMM_GLOAD
+#undef BQMM_STORE
 
   const bool vec = (n % 4u) == 0u;
 #pragma unroll
@@ -94,8 +145,13 @@ __global__ __launch_bounds__(kThreads) void dense_gemm_bf16_kernel(
 
 hipError_t launch_dense_gemm_bf16(const void *a, const void *w, void *out, uint32_t m, uint32_t n,
                                   uint32_t k, hipStream_t s) {
-  const dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);
-  hipLaunchKernelGGL(dense_gemm_bf16_kernel, grid, dim3(kThreads), 0, s,
+  // two stages (73.7 KB) exceed the 64 KB default dynamic-LDS limit
+  static const hipError_t attr_err = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(dense_gemm_bf16_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+      2 * kStageBytes);
+  if (attr_err != hipSuccess) return attr_err;
+  const dim3 grid((m + BM - 1) / BM, (n + BN - 1) / BN);
+  hipLaunchKernelGGL(dense_gemm_bf16_kernel, grid, dim3(kThreads), 2 * kStageBytes, s,
                      static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(w),
                      static_cast<uint16_t *>(out), m, n, k);
   return hipGetLastError();

@@ -80,6 +80,7 @@ def _err(bq):
     (lambda l: l.dequant_q2_0_to_bf16(A, B, 4, 512, 48, None), -2, "multiple of 32"),
     (lambda l: l.dequant_q2_0_to_bf16(A, B, 4, 480, 128, None), -1, "not a multiple"),
     (lambda l: l.dense_gemm_bf16(A, B, C, 4, 4, 96, None), -1, "multiple of 64"),
+    (lambda l: l.dense_gemm_bf16(A, B, C, 4, 128 * 65536, 64, None), -1, "too large"),
     (lambda l: l.q4k_mmq_gemm(A, B, C, 4, 4, 384, None), -1, "multiple of 256"),
     (lambda l: l.q2_0_prefill_gemm(A, B, C, None, None, 4, 4, 512, 128, 1, None), -1, "act_q8"),
     (lambda l: l.q2_0_prefill_gemm(A, B, C, None, None, 4, 4, 512, 128, 0, None), -1, "scratch"),

@@ -13,8 +13,9 @@ graph and replayed between HIP events:
              step with q2_0_gemv_gate_up_silu in place of the first three calls;
   prefill  : quantize_act_q8_1 + q2_0_mmq_gemm, qkvz n=12288 k=2048, m in
              {512, 2048}; and the bf16 fallback (dequant + dense GEMM) at m=512;
-  ffn      : m=4096 FFN prefill, Q2_0 and Q4_K: quantize, gate and up MMQ,
-             silu_mul, quantize, down MMQ;
+  ffn      : m=4096 FFN prefill, Q2_0 and Q4_K: quantize, gate and up MMQ
+             (sharing the quantized input), silu_mul fused into the down
+             projection's quantization, down MMQ;
   copy     : (not in the default set) a plain 256 MiB device-to-device copy,
              the known-size reference for the HBM byte counters.
 The JSON line reports the decode GEMV (the workload the headline metric is
@@ -257,13 +258,12 @@ def ffn_legs(bq, dev, F):
             bq.quantize_act_q8_1(x, q8a, m, H)
             gemm(q8a, wg, gate, m, I, H)
             gemm(q8a, wu, up, m, I, H)
-            bq.silu_mul_bf16(gate, up, gate, m * I)
-            bq.quantize_act_q8_1(gate, q8h, m, I)
+            bq.silu_mul_quantize_q8_1(gate, up, q8h, m, I)
             gemm(q8h, wd, out, m, H, I)
 
         keep = [wg, wu, wd, x, q8a, q8h, gate, up, out]
-        legs.append(Leg(f"ffn_prefill_{fmt}_m4096", ffn, keep, 6, 3 * 2.0 * m * H * I, "TOPS",
-                        f"{kname} x3 + quantize x2 + silu_mul", INT8_PEAK_TOPS, "mfma"))
+        legs.append(Leg(f"ffn_prefill_{fmt}_m4096", ffn, keep, 5, 3 * 2.0 * m * H * I, "TOPS",
+                        f"{kname} x3 + quantize + silu_mul_quantize", INT8_PEAK_TOPS, "mfma"))
         legs.append(Leg(f"ffn_gate_proj_{fmt}_m4096", lambda wg=wg, gemm=gemm: gemm(q8a, wg, gate, m, I, H),
                         keep, 1, 2.0 * m * H * I, "TOPS", kname, INT8_PEAK_TOPS, "mfma"))
     return legs

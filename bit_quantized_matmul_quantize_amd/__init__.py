@@ -29,6 +29,7 @@ EXPORTS = {
     "q2_0_weight_bytes": (_U64, [_U32, _U32, _U32]),
     "q4k_weight_bytes": (_U64, [_U32, _U32]),
     "quantize_act_q8_1": (_I, [_P, _P, _U32, _U32, _P]),
+    "silu_mul_quantize_q8_1": (_I, [_P, _P, _P, _U32, _U32, _P]),
     "q2_0_mmq_gemm": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
     "q2_0_gemv_vec": (_I, [_P, _P, _P, _U32, _U32, _P]),
     "q2_0_gemv_vec_batchm": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
@@ -121,6 +122,11 @@ def q4k_weight_bytes(n: int, k: int) -> int:
 
 def quantize_act_q8_1(act, out_q8, m: int, k: int, stream=None):
     _check(lib().quantize_act_q8_1(_ptr(_bf16(act, "act")), _ptr(_u8(out_q8, "out_q8")), m, k, _stream(stream)))
+
+
+def silu_mul_quantize_q8_1(gate, up, out_q8, m: int, k: int, stream=None):
+    _check(lib().silu_mul_quantize_q8_1(_ptr(_bf16(gate, "gate")), _ptr(_bf16(up, "up")),
+                                        _ptr(_u8(out_q8, "out_q8")), m, k, _stream(stream)))
 
 
 def q2_0_mmq_gemm(act_q8, w_q2, out, m: int, n: int, k: int, stream=None):

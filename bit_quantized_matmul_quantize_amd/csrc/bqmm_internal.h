@@ -45,6 +45,8 @@ __device__ __forceinline__ float silu_mul_f32(float g, float u) {
 
 hipError_t launch_quantize_act_q8_1(const void *act, void *out, uint32_t m, uint32_t k,
                                     hipStream_t s);
+hipError_t launch_silu_mul_quantize_q8_1(const void *gate, const void *up, void *out, uint32_t m,
+                                         uint32_t k, hipStream_t s);
 hipError_t launch_dequant_q2_0(const void *w, void *out, uint32_t n, uint32_t k, uint32_t group,
                                hipStream_t s);
 hipError_t launch_silu_mul(const void *gate, const void *up, void *out, uint64_t count,

@@ -79,6 +79,19 @@ int quantize_act_q8_1(const void *act_bf16, void *out_q8, uint32_t m, uint32_t k
                     "quantize_act_q8_1");
 }
 
+int silu_mul_quantize_q8_1(const void *gate_bf16, const void *up_bf16, void *out_q8, uint32_t m,
+                           uint32_t k, void *stream) {
+  REQUIRE(gate_bf16 && up_bf16 && out_q8, BQ_EINVAL, "silu_mul_quantize_q8_1: null pointer");
+  REQUIRE(m >= 1 && k >= 1, BQ_EINVAL, "silu_mul_quantize_q8_1: m=%u k=%u must be >= 1", m, k);
+  REQUIRE(aligned16(gate_bf16) && aligned16(up_bf16) && aligned16(out_q8), BQ_EALIGN,
+          "silu_mul_quantize_q8_1: buffers must be 16-byte aligned");
+  const uint64_t kpad = ((uint64_t)k + 255u) / 256u * 256u;
+  const uint64_t blocks = (uint64_t)m * ((kpad + 2047u) / 2048u);
+  REQUIRE(blocks < (1ull << 31), BQ_EINVAL, "silu_mul_quantize_q8_1: m*k too large");
+  return hip_status(bqmm::launch_silu_mul_quantize_q8_1(gate_bf16, up_bf16, out_q8, m, k, as_stream(stream)),
+                    "silu_mul_quantize_q8_1");
+}
+
 static int check_mmq(const char *name, const void *act_q8, const void *w, const void *out,
                      uint32_t m, uint32_t n, uint32_t k, uint32_t kmult) {
   REQUIRE(act_q8 && w && out, BQ_EINVAL, "%s: null pointer", name);

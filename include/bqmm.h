@@ -97,6 +97,17 @@ uint64_t q4k_weight_bytes(uint32_t n, uint32_t k);
  *  padded to 256.]  m >= 1, k >= 1.  act_bf16 and out_q8 16-byte aligned. */
 int quantize_act_q8_1(const void *act_bf16, void *out_q8, uint32_t m, uint32_t k, void *stream);
 
+/* The FFN hidden activation quantized straight from its producer:
+ *   out_q8 = q8_1 of h,  h[i][j] = bf16_rne(silu(gate[i][j]) * up[i][j]),
+ * i.e. silu_mul_bf16 followed by quantize_act_q8_1, without writing h; the
+ * result equals those two calls bit for bit (same binary32 silu, same rule).
+ * [page layers/dense_ffn_decode_batch.rs, fn forward_km_q2: silu_mul
+ *  produces the down projection's input; page layers/ops/q4k_mmq.rs: each
+ *  prefill quantizes its activations to q8_1.]
+ * gate, up: [m][k] bf16; out_q8 holds q8_1_act_bytes(m, k) bytes.  m, k >= 1. */
+int silu_mul_quantize_q8_1(const void *gate_bf16, const void *up_bf16, void *out_q8,
+                           uint32_t m, uint32_t k, void *stream);
+
 /* Q2_0 MMQ: out[m][n] (bf16, row-major, row stride n) =
  *   sum_k deq(act_q8)[m][k] * deq(w_q2)[n][k],
  * on int8 matrix cores with exact int32 block dot products; scales applied

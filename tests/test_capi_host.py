@@ -64,6 +64,9 @@ def _err(bq):
     (lambda l: l.quantize_act_q8_1(None, B, 4, 512, None), -1, "null"),
     (lambda l: l.quantize_act_q8_1(A, B, 0, 512, None), -1, "m=0"),
     (lambda l: l.quantize_act_q8_1(A, MIS, 4, 512, None), -3, "aligned"),
+    (lambda l: l.silu_mul_quantize_q8_1(A, None, C, 4, 512, None), -1, "null"),
+    (lambda l: l.silu_mul_quantize_q8_1(A, MIS, C, 4, 512, None), -3, "aligned"),
+    (lambda l: l.silu_mul_quantize_q8_1(A, B, C, 4, 0, None), -1, "k=0"),
     (lambda l: l.q2_0_mmq_gemm(A, B, C, 4, 256, 500, None), -1, "multiple of 128"),
     (lambda l: l.q2_0_mmq_gemm(A, B, C, 0, 256, 512, None), -1, "m=0"),
     (lambda l: l.q2_0_mmq_gemm(A, MIS, C, 4, 256, 512, None), -3, "aligned"),

@@ -62,3 +62,47 @@ def test_quantize_ffn_down_input_full_size(gpu):
     act = inputs.activations(g, 4096, 17408)
     ref, _ = oracle.quantize_act_q8_1(act, 4096, 17408)
     assert np.array_equal(_run(gpu, act, 4096, 17408), ref)
+
+
+# ---- silu_mul fused into the quantizer ------------------------------------------
+
+def _fused(gpu, gate, up, m, k):
+    out = torch.full((bq.q8_1_act_bytes(m, k),), 0x5A, dtype=torch.uint8, device=gpu)
+    bq.silu_mul_quantize_q8_1(dev_bf16(gate, gpu), dev_bf16(up, gpu), out, m, k)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _chain(gpu, gate, up, m, k):
+    """silu_mul_bf16 then quantize_act_q8_1 on the device: the calls the fused entry replaces."""
+    g, u = dev_bf16(gate, gpu), dev_bf16(up, gpu)
+    h = torch.empty((m, k), dtype=torch.bfloat16, device=gpu)
+    bq.silu_mul_bf16(g, u, h, m * k)
+    out = torch.full((bq.q8_1_act_bytes(m, k),), 0x5A, dtype=torch.uint8, device=gpu)
+    bq.quantize_act_q8_1(h, out, m, k)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), h
+
+
+@pytest.mark.parametrize("m,k,seed", [(4, 512, 80), (3, 300, 81), (7, 4100, 82), (64, 17408, 83)])
+def test_silu_mul_quantize_equals_chain(gpu, m, k, seed):
+    g = inputs.rng(seed)
+    gate = inputs.activations(g, m, k, outliers=True)
+    up = inputs.activations(g, m, k)
+    got = _fused(gpu, gate, up, m, k)
+    ref, h = _chain(gpu, gate, up, m, k)
+    assert np.array_equal(got, ref)
+    # and against the oracle on the device's own bf16 hidden activation
+    h_bits = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    oref, flagged = oracle.quantize_act_q8_1(h_bits, m, k)
+    assert flagged == 0 and np.array_equal(got, oref)
+
+
+def test_silu_mul_quantize_ffn_full_size(gpu):
+    # m = 4096, k = 17408: the FFN down projection's input at prefill
+    g = inputs.rng(84)
+    gate = inputs.activations(g, 4096, 17408)
+    up = inputs.activations(g, 4096, 17408)
+    got = _fused(gpu, gate, up, 4096, 17408)
+    ref, _ = _chain(gpu, gate, up, 4096, 17408)
+    assert np.array_equal(got, ref)

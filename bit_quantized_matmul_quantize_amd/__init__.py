@@ -31,6 +31,8 @@ EXPORTS = {
     "quantize_act_q8_1": (_I, [_P, _P, _U32, _U32, _P]),
     "silu_mul_quantize_q8_1": (_I, [_P, _P, _P, _U32, _U32, _P]),
     "q2_0_mmq_gemm": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
+    "q2_0_mmq_gemm_ldc": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _P]),
+    "q4k_mmq_gemm_ldc": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _P]),
     "q2_0_gemv_vec": (_I, [_P, _P, _P, _U32, _U32, _P]),
     "q2_0_gemv_vec_batchm": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
     "q2_0_gemv_gate_up_silu": (_I, [_P, _P, _P, _P, _U32, _U32, _U32, _P]),
@@ -132,6 +134,26 @@ def silu_mul_quantize_q8_1(gate, up, out_q8, m: int, k: int, stream=None):
 def q2_0_mmq_gemm(act_q8, w_q2, out, m: int, n: int, k: int, stream=None):
     _check(lib().q2_0_mmq_gemm(_ptr(_u8(act_q8, "act_q8")), _ptr(_u8(w_q2, "w_q2")), _ptr(_bf16(out, "out")),
                                m, n, k, _stream(stream)))
+
+
+def _ptr_rows(t, m: int, n: int, ldc: int, what):
+    """A [m, n] bf16 view whose rows are ldc elements apart (a column range of a wider buffer)."""
+    _bf16(t, what)
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if tuple(t.shape) != (m, n) or (m > 1 and t.stride(0) != ldc) or (n > 1 and t.stride(1) != 1):
+        raise ValueError(f"{what}: expected an [{m}, {n}] view with row stride {ldc}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def q2_0_mmq_gemm_ldc(act_q8, w_q2, out, m: int, n: int, k: int, ldc: int, stream=None):
+    _check(lib().q2_0_mmq_gemm_ldc(_ptr(_u8(act_q8, "act_q8")), _ptr(_u8(w_q2, "w_q2")),
+                                   _ptr_rows(out, m, n, ldc, "out"), m, n, k, ldc, _stream(stream)))
+
+
+def q4k_mmq_gemm_ldc(act_q8, w_q4k, out, m: int, n: int, k: int, ldc: int, stream=None):
+    _check(lib().q4k_mmq_gemm_ldc(_ptr(_u8(act_q8, "act_q8")), _ptr(_u8(w_q4k, "w_q4k")),
+                                  _ptr_rows(out, m, n, ldc, "out"), m, n, k, ldc, _stream(stream)))
 
 
 def q2_0_gemv_vec(act, w_q2, out, n: int, k: int, stream=None):

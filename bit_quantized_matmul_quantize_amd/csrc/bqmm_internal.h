@@ -61,12 +61,13 @@ hipError_t launch_q2_0_gemv_mfma(const void *act, const void *w, void *out, uint
 hipError_t launch_q2_0_gemv_mfma_gate_up(const void *act, const void *w_gate, const void *w_up,
                                          void *out, uint32_t m, uint32_t n, uint32_t k,
                                          hipStream_t s);
+// ldc: row stride of out in elements (>= n); out row i starts at out + i * ldc
 hipError_t launch_q2_0_mmq(const void *act_q8, const void *w, void *out, int32_t *dots,
                            uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m,
-                           uint32_t n, uint32_t k, hipStream_t s);
+                           uint32_t n, uint32_t k, uint32_t ldc, hipStream_t s);
 hipError_t launch_q4k_mmq(const void *act_q8, const void *w, void *out, int32_t *dots,
                           uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m,
-                          uint32_t n, uint32_t k, hipStream_t s);
+                          uint32_t n, uint32_t k, uint32_t ldc, hipStream_t s);
 hipError_t launch_dense_gemm_bf16(const void *a, const void *w, void *out, uint32_t m, uint32_t n,
                                   uint32_t k, hipStream_t s);
 

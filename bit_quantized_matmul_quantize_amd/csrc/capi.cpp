@@ -106,18 +106,38 @@ int q2_0_mmq_gemm(const void *act_q8, const void *w_q2, void *out_bf16, uint32_t
                   uint32_t k, void *stream) {
   const int st = check_mmq("q2_0_mmq_gemm", act_q8, w_q2, out_bf16, m, n, k, 128u);
   if (st != BQ_OK) return st;
-  return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, out_bf16, nullptr, 0, 0, 0, 0, m, n, k,
+  return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, out_bf16, nullptr, 0, 0, 0, 0, m, n, k, n,
                                           as_stream(stream)),
                     "q2_0_mmq_gemm");
+}
+
+int q2_0_mmq_gemm_ldc(const void *act_q8, const void *w_q2, void *out_bf16, uint32_t m, uint32_t n,
+                      uint32_t k, uint32_t ldc, void *stream) {
+  const int st = check_mmq("q2_0_mmq_gemm_ldc", act_q8, w_q2, out_bf16, m, n, k, 128u);
+  if (st != BQ_OK) return st;
+  REQUIRE(ldc >= n, BQ_EINVAL, "q2_0_mmq_gemm_ldc: ldc=%u must be >= n=%u", ldc, n);
+  return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, out_bf16, nullptr, 0, 0, 0, 0, m, n, k, ldc,
+                                          as_stream(stream)),
+                    "q2_0_mmq_gemm_ldc");
 }
 
 int q4k_mmq_gemm(const void *act_q8, const void *w_q4k, void *out_bf16, uint32_t m, uint32_t n,
                  uint32_t k, void *stream) {
   const int st = check_mmq("q4k_mmq_gemm", act_q8, w_q4k, out_bf16, m, n, k, 256u);
   if (st != BQ_OK) return st;
-  return hip_status(bqmm::launch_q4k_mmq(act_q8, w_q4k, out_bf16, nullptr, 0, 0, 0, 0, m, n, k,
+  return hip_status(bqmm::launch_q4k_mmq(act_q8, w_q4k, out_bf16, nullptr, 0, 0, 0, 0, m, n, k, n,
                                          as_stream(stream)),
                     "q4k_mmq_gemm");
+}
+
+int q4k_mmq_gemm_ldc(const void *act_q8, const void *w_q4k, void *out_bf16, uint32_t m, uint32_t n,
+                     uint32_t k, uint32_t ldc, void *stream) {
+  const int st = check_mmq("q4k_mmq_gemm_ldc", act_q8, w_q4k, out_bf16, m, n, k, 256u);
+  if (st != BQ_OK) return st;
+  REQUIRE(ldc >= n, BQ_EINVAL, "q4k_mmq_gemm_ldc: ldc=%u must be >= n=%u", ldc, n);
+  return hip_status(bqmm::launch_q4k_mmq(act_q8, w_q4k, out_bf16, nullptr, 0, 0, 0, 0, m, n, k, ldc,
+                                         as_stream(stream)),
+                    "q4k_mmq_gemm_ldc");
 }
 
 static int check_blockdots(const char *name, const void *act_q8, const void *w, const int32_t *out,
@@ -135,7 +155,7 @@ int q2_0_mmq_blockdots(const void *act_q8, const void *w_q2, int32_t *out, uint3
                        uint32_t n0, uint32_t nt, uint32_t m, uint32_t n, uint32_t k, void *stream) {
   const int st = check_blockdots("q2_0_mmq_blockdots", act_q8, w_q2, out, m0, mt, n0, nt, m, n, k, 128u);
   if (st != BQ_OK) return st;
-  return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, nullptr, out, m0, mt, n0, nt, m, n, k,
+  return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, nullptr, out, m0, mt, n0, nt, m, n, k, n,
                                           as_stream(stream)),
                     "q2_0_mmq_blockdots");
 }
@@ -144,7 +164,7 @@ int q4k_mmq_blockdots(const void *act_q8, const void *w_q4k, int32_t *out, uint3
                       uint32_t n0, uint32_t nt, uint32_t m, uint32_t n, uint32_t k, void *stream) {
   const int st = check_blockdots("q4k_mmq_blockdots", act_q8, w_q4k, out, m0, mt, n0, nt, m, n, k, 256u);
   if (st != BQ_OK) return st;
-  return hip_status(bqmm::launch_q4k_mmq(act_q8, w_q4k, nullptr, out, m0, mt, n0, nt, m, n, k,
+  return hip_status(bqmm::launch_q4k_mmq(act_q8, w_q4k, nullptr, out, m0, mt, n0, nt, m, n, k, n,
                                          as_stream(stream)),
                     "q4k_mmq_blockdots");
 }
@@ -236,7 +256,7 @@ int q2_0_prefill_gemm(const void *act_bf16, const void *w_q2, void *out_bf16, vo
     st = hip_status(bqmm::launch_quantize_act_q8_1(act_bf16, act_q8, m, k, as_stream(stream)),
                     "q2_0_prefill_gemm (quantize)");
     if (st != BQ_OK) return st;
-    return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, out_bf16, nullptr, 0, 0, 0, 0, m, n, k,
+    return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, out_bf16, nullptr, 0, 0, 0, 0, m, n, k, n,
                                             as_stream(stream)),
                       "q2_0_prefill_gemm (mmq)");
   }

@@ -56,7 +56,7 @@ template <bool kDump>
 __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
     const uint8_t *__restrict__ act_q8, const uint8_t *__restrict__ w, uint16_t *__restrict__ out,
     int32_t *__restrict__ dots, uint32_t m, uint32_t n, uint32_t k, uint32_t m0, uint32_t mt,
-    uint32_t n0, uint32_t nt, uint32_t tile_n0, uint32_t tile_m0) {
+    uint32_t n0, uint32_t nt, uint32_t tile_n0, uint32_t tile_m0, uint32_t ldc) {
   // Two LDS stages (dynamic shared memory, kStageBytes each): group g is
   // computed from stage g % 2 while group g + 1 is written into the other.
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -248,13 +248,13 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
 #undef BQMM_STAGE
 
   if constexpr (!kDump) {
-    const bool full = (m_base + BM <= m) && (n_base + BN <= n) && (n % 4u) == 0u;
+    const bool full = (m_base + BM <= m) && (n_base + BN <= n) && (ldc % 4u) == 0u;
 #pragma unroll
     for (int sm = 0; sm < 2; ++sm) {
       const uint32_t mloc = wm * 64 + sm * 32 + l32;
       const uint32_t mm = m_base + mloc;
       const float scale = ldexpf(1.0f, rowexp[mloc] - 30);
-      uint16_t *orow = out + (uint64_t)min(mm, m - 1u) * n;
+      uint16_t *orow = out + (uint64_t)min(mm, m - 1u) * ldc;
 #pragma unroll
       for (int sn = 0; sn < 2; ++sn)
 #pragma unroll
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
             *reinterpret_cast<uint2 *>(orow + nn) =
                 make_uint2(pack_bf16x2(v[0] * scale, v[1] * scale), pack_bf16x2(v[2] * scale, v[3] * scale));
           } else if (mm < m) {
-            if ((n % 4u) == 0u && nn + 4 <= n) {
+            if ((ldc % 4u) == 0u && nn + 4 <= n) {
               *reinterpret_cast<uint2 *>(orow + nn) =
                   make_uint2(pack_bf16x2(v[0] * scale, v[1] * scale), pack_bf16x2(v[2] * scale, v[3] * scale));
             } else {
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
 
 hipError_t launch_q2_0_mmq(const void *act_q8, const void *w, void *out, int32_t *dots,
                            uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m,
-                           uint32_t n, uint32_t k, hipStream_t s) {
+                           uint32_t n, uint32_t k, uint32_t ldc, hipStream_t s) {
   // Two stages exceed the 64 KB default dynamic-LDS limit; gfx950 allows 160 KB.
   static const hipError_t attr_err = [] {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(q2_0_mmq_kernel<false>),
@@ -298,14 +298,14 @@ hipError_t launch_q2_0_mmq(const void *act_q8, const void *w, void *out, int32_t
     const dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);
     hipLaunchKernelGGL(q2_0_mmq_kernel<false>, grid, dim3(kThreads), 2 * kStageBytes, s,
                        static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
-                       static_cast<uint16_t *>(out), nullptr, m, n, k, 0u, 0u, 0u, 0u, 0u, 0u);
+                       static_cast<uint16_t *>(out), nullptr, m, n, k, 0u, 0u, 0u, 0u, 0u, 0u, ldc);
   } else {
     const uint32_t tn0 = n0 / BN, tn1 = (n0 + nt - 1) / BN;
     const uint32_t tm0 = m0 / BM, tm1 = (m0 + mt - 1) / BM;
     const dim3 grid(tn1 - tn0 + 1, tm1 - tm0 + 1);
     hipLaunchKernelGGL(q2_0_mmq_kernel<true>, grid, dim3(kThreads), 2 * kStageBytes, s,
                        static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
-                       nullptr, dots, m, n, k, m0, mt, n0, nt, tn0, tm0);
+                       nullptr, dots, m, n, k, m0, mt, n0, nt, tn0, tm0, n);
   }
   return hipGetLastError();
 }

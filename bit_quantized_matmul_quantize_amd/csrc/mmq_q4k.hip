@@ -57,7 +57,7 @@ template <bool kDump>
 __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
     const uint8_t *__restrict__ act_q8, const uint8_t *__restrict__ w, uint16_t *__restrict__ out,
     int32_t *__restrict__ dots, uint32_t m, uint32_t n, uint32_t k, uint32_t m0, uint32_t mt,
-    uint32_t n0, uint32_t nt, uint32_t tile_n0, uint32_t tile_m0) {
+    uint32_t n0, uint32_t nt, uint32_t tile_n0, uint32_t tile_m0, uint32_t ldc) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const uint32_t tid = threadIdx.x;
@@ -232,11 +232,11 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
 #undef BQMM_STAGE
 
   if constexpr (!kDump) {
-    const bool full = (m_base + BM <= m) && (n_base + BN <= n) && (n % 4u) == 0u;
+    const bool full = (m_base + BM <= m) && (n_base + BN <= n) && (ldc % 4u) == 0u;
 #pragma unroll
     for (int sm = 0; sm < 2; ++sm) {
       const uint32_t mm = m_base + wm * 64 + sm * 32 + l32;
-      uint16_t *orow = out + (uint64_t)min(mm, m - 1u) * n;
+      uint16_t *orow = out + (uint64_t)min(mm, m - 1u) * ldc;
 #pragma unroll
       for (int sn = 0; sn < 2; ++sn)
 #pragma unroll
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
             *reinterpret_cast<uint2 *>(orow + nn) =
                 make_uint2(pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3]));
           } else if (mm < m) {
-            if ((n % 4u) == 0u && nn + 4 <= n) {
+            if ((ldc % 4u) == 0u && nn + 4 <= n) {
               *reinterpret_cast<uint2 *>(orow + nn) =
                   make_uint2(pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3]));
             } else {
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
 
 hipError_t launch_q4k_mmq(const void *act_q8, const void *w, void *out, int32_t *dots,
                           uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m,
-                          uint32_t n, uint32_t k, hipStream_t s) {
+                          uint32_t n, uint32_t k, uint32_t ldc, hipStream_t s) {
   // Two stages exceed the 64 KB default dynamic-LDS limit; gfx950 allows 160 KB.
   static const hipError_t attr_err = [] {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(q4k_mmq_kernel<false>),
@@ -280,14 +280,14 @@ hipError_t launch_q4k_mmq(const void *act_q8, const void *w, void *out, int32_t 
     const dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);
     hipLaunchKernelGGL(q4k_mmq_kernel<false>, grid, dim3(kThreads), 2 * kStageBytes, s,
                        static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
-                       static_cast<uint16_t *>(out), nullptr, m, n, k, 0u, 0u, 0u, 0u, 0u, 0u);
+                       static_cast<uint16_t *>(out), nullptr, m, n, k, 0u, 0u, 0u, 0u, 0u, 0u, ldc);
   } else {
     const uint32_t tn0 = n0 / BN, tn1 = (n0 + nt - 1) / BN;
     const uint32_t tm0 = m0 / BM, tm1 = (m0 + mt - 1) / BM;
     const dim3 grid(tn1 - tn0 + 1, tm1 - tm0 + 1);
     hipLaunchKernelGGL(q4k_mmq_kernel<true>, grid, dim3(kThreads), 2 * kStageBytes, s,
                        static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
-                       nullptr, dots, m, n, k, m0, mt, n0, nt, tn0, tm0);
+                       nullptr, dots, m, n, k, m0, mt, n0, nt, tn0, tm0, n);
   }
   return hipGetLastError();
 }

@@ -119,6 +119,19 @@ int silu_mul_quantize_q8_1(const void *gate_bf16, const void *up_bf16, void *out
 int q2_0_mmq_gemm(const void *act_q8, const void *w_q2, void *out_bf16,
                   uint32_t m, uint32_t n, uint32_t k, void *stream);
 
+/* The MMQ GEMMs with an output row stride: out row i starts at out_bf16 +
+ * i*ldc (ldc >= n, elements); the ldc - n columns between rows are not
+ * written.  Lets a projection write straight into a column range of a wider
+ * buffer (pass the range's first element as out_bf16), e.g. the segments of
+ * the deinterleaved qkvz buffer.  [page layers/qwen3_ssm/init_q2.rs, fn
+ *  qkvz_q2_prefill_gemm / fn set_packed_q2_qkvz: the packed qkvz projection
+ *  and the buffer it fills; page layers/ops/q4k_mmq.rs, fn q4k_mmq_gemm.]
+ * Constraints as for q2_0_mmq_gemm / q4k_mmq_gemm; out_bf16 16-byte aligned. */
+int q2_0_mmq_gemm_ldc(const void *act_q8, const void *w_q2, void *out_bf16,
+                      uint32_t m, uint32_t n, uint32_t k, uint32_t ldc, void *stream);
+int q4k_mmq_gemm_ldc(const void *act_q8, const void *w_q4k, void *out_bf16,
+                     uint32_t m, uint32_t n, uint32_t k, uint32_t ldc, void *stream);
+
 /* Q2_0 decode GEMV, one row: out[n] (bf16) = sum_k act[k] * deq(w_q2)[n][k],
  * on the unquantized bf16 activation, fp32 accumulation.
  * [page layers/qwen3_ssm/init.rs, kernel q2_0_gemv_vec; page

@@ -71,6 +71,9 @@ def _err(bq):
     (lambda l: l.q2_0_mmq_gemm(A, B, C, 0, 256, 512, None), -1, "m=0"),
     (lambda l: l.q2_0_mmq_gemm(A, MIS, C, 4, 256, 512, None), -3, "aligned"),
     (lambda l: l.q2_0_mmq_gemm(A, B, C, 128 * 65536, 256, 512, None), -1, "too large"),
+    (lambda l: l.q2_0_mmq_gemm_ldc(A, B, C, 4, 256, 512, 255, None), -1, "ldc=255"),
+    (lambda l: l.q2_0_mmq_gemm_ldc(A, B, MIS, 4, 256, 512, 512, None), -3, "aligned"),
+    (lambda l: l.q4k_mmq_gemm_ldc(A, B, C, 4, 256, 512, 100, None), -1, "ldc=100"),
     (lambda l: l.q2_0_gemv_vec(A, B, C, 256, 200, None), -1, "group size 128"),
     (lambda l: l.q2_0_gemv_vec(A, B, None, 256, 512, None), -1, "null"),
     (lambda l: l.q2_0_gemv_vec_batchm(A, B, C, 9, 256, 512, None), -2, "m=9"),

@@ -126,3 +126,23 @@ def test_q4k_ffn_prefill_sampled(gpu):
         y = host_f64(out)
         R = oracle.q4k_mmq(_q8_rows(q8, m, k, rows), w, len(rows), n, k)
         assert row_error(y[rows], R) <= ROW_TOL
+
+
+def test_q4k_strided_output(gpu):
+    # q4k_mmq_gemm_ldc: same values as q4k_mmq_gemm, written into a column range
+    # of a wider buffer, the other columns untouched
+    m, n, k, ldc, off = 130, 200, 512, 520, 264
+    g = inputs.rng(54)
+    w = inputs.q4k_weight(g, n, k)
+    act = inputs.activations(g, m, k)
+    q8, _ = oracle.quantize_act_q8_1(act, m, k)
+    q8d, wd = dev_u8(q8, gpu), dev_u8(w, gpu)
+    ref = empty_bf16((m, n), gpu)
+    bq.q4k_mmq_gemm(q8d, wd, ref, m, n, k)
+    big = torch.full((m, ldc), -3.0, dtype=torch.bfloat16, device=gpu)
+    bq.q4k_mmq_gemm_ldc(q8d, wd, big[:, off:off + n], m, n, k, ldc)
+    torch.cuda.synchronize()
+    assert torch.equal(big[:, off:off + n].contiguous().view(torch.int16), ref.view(torch.int16))
+    mask = torch.ones_like(big, dtype=torch.bool)
+    mask[:, off:off + n] = False
+    assert bool((big[mask] == -3.0).all())

@@ -146,3 +146,27 @@ def test_ffn_prefill_q2_sampled(gpu):
         y = _mmq(gpu, q8d, dev_u8(w, gpu), m, n, k)
         R = oracle.q2_0_mmq(_rows_sel(q8, m, k, rows), w, len(rows), n, k)
         assert row_error(y[rows], R) <= ROW_TOL
+
+
+@pytest.mark.parametrize("m,n,k,ldc,off,seed", [(300, 136, 512, 1024, 256, 60),    # ragged tiles
+                                                (130, 256, 1024, 266, 8, 61),    # ldc % 4 != 0: scalar stores
+                                                (64, 128, 384, 128, 0, 62)])     # ldc == n
+def test_strided_output(gpu, m, n, k, ldc, off, seed):
+    # q2_0_mmq_gemm_ldc writes the same values as q2_0_mmq_gemm into columns
+    # [off, off + n) of a buffer with row stride ldc and leaves the rest alone
+    # (off % 8 == 0 keeps the first element 16-byte aligned)
+    g = inputs.rng(seed)
+    w = inputs.q2_0_weight(g, n, k)
+    act = inputs.activations(g, m, k, outliers=True)
+    _, q8d = _q8_dev(gpu, act, m, k)
+    wd = dev_u8(w, gpu)
+    ref = empty_bf16((m, n), gpu)
+    bq.q2_0_mmq_gemm(q8d, wd, ref, m, n, k)
+    big = torch.full((m, ldc), -3.0, dtype=torch.bfloat16, device=gpu)
+    bq.q2_0_mmq_gemm_ldc(q8d, wd, big[:, off:off + n], m, n, k, ldc)
+    torch.cuda.synchronize()
+    got = big[:, off:off + n].contiguous()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    mask = torch.ones_like(big, dtype=torch.bool)
+    mask[:, off:off + n] = False
+    assert bool((big[mask] == -3.0).all())

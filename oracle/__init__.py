@@ -62,6 +62,8 @@ def _load():
             "oracle_q4k_decode": (None, [P, P, U32, U32]),
             "oracle_q4k_blockdots": (None, [P, P, P, U32, U32, U32]),
             "oracle_q4k_mmq": (None, [P, P, P, U32, U32, U32]),
+            "oracle_q4k_gemv": (None, [P, P, P, U32, U32, U32]),
+            "oracle_quantize_weight_q4k": (ctypes.c_int64, [P, P, U32, U32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -212,6 +214,22 @@ def q4k_mmq(q8: np.ndarray, w: np.ndarray, m: int, n: int, k: int) -> np.ndarray
     out = np.zeros((m, n), dtype=np.float64)
     _load().oracle_q4k_mmq(_ptr(_u8(q8)), _ptr(_u8(w)), _ptr(out), m, n, k)
     return out
+
+
+def q4k_gemv(act_bf16: np.ndarray, w: np.ndarray, m: int, n: int, k: int) -> np.ndarray:
+    out = np.zeros((m, n), dtype=np.float64)
+    _load().oracle_q4k_gemv(_ptr(_u16(act_bf16)), _ptr(_u8(w)), _ptr(out), m, n, k)
+    return out
+
+
+def quantize_weight_q4k(w_bf16: np.ndarray, n: int, k: int):
+    """bf16 weight bits [n][k] -> (block_q4_K bytes, number of super-blocks
+    outside the supported range)."""
+    w = _u16(w_bf16)
+    assert w.size == n * k and k % 256 == 0
+    out = np.zeros(q4k_bytes(n, k), dtype=np.uint8)
+    flagged = _load().oracle_quantize_weight_q4k(_ptr(w), _ptr(out), n, k)
+    return out, int(flagged)
 
 
 # --- chains (compositions of the functions above) ---------------------------

@@ -16,9 +16,10 @@
  *
  * Floating point: every result that the method reaches exactly (dequantized
  * values, products, dot products) is formed in fp64, which is exact for all
- * of them except the final sums.  The one place where floating point decides
- * an integer -- the q8_1 code of an activation -- is taken in fp32 with IEEE
- * division and C roundf, the precision the kernel uses.
+ * of them except the final sums.  Where floating point decides an integer --
+ * the q8_1 code of an activation, the sub-scales and codes of the Q4_K weight
+ * quantizer -- it is taken in fp32 with IEEE division and C roundf, the
+ * precision the kernels use.
  */
 #include <math.h>
 #include <stdint.h>
@@ -462,4 +463,128 @@ void oracle_q4k_mmq(const uint8_t *q8, const uint8_t *w, double *R,
     }
     free(row);
     free(a);
+}
+
+/* Q4_K GEMV on unquantized bf16 activations, m rows (m = 1 for decode):
+ * R[i][j] = sum_k a_bf16[i][k] * deq_q4k(W)[j][k], fp64.
+ * [page layers/ops/q4k_mmq.rs, fn q4k_mmq_gemm: C[m, n] = A[m, k] x W[n, k]
+ *  with W in block_q4_K.]  The pages run Q4_K only through q8_1 and the MMQ;
+ * the decode form taken here is the same product on the bf16 activations
+ * with no quantize step, as the Q2_0 decode GEMV takes them
+ * ([page layers/qwen3_ssm/init.rs, q2_0_gemv_vec]).  Plain definition. */
+void oracle_q4k_gemv(const uint16_t *act, const uint8_t *w, double *R,
+                     uint32_t m, uint32_t n, uint32_t k)
+{
+    double *a = (double *)malloc(sizeof(double) * (uint64_t)m * k);
+    double *row = (double *)malloc(sizeof(double) * k);
+    for (uint64_t i = 0; i < (uint64_t)m * k; ++i) a[i] = oracle_bf16_to_f64(act[i]);
+    for (uint64_t j = 0; j < n; ++j) {
+        oracle_q4k_decode(w + j * (k / 256u) * 144u, row, 1u, k);
+        for (uint64_t i = 0; i < m; ++i) {
+            double s = 0.0;
+            for (uint64_t kk = 0; kk < k; ++kk) s += a[i * k + kk] * row[kk];
+            R[i * n + j] = s;
+        }
+    }
+    free(row);
+    free(a);
+}
+
+/* Q4_K weight quantization: bf16 [n][k] -> block_q4_K [n][k/256], k a
+ * multiple of 256, super-block s of row r at byte (r * k/256 + s) * 144.
+ * [page layers/ops/q4k_mmq.rs, fn quantize_weight_q4k: bf16 weights
+ *  [nrows, n_per_row] become block_q4_K, one 256-value block per thread; the
+ *  module notes that each weight is converted once and cached.]
+ * The page names the conversion but prints no rule.  Reading adopted: an
+ * affine min/max fit per 32-value sub-block j, whose step and offset are then
+ * stored as 6-bit multiples of two fp16 super-block scales.  All arithmetic
+ * is binary32 with IEEE division and C roundf (ties away from zero):
+ *   lo_j = min(+0, min x)          (the format's offset -dmin*m_j is <= 0)
+ *   hi_j = max(lo_j, max x)
+ *   S_j  = (hi_j - lo_j) / 15      (step that spans the sub-block)
+ *   M_j  = 0 - lo_j                (offset, >= +0)
+ *   d    = fp16_rne(max_j S_j / 63), dmin = fp16_rne(max_j M_j / 63)
+ *   sc_j = d    > 0 ? min(63, roundf(S_j / d))    : 0
+ *   m_j  = dmin > 0 ? min(63, roundf(M_j / dmin)) : 0
+ *   q    = clamp(roundf((x + dmin * m_j) / (d * sc_j)), 0, 15),  q = 0 when
+ *          d * sc_j == 0.
+ * The two products are exact in binary32 (11-bit times 6-bit significands).
+ * The maxima start at +0, so no step or scale is a negative zero.  Bytes are
+ * then packed in the layout q4k_scale_min and q4k_code read.
+ * Returns the number of super-blocks outside the supported range: a value
+ * that is not finite, or d or dmin that overflows binary16. */
+int64_t oracle_quantize_weight_q4k(const uint16_t *wb, uint8_t *out, uint32_t n, uint32_t k)
+{
+    uint64_t nsb = k / 256u;
+    int64_t flagged = 0;
+    for (uint64_t r = 0; r < n; ++r)
+        for (uint64_t s = 0; s < nsb; ++s) {
+            const uint16_t *src = wb + r * k + s * 256u;
+            uint8_t *blk = out + (r * nsb + s) * 144u;
+            float x[256], S[8], M[8];
+            int bad = 0;
+            for (int e = 0; e < 256; ++e) {
+                x[e] = (float)oracle_bf16_to_f64(src[e]);
+                if (!isfinite(x[e])) bad = 1;
+            }
+            float maxS = 0.0f, maxM = 0.0f;
+            for (int j = 0; j < 8; ++j) {
+                float lo = 0.0f;
+                for (int i = 0; i < 32; ++i)
+                    if (x[32 * j + i] < lo) lo = x[32 * j + i];
+                float hi = lo;
+                for (int i = 0; i < 32; ++i)
+                    if (x[32 * j + i] > hi) hi = x[32 * j + i];
+                S[j] = (hi - lo) / 15.0f;
+                M[j] = 0.0f - lo;
+                if (S[j] > maxS) maxS = S[j];
+                if (M[j] > maxM) maxM = M[j];
+            }
+            uint16_t dh = oracle_f32_to_f16(maxS / 63.0f);
+            uint16_t mh = oracle_f32_to_f16(maxM / 63.0f);
+            float d = oracle_f16_to_f32(dh), dmin = oracle_f16_to_f32(mh);
+            if (!isfinite(d) || !isfinite(dmin)) bad = 1;
+            flagged += bad;
+            uint32_t sc[8], mn[8];
+            for (int j = 0; j < 8; ++j) {
+                sc[j] = 0u;
+                mn[j] = 0u;
+                if (d > 0.0f) {
+                    float t = roundf(S[j] / d);
+                    sc[j] = t > 63.0f ? 63u : (uint32_t)t;
+                }
+                if (dmin > 0.0f) {
+                    float t = roundf(M[j] / dmin);
+                    mn[j] = t > 63.0f ? 63u : (uint32_t)t;
+                }
+            }
+            /* header: fp16 d, fp16 dmin, then the twelve scale/min bytes */
+            blk[0] = (uint8_t)(dh & 0xFFu);
+            blk[1] = (uint8_t)(dh >> 8);
+            blk[2] = (uint8_t)(mh & 0xFFu);
+            blk[3] = (uint8_t)(mh >> 8);
+            uint8_t *Sb = blk + 4;
+            for (int j = 0; j < 4; ++j) {
+                Sb[j] = (uint8_t)((sc[j] & 63u) | ((sc[j + 4] >> 4) << 6));
+                Sb[j + 4] = (uint8_t)((mn[j] & 63u) | ((mn[j + 4] >> 4) << 6));
+                Sb[j + 8] = (uint8_t)((sc[j + 4] & 15u) | ((mn[j + 4] & 15u) << 4));
+            }
+            /* codes: chunk t of 64 values, byte 16 + 32t + i holds value
+             * 64t + i in the low nibble and 64t + 32 + i in the high nibble */
+            memset(blk + 16, 0, 128);
+            for (int e = 0; e < 256; ++e) {
+                int j = e / 32;
+                float step = d * (float)sc[j];
+                float off = dmin * (float)mn[j];
+                uint32_t q = 0u;
+                if (step > 0.0f) {
+                    float t = roundf((x[e] + off) / step);
+                    q = t < 0.0f ? 0u : (t > 15.0f ? 15u : (uint32_t)t);
+                }
+                int t64 = e / 64, within = e % 64;
+                uint8_t *b = blk + 16 + 32 * t64 + (within % 32);
+                *b = (uint8_t)(*b | (within < 32 ? q : (q << 4)));
+            }
+        }
+    return flagged;
 }

@@ -31,5 +31,7 @@ uint64_t oracle_q4k_bytes(uint32_t n, uint32_t k);
 void oracle_q4k_decode(const uint8_t *w, double *out, uint32_t n, uint32_t k);
 void oracle_q4k_blockdots(const uint8_t *q8, const uint8_t *w, int32_t *D, uint32_t m, uint32_t n, uint32_t k);
 void oracle_q4k_mmq(const uint8_t *q8, const uint8_t *w, double *R, uint32_t m, uint32_t n, uint32_t k);
+void oracle_q4k_gemv(const uint16_t *act, const uint8_t *w, double *R, uint32_t m, uint32_t n, uint32_t k);
+int64_t oracle_quantize_weight_q4k(const uint16_t *wb, uint8_t *out, uint32_t n, uint32_t k);
 
 #endif

@@ -12,6 +12,7 @@ import pytest
 
 import inputs
 import oracle
+import q4k_pack
 
 # Twelve scale bytes and their sub-scales/mins, worked by hand:
 # j < 4 : sc = S[j] & 63 -> 1, 2, 3, 4 ; m = S[j+4] & 63 -> 5, 6, 7, 8
@@ -60,25 +61,7 @@ def test_nibble_placement():
     assert np.array_equal(dec, expect)
 
 
-def _py_unpack_q4k(w, n, k):
-    """Independent unpacker (vectorised numpy), returns codes [n][k], per-weight
-    scale d*sc and min dmin*m."""
-    nsb = k // 256
-    blk = w.reshape(n, nsb, 144)
-    d = blk[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)
-    dmin = blk[..., 2:4].copy().view(np.float16)[..., 0].astype(np.float64)
-    S = blk[..., 4:16].astype(np.int64)
-    sc = np.zeros((n, nsb, 8), np.int64)
-    mn = np.zeros((n, nsb, 8), np.int64)
-    sc[..., :4] = S[..., 0:4] & 63
-    mn[..., :4] = S[..., 4:8] & 63
-    sc[..., 4:] = (S[..., 8:12] & 15) | ((S[..., 0:4] >> 6) << 4)
-    mn[..., 4:] = (S[..., 8:12] >> 4) | ((S[..., 4:8] >> 6) << 4)
-    qs = blk[..., 16:].reshape(n, nsb, 4, 32).astype(np.int64)
-    codes = np.stack([qs & 15, qs >> 4], axis=3).reshape(n, nsb, 256)  # chunk t: low then high
-    scale = np.repeat(d[..., None] * sc, 32, axis=-1)
-    mins = np.repeat(dmin[..., None] * mn, 32, axis=-1)
-    return codes.reshape(n, k), scale.reshape(n, k), mins.reshape(n, k)
+_py_unpack_q4k = q4k_pack.unpack
 
 
 @pytest.mark.parametrize("seed", [51, 52])

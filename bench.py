@@ -16,6 +16,10 @@ graph and replayed between HIP events:
   ffn      : m=4096 FFN prefill, Q2_0 and Q4_K: quantize, gate and up MMQ
              (sharing the quantized input), silu_mul fused into the down
              projection's quantization, down MMQ;
+  q4k      : Q4_K decode GEMV (m=1) on the FFN gate [17408, 5120] and down
+             [5120, 17408] shapes, each weight rotated through 8 copies
+             (401 MB); and the Q4_K weight quantizer on a bf16 [17408, 5120]
+             weight (two input/output pairs alternate);
   copy     : (not in the default set) a plain 256 MiB device-to-device copy,
              the known-size reference for the HBM byte counters.
 The JSON line reports the decode GEMV (the workload the headline metric is
@@ -60,7 +64,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
-    p.add_argument("--legs", default="decode,verify,prefill,ffn")
+    p.add_argument("--legs", default="decode,verify,prefill,ffn,q4k")
     return p.parse_args()
 
 
@@ -269,6 +273,37 @@ def ffn_legs(bq, dev, F):
     return legs
 
 
+def q4k_legs(bq, dev, Q):
+    import torch
+    legs = []
+    copies, calls = 8, 64
+    for name, wkey, akey, n, k in (("q4k_decode_gate", "w_gate", "a_gate", Q["inter"], Q["hidden"]),
+                                   ("q4k_decode_down", "w_down", "a_down", Q["hidden"], Q["inter"])):
+        w0 = torch.from_numpy(Q[wkey]).to(dev)
+        ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+        x = torch.from_numpy(Q[akey][0].copy().view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty((n,), dtype=torch.bfloat16, device=dev)
+
+        def fn(ws=ws, x=x, y=y, n=n, k=k):
+            for i in range(calls):
+                bq.q4k_gemv_vec(x, ws[i % copies], y, n, k)
+
+        legs.append(Leg(f"{name}_n{n}_k{k}", fn, ws + [x, y], calls, calls * (w0.numel() + 2 * k + 2 * n),
+                        "GB/s", "q4k_gemv1_kernel", HBM_PEAK_GBS, "hbm"))
+    n, k = Q["inter"], Q["hidden"]
+    xb = [torch.from_numpy(Q["w_bf16"].view(np.int16)).to(dev).view(torch.bfloat16)]
+    xb.append(xb[0].clone())
+    qs = [torch.empty((bq.q4k_weight_bytes(n, k),), dtype=torch.uint8, device=dev) for _ in range(2)]
+
+    def quant():
+        for i in range(2):
+            bq.quantize_weight_q4k(xb[i], qs[i], n, k)
+
+    legs.append(Leg(f"q4k_quantize_weight_n{n}_k{k}", quant, xb + qs, 2, 2 * (2 * n * k + qs[0].numel()),
+                    "GB/s", "quantize_weight_q4k_kernel", HBM_PEAK_GBS, "hbm"))
+    return legs
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -299,6 +334,8 @@ def main():
         legs += prefill_legs(bq, dev, inputs.prefill_qkvz())
     if "ffn" in legs_wanted:
         legs += ffn_legs(bq, dev, inputs.prefill_ffn())
+    if "q4k" in legs_wanted:
+        legs += q4k_legs(bq, dev, inputs.q4k_decode())
     if "copy" in legs_wanted:
         legs.append(copy_leg(dev))
 

@@ -40,6 +40,8 @@ EXPORTS = {
     "dense_gemm_bf16": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
     "q2_0_prefill_gemm": (_I, [_P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _I, _P]),
     "q4k_mmq_gemm": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
+    "q4k_gemv_vec": (_I, [_P, _P, _P, _U32, _U32, _P]),
+    "quantize_weight_q4k": (_I, [_P, _P, _U32, _U32, _P]),
     "silu_mul_bf16": (_I, [_P, _P, _P, _U64, _P]),
     "q2_0_mmq_blockdots": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _P]),
     "q4k_mmq_blockdots": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _P]),
@@ -192,6 +194,16 @@ def q2_0_prefill_gemm(act, w_q2, out, scratch, act_q8, m: int, n: int, k: int, g
 def q4k_mmq_gemm(act_q8, w_q4k, out, m: int, n: int, k: int, stream=None):
     _check(lib().q4k_mmq_gemm(_ptr(_u8(act_q8, "act_q8")), _ptr(_u8(w_q4k, "w_q4k")), _ptr(_bf16(out, "out")),
                               m, n, k, _stream(stream)))
+
+
+def q4k_gemv_vec(act, w_q4k, out, n: int, k: int, stream=None):
+    _check(lib().q4k_gemv_vec(_ptr(_bf16(act, "act")), _ptr(_u8(w_q4k, "w_q4k")), _ptr(_bf16(out, "out")),
+                              n, k, _stream(stream)))
+
+
+def quantize_weight_q4k(w, out_q4k, n: int, k: int, stream=None):
+    _check(lib().quantize_weight_q4k(_ptr(_bf16(w, "w")), _ptr(_u8(out_q4k, "out_q4k")), n, k,
+                                     _stream(stream)))
 
 
 def silu_mul_bf16(gate, up, out, count: int | None = None, stream=None):

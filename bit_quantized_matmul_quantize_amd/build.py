@@ -19,8 +19,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbqmm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["quantize.hip", "elementwise.hip", "gemv.hip", "gemv_mfma.hip", "mmq_q2.hip", "mmq_q4k.hip",
-           "gemm_bf16.hip", "capi.cpp"]
+SOURCES = ["quantize.hip", "quantize_q4k.hip", "elementwise.hip", "gemv.hip", "gemv_mfma.hip",
+           "gemv_q4k.hip", "mmq_q2.hip", "mmq_q4k.hip", "gemm_bf16.hip", "capi.cpp"]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

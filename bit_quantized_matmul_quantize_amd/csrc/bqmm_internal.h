@@ -56,6 +56,10 @@ hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t 
 hipError_t launch_q2_0_gemv_gate_up_silu(const void *act, const void *w_gate, const void *w_up,
                                          void *out, uint32_t m, uint32_t n, uint32_t k,
                                          hipStream_t s);
+hipError_t launch_q4k_gemv(const void *act, const void *w, void *out, uint32_t n, uint32_t k,
+                           hipStream_t s);
+hipError_t launch_quantize_weight_q4k(const void *w_bf16, void *out, uint32_t n, uint32_t k,
+                                      hipStream_t s);
 hipError_t launch_q2_0_gemv_mfma(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
                                  uint32_t k, hipStream_t s);
 hipError_t launch_q2_0_gemv_mfma_gate_up(const void *act, const void *w_gate, const void *w_up,

@@ -208,6 +208,27 @@ int q2_0_gemv_gate_up_silu(const void *act_bf16, const void *w_gate_q2, const vo
                     "q2_0_gemv_gate_up_silu");
 }
 
+int q4k_gemv_vec(const void *act_bf16, const void *w_q4k, void *out_bf16, uint32_t n, uint32_t k,
+                 void *stream) {
+  REQUIRE(act_bf16 && w_q4k && out_bf16, BQ_EINVAL, "q4k_gemv_vec: null pointer");
+  REQUIRE(n >= 1 && k >= 1, BQ_EINVAL, "q4k_gemv_vec: n=%u k=%u must be >= 1", n, k);
+  REQUIRE(k % 256u == 0, BQ_EINVAL, "q4k_gemv_vec: k=%u must be a multiple of 256", k);
+  REQUIRE(k <= 65536u, BQ_EUNSUPPORTED, "q4k_gemv_vec: k=%u > 65536", k);
+  REQUIRE(aligned16(act_bf16) && aligned16(w_q4k) && aligned16(out_bf16), BQ_EALIGN,
+          "q4k_gemv_vec: buffers must be 16-byte aligned");
+  return hip_status(bqmm::launch_q4k_gemv(act_bf16, w_q4k, out_bf16, n, k, as_stream(stream)), "q4k_gemv_vec");
+}
+
+int quantize_weight_q4k(const void *w_bf16, void *out_q4k, uint32_t n, uint32_t k, void *stream) {
+  REQUIRE(w_bf16 && out_q4k, BQ_EINVAL, "quantize_weight_q4k: null pointer");
+  REQUIRE(n >= 1 && k >= 1, BQ_EINVAL, "quantize_weight_q4k: n=%u k=%u must be >= 1", n, k);
+  REQUIRE(k % 256u == 0, BQ_EINVAL, "quantize_weight_q4k: k=%u must be a multiple of 256", k);
+  REQUIRE(aligned16(w_bf16) && aligned16(out_q4k), BQ_EALIGN,
+          "quantize_weight_q4k: buffers must be 16-byte aligned");
+  return hip_status(bqmm::launch_quantize_weight_q4k(w_bf16, out_q4k, n, k, as_stream(stream)),
+                    "quantize_weight_q4k");
+}
+
 static int check_dequant(const void *w, const void *out, uint32_t n, uint32_t k, uint32_t group) {
   REQUIRE(w && out, BQ_EINVAL, "dequant_q2_0_to_bf16: null pointer");
   REQUIRE(n >= 1 && k >= 1, BQ_EINVAL, "dequant_q2_0_to_bf16: n=%u k=%u must be >= 1", n, k);

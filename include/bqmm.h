@@ -190,6 +190,35 @@ int q2_0_prefill_gemm(const void *act_bf16, const void *w_q2, void *out_bf16,
 int q4k_mmq_gemm(const void *act_q8, const void *w_q4k, void *out_bf16,
                  uint32_t m, uint32_t n, uint32_t k, void *stream);
 
+/* Q4_K decode GEMV, one row: out[n] (bf16) = sum_k act[k] * deq_q4k(w)[n][k],
+ * on the unquantized bf16 activation, fp32 accumulation; deq_q4k as for
+ * q4k_mmq_gemm (w = d * sc_j * q - dmin * m_j per 32-weight sub-block).
+ * [page layers/ops/q4k_mmq.rs: block_q4_K and fn q4k_mmq_gemm, C = A x W^T;
+ *  the bf16-input decode form follows the Q2_0 decode GEMV, page
+ *  layers/qwen3_ssm/init.rs, q2_0_gemv_vec.]
+ * act_bf16: [k]; w_q4k: [n][k/256] blocks of 144 bytes; out_bf16: [n].
+ * k % 256 == 0 and k <= 65536 (the activation vector is staged in LDS;
+ * larger k returns BQ_EUNSUPPORTED); n >= 1. */
+int q4k_gemv_vec(const void *act_bf16, const void *w_q4k, void *out_bf16,
+                 uint32_t n, uint32_t k, void *stream);
+
+/* Q4_K weight quantization: out_q4k ([n][k/256] blocks of 144 bytes,
+ * q4k_weight_bytes(n, k)) from w_bf16 ([n][k] bf16, row-major).
+ * [page layers/ops/q4k_mmq.rs, fn quantize_weight_q4k: bf16 [nrows,
+ *  n_per_row] to block_q4_K, one 256-value block per thread.]  The page gives
+ * no rule; the one implemented, bit-exact, in binary32 with IEEE division
+ * and roundf (ties away from zero), per 32-value sub-block j:
+ *   lo_j = min(+0, min x), hi_j = max(lo_j, max x),
+ *   S_j = (hi_j - lo_j) / 15, M_j = 0 - lo_j,
+ *   d = fp16_rne(max_j S_j / 63), dmin = fp16_rne(max_j M_j / 63),
+ *   sc_j = d > 0 ? min(63, roundf(S_j / d)) : 0 (m_j likewise from M_j, dmin),
+ *   q = clamp(roundf((x + dmin*m_j) / (d*sc_j)), 0, 15), 0 if d*sc_j == 0.
+ * Supported range: finite inputs with max S_j / 63 and max M_j / 63 within
+ * binary16 (|x| below about 1.5e7); outside it the bytes are unspecified.
+ * k % 256 == 0; n >= 1; both buffers 16-byte aligned. */
+int quantize_weight_q4k(const void *w_bf16, void *out_q4k, uint32_t n, uint32_t k,
+                        void *stream);
+
 /* out[i] = bf16_rne(silu(gate[i]) * up[i]) for i < count, silu(g) =
  * g/(1+exp(-g)) in fp32.  out == gate is allowed (in place).
  * [page layers/dense_ffn_decode_batch.rs, fn forward_km_q2: silu_mul over

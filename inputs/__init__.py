@@ -71,6 +71,12 @@ def q4k_weight(g: np.random.Generator, n: int, k: int) -> np.ndarray:
     return blk.reshape(-1)
 
 
+def bf16_weight(g: np.random.Generator, n: int, k: int, scale: float = 0.02) -> np.ndarray:
+    """bf16 bit patterns [n][k] of N(0, scale^2) weights (input of the Q4_K
+    weight quantizer)."""
+    return f32_to_bf16_bits(g.standard_normal(size=(n, k), dtype=np.float32) * np.float32(scale))
+
+
 def activations(g: np.random.Generator, m: int, k: int, outliers: bool = False) -> np.ndarray:
     """bf16 bit patterns [m][k]: N(0,1), optionally 1% of columns times 20."""
     x = g.standard_normal(size=(m, k), dtype=np.float32)
@@ -122,6 +128,17 @@ def prefill_qkvz(seed: int = 4, rows: int = 2048):
     w = q2_0_weight(g, n, k)
     a = activations(g, rows, k, outliers=True)
     return dict(n=n, k=k, w=w, act=a)
+
+
+def q4k_decode(seed: int = 6):
+    """Q4_K decode (m=1) on the FFN shapes: gate/up [17408, 5120] and down
+    [5120, 17408] weights, N(0,1) activations with 1% outlier channels; and a
+    bf16 N(0, 0.02^2) [17408, 5120] weight for the Q4_K weight quantizer."""
+    g = rng(seed)
+    return dict(hidden=HIDDEN, inter=INTER,
+                w_gate=q4k_weight(g, INTER, HIDDEN), a_gate=activations(g, 1, HIDDEN, outliers=True),
+                w_down=q4k_weight(g, HIDDEN, INTER), a_down=activations(g, 1, INTER, outliers=True),
+                w_bf16=bf16_weight(g, INTER, HIDDEN))
 
 
 def prefill_ffn(seed: int = 5, rows: int = 4096, formats=("q2_0", "q4k")):

@@ -96,6 +96,15 @@ def _err(bq):
     (lambda l: l.q2_0_mmq_blockdots(A, B, C, 4, 1, 0, 1, 4, 256, 512, None), -1, "outside"),
     (lambda l: l.q2_0_mmq_blockdots(A, B, C, 0, 0, 0, 1, 4, 256, 512, None), -1, "empty"),
     (lambda l: l.q4k_mmq_blockdots(A, B, C, 0, 1, 250, 7, 4, 256, 512, None), -1, "outside"),
+    (lambda l: l.q4k_gemv_vec(A, B, C, 256, 384, None), -1, "multiple of 256"),
+    (lambda l: l.q4k_gemv_vec(A, B, C, 0, 512, None), -1, "n=0"),
+    (lambda l: l.q4k_gemv_vec(None, B, C, 4, 512, None), -1, "null"),
+    (lambda l: l.q4k_gemv_vec(A, MIS, C, 4, 512, None), -3, "aligned"),
+    (lambda l: l.q4k_gemv_vec(A, B, C, 4, 65536 + 256, None), -2, "> 65536"),
+    (lambda l: l.quantize_weight_q4k(A, B, 4, 300, None), -1, "multiple of 256"),
+    (lambda l: l.quantize_weight_q4k(A, None, 4, 512, None), -1, "null"),
+    (lambda l: l.quantize_weight_q4k(A, MIS, 4, 512, None), -3, "aligned"),
+    (lambda l: l.quantize_weight_q4k(A, B, 0, 512, None), -1, "n=0"),
 ])
 def test_validation_rejects_before_any_hip_call(bq, call, status, needle):
     assert call(bq.lib()) == status

@@ -236,11 +236,12 @@ hipError_t launch_g(const void *act, const void *w, void *out, uint32_t n, uint3
 hipError_t launch_q4k_gemv(const void *act, const void *w, void *out, uint32_t n, uint32_t k,
                            hipStream_t s) {
   if (k > kMaxK) return hipErrorInvalidValue;
-  // Groups of 16 lanes (a ragged last slice wastes fewer lanes than with 32);
-  // two rows per lane unless that leaves fewer than two workgroups per
-  // compute unit.
-  if (n >= 2u * 256u * 32u) return launch_g<16, 2>(act, w, out, n, k, s);
-  return launch_g<16, 1>(act, w, out, n, k, s);
+  // Half-wave groups, one row per lane: measured on the FFN shapes against
+  // 16-lane groups and two rows per lane (gate [17408, 5120] 11.3 us vs
+  // 11.6 / 13.3 us; down [5120, 17408] 12.9 us vs 13.8 / 14.0 us): more
+  // workgroups of fewer rows balance better over the compute units, and the
+  // per-instruction footprint of one row per lane is more compact.
+  return launch_g<32, 1>(act, w, out, n, k, s);
 }
 
 }  // namespace bqmm

@@ -40,6 +40,12 @@ __device__ __forceinline__ float silu_mul_f32(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
 }
 
+// Batch size from which the batched Q2_0 GEMV (single and fused gate/up) runs
+// on matrix cores rather than on the vector ALU; both sources dispatch on it.
+#ifndef BQMM_GEMV_MIN_M_MFMA
+#define BQMM_GEMV_MIN_M_MFMA 4
+#endif
+
 // ---- launchers (one per kernel source) ------------------------------------
 // Arguments are validated by the C ABI layer before these are called.
 

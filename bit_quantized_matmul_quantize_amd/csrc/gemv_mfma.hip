@@ -28,10 +28,17 @@
 // by the T row tiles a wave processes.  The group scale is applied once per
 // group and output with an fma.
 //
-// Work split (at most 128 VGPRs, so that two 8-wave workgroups share a CU):
-// a wave owns T tiles of 16 rows and a contiguous range of the
+// Work split: a wave owns T tiles of 16 rows and a contiguous range of the
 // 128-groups; the W waves of a workgroup split k between them and add their
-// partial sums through LDS at the end.  There is no barrier in the main loop.
+// partial sums through LDS at the end.  The T tiles share each activation
+// load, which is what limits this kernel, so T is as large as the launch
+// allows: the grid must fit the compute units in one round (a second, partial
+// round of these latency-bound waves nearly doubles the time).  Measured on
+// the FFN shapes at m = 8: wide single (n = 17408) T = 3 within 128 VGPRs, so
+// two 8-wave workgroups share a CU and all 363 fit at once (20.4 us, was 25.4
+// with T = 2 at 134 VGPRs, one workgroup per CU and 544 of them); narrow
+// (n = 5120) T = 2, 160 workgroups (24.7 us, was 31.2 with T = 1); fused
+// gate/up T = 3 of each weight (36.7 us, was 46.1 with T = 1).  There is no barrier in the main loop.
 // A wave's weight scales are staged once in LDS ([group][row], so one 8-byte
 // read gives the four rows of a lane's outputs).  Loads run P groups ahead,
 // unconditionally from clamped addresses.
@@ -63,15 +70,12 @@ __device__ __forceinline__ v4f mfma(v4u a, v4u b, v4f c) {
 #ifndef BQMM_GEMVX_WIDE_N
 #define BQMM_GEMVX_WIDE_N 8192
 #endif
-#ifndef BQMM_GEMVX_MINW
-#define BQMM_GEMVX_MINW 2
-#endif
 #ifndef BQMM_GEMVX_P
 #define BQMM_GEMVX_P 2
 #endif
 
-template <int M, int T, int W, int P, int NW>
-__global__ __launch_bounds__(64 * W, W >= 8 ? BQMM_GEMVX_MINW : 1) void q2_0_gemv_mfma_kernel(const uint16_t *__restrict__ act,
+template <int M, int T, int W, int P, int NW, int MINW>
+__global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint16_t *__restrict__ act,
                                                                 const uint8_t *__restrict__ w,
                                                                 const uint8_t *__restrict__ w2,
                                                                 uint16_t *__restrict__ out,
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(64 * W, W >= 8 ? BQMM_GEMVX_MINW : 1) void q2_0_gem
   }
 }
 
-template <int M, int W, int T, int NW>
+template <int M, int W, int T, int NW, int MINW>
 hipError_t launch_w(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
                     hipStream_t s) {
   constexpr int P = BQMM_GEMVX_P;
@@ -222,48 +226,83 @@ hipError_t launch_w(const void *act, const void *w, const void *w2, void *out, u
   const size_t lds = sc_bytes > red_bytes ? sc_bytes : red_bytes;
   if (lds > 65536) return hipErrorInvalidValue;  // k too large for the staged scales
   const uint32_t blocks = (n + 16 * T - 1) / (16 * T);
-  hipLaunchKernelGGL((q2_0_gemv_mfma_kernel<M, T, W, P, NW>), dim3(blocks), dim3(64 * W), lds, s,
+  hipLaunchKernelGGL((q2_0_gemv_mfma_kernel<M, T, W, P, NW, MINW>), dim3(blocks), dim3(64 * W), lds, s,
                      static_cast<const uint16_t *>(act), static_cast<const uint8_t *>(w),
                      static_cast<const uint8_t *>(w2), static_cast<uint16_t *>(out), n, k);
   return hipGetLastError();
 }
 
-// Eight waves split k when it has at least eight groups (W <= G is required);
-// narrow outputs take one 16-row tile per wave so that the grid still has a
-// few waves per SIMD.  The fused gate/up kernel takes one tile of each weight
-// (the same rows), so per-row sums are identical to the single kernel's.
+// Eight waves split k when it has at least eight groups (W <= G is required).
+// The tiles per wave and the register bound (minimum waves per SIMD) are set
+// per case below.  The fused gate/up kernel takes T tiles of each weight (the
+// same rows) and the same k split, so per-row sums are identical to the
+// single kernel's.
+#ifndef BQMM_GEMVX_T_WIDE
+#define BQMM_GEMVX_T_WIDE 3
+#endif
+#ifndef BQMM_GEMVX_T_NARROW
+#define BQMM_GEMVX_T_NARROW 2
+#endif
+#ifndef BQMM_GEMVX_T_FUSED
+#define BQMM_GEMVX_T_FUSED 3
+#endif
+#ifndef BQMM_GEMVX_MINW_WIDE
+#define BQMM_GEMVX_MINW_WIDE 4
+#endif
+#ifndef BQMM_GEMVX_MINW_NARROW
+#define BQMM_GEMVX_MINW_NARROW 2
+#endif
+#ifndef BQMM_GEMVX_MINW_FUSED
+#define BQMM_GEMVX_MINW_FUSED 2
+#endif
 template <int M, int NW>
 hipError_t launch_m(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
                     hipStream_t s) {
   const uint32_t G = k >> 7;
   if (G >= 8) {
-    if (NW == 1 && n >= BQMM_GEMVX_WIDE_N) return launch_w<M, 8, 2, NW>(act, w, w2, out, n, k, s);
-    return launch_w<M, 8, 1, NW>(act, w, w2, out, n, k, s);
+    if constexpr (NW == 2) {
+      return launch_w<M, 8, BQMM_GEMVX_T_FUSED, NW, BQMM_GEMVX_MINW_FUSED>(act, w, w2, out, n, k, s);
+    } else {
+      if (n >= BQMM_GEMVX_WIDE_N)
+        return launch_w<M, 8, BQMM_GEMVX_T_WIDE, NW, BQMM_GEMVX_MINW_WIDE>(act, w, w2, out, n, k, s);
+      return launch_w<M, 8, BQMM_GEMVX_T_NARROW, NW, BQMM_GEMVX_MINW_NARROW>(act, w, w2, out, n, k, s);
+    }
   }
-  return launch_w<M, 1, 2, NW>(act, w, w2, out, n, k, s);
+  return launch_w<M, 1, 2, NW, 1>(act, w, w2, out, n, k, s);
+}
+
+
+// m below the dispatch threshold never reaches these entry points; those
+// sizes are not instantiated.
+template <int NW>
+hipError_t launch_any_m(const void *act, const void *w, const void *w2, void *out, uint32_t m, uint32_t n,
+                        uint32_t k, hipStream_t s) {
+  if (m < (uint32_t)BQMM_GEMV_MIN_M_MFMA) return hipErrorInvalidValue;
+  switch (m) {
+#if BQMM_GEMV_MIN_M_MFMA <= 4
+    case 4: return launch_m<4, NW>(act, w, w2, out, n, k, s);
+#endif
+#if BQMM_GEMV_MIN_M_MFMA <= 5
+    case 5: return launch_m<5, NW>(act, w, w2, out, n, k, s);
+#endif
+    case 6: return launch_m<6, NW>(act, w, w2, out, n, k, s);
+    case 7: return launch_m<7, NW>(act, w, w2, out, n, k, s);
+    case 8: return launch_m<8, NW>(act, w, w2, out, n, k, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_q2_0_gemv_mfma(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
                                  uint32_t k, hipStream_t s) {
-  switch (m) {
-    case 6: return launch_m<6, 1>(act, w, nullptr, out, n, k, s);
-    case 7: return launch_m<7, 1>(act, w, nullptr, out, n, k, s);
-    case 8: return launch_m<8, 1>(act, w, nullptr, out, n, k, s);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_any_m<1>(act, w, nullptr, out, m, n, k, s);
 }
 
 hipError_t launch_q2_0_gemv_mfma_gate_up(const void *act, const void *w_gate, const void *w_up,
                                          void *out, uint32_t m, uint32_t n, uint32_t k,
                                          hipStream_t s) {
-  switch (m) {
-    case 6: return launch_m<6, 2>(act, w_gate, w_up, out, n, k, s);
-    case 7: return launch_m<7, 2>(act, w_gate, w_up, out, n, k, s);
-    case 8: return launch_m<8, 2>(act, w_gate, w_up, out, n, k, s);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_any_m<2>(act, w_gate, w_up, out, m, n, k, s);
 }
 
 }  // namespace bqmm

@@ -41,13 +41,17 @@ def test_decode_qkvz_full(gpu):
                                         (1, 100, 17408, 30),    # m=1: prep loop over 1088 items
                                         (1, 3, 33792, 31),      # m=1 beyond the LDS-staged kernel's k
                                         (1, 4096 + 37, 2048, 32),
-                                        # batched kernel, wide launch shape (n >= 8192):
+                                        # vector batched kernel (m <= 3), wide launch shape (n >= 8192):
                                         (2, 8192 + 45, 1152, 33),   # two slices, the second ragged
-                                        (4, 9000, 384, 34),         # one slice, fewer than the prefetch depth
-                                        (7, 8192, 4096, 35),        # one full prefetch round plus one slice
+                                        (3, 9000, 384, 34),         # one slice, fewer than the prefetch depth
+                                        (3, 8192, 4096, 35),        # one full prefetch round plus one slice
                                         (1, 8192 + 5, 36864, 36),   # m=1 beyond the decode kernel's k
-                                        # matrix-core kernel (m >= 6): one wave per group range
-                                        (6, 100, 512, 39), (6, 8192 + 16, 2048, 40)])
+                                        (4, 9, 65536 + 1024, 37),   # m >= 4 beyond the matrix-core kernel's k
+                                        # matrix-core kernel (m >= 4): one wave per group range
+                                        (6, 100, 512, 39), (6, 8192 + 16, 2048, 40),
+                                        (4, 8192 + 16, 2048, 41),   # wide: 3 tiles per wave, last workgroup ragged
+                                        (5, 1000, 1024, 42),        # narrow: 2 tiles per wave, ragged
+                                        (4, 151, 1152, 43)])
 def test_ragged(gpu, m, n, k, seed):
     g = inputs.rng(seed)
     w = inputs.q2_0_weight(g, n, k)

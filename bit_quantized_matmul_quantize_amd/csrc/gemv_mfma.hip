@@ -73,6 +73,7 @@ __device__ __forceinline__ v4f mfma(v4u a, v4u b, v4f c) {
 #ifndef BQMM_GEMVX_P
 #define BQMM_GEMVX_P 2
 #endif
+constexpr int kStageBatch = 8;  // scale-staging loads per lane per round
 
 template <int M, int T, int W, int P, int NW, int MINW>
 __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint16_t *__restrict__ act,
@@ -113,20 +114,37 @@ __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint
       aq[slot][j] = *reinterpret_cast<const uint4 *>(ap + 128u * g_ + 32u * j);     \
   } while (0)
 
+  // Stage this wave's scales in LDS: [weight][group][row] fp16.  A round
+  // issues kStageBatch loads per lane before storing any, and the first round
+  // goes out before the weight prefetch: vector-memory counters retire in
+  // order, so stores placed after the prefetch would wait for its HBM loads,
+  // and a load-store loop would pay one memory latency per iteration.
+  // Entries are numbered group-major (consecutive lanes take consecutive rows,
+  // so the LDS writes are contiguous and the row index is a division by a
+  // constant).
+  uint16_t *sc = reinterpret_cast<uint16_t *>(smem) + wave * (NW * kRows * gmax);
+  const uint32_t per_w = kRows * ng, nst = NW * per_w;
+  auto stage_round = [&](uint32_t base) {
+    uint32_t v[kStageBatch], dst[kStageBatch];
+#pragma unroll
+    for (int b = 0; b < kStageBatch; ++b) {
+      const uint32_t i = min(base + lane + 64u * b, nst - 1u);
+      const uint32_t wv = i >= per_w ? 1u : 0u, rem = i - wv * per_w;
+      const uint32_t gi = rem / kRows, r = rem - gi * kRows;
+      const uint16_t *scales = reinterpret_cast<const uint16_t *>((wv == 0 ? w : w2) + (uint64_t)n * k / 4u);
+      v[b] = scales[(uint64_t)min(row0 + r, n - 1u) * G + gb + gi];
+      dst[b] = (wv * gmax + gi) * kRows + r;
+    }
+#pragma unroll
+    for (int b = 0; b < kStageBatch; ++b)
+      if (base + lane + 64u * b < nst) sc[dst[b]] = (uint16_t)v[b];
+  };
+  stage_round(0);
+
 #pragma unroll
   for (int p = 0; p < P; ++p) BQMM_LOADX(p, p);
 
-  // stage this wave's scales: [weight][group][row] fp16
-  uint16_t *sc = reinterpret_cast<uint16_t *>(smem) + wave * (NW * kRows * gmax);
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    const uint16_t *scales = reinterpret_cast<const uint16_t *>((v == 0 ? w : w2) + (uint64_t)n * k / 4u);
-    for (uint32_t i = lane; i < kRows * ng; i += 64u) {
-      const uint32_t r = i / ng, gi = i - r * ng;
-      const uint32_t row = min(row0 + r, n - 1u);
-      sc[(v * gmax + gi) * kRows + r] = scales[(uint64_t)row * G + gb + gi];
-    }
-  }
+  for (uint32_t base = 64u * kStageBatch; base < nst; base += 64u * kStageBatch) stage_round(base);
 
   const uint32_t M0 = vconst_(0x00030003u), M1 = vconst_(0x000C000Cu), M2 = vconst_(0x00300030u),
                  M3 = vconst_(0x00600060u);

@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <tuple>
+#include <vector>
+
 namespace bqmm {
 
 // ---- device helpers ------------------------------------------------------
@@ -38,6 +42,25 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
 // fused gate/up GEMV epilogue share it, so both round the same value.
 __device__ __forceinline__ float silu_mul_f32(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
+}
+
+// ---- host helpers ---------------------------------------------------------
+
+// Raise a kernel's dynamic-LDS limit (beyond the 64 KB default) on the current
+// device.  The attribute is per device, so it is set once per (kernel, device)
+// and remembered; the lookup takes a lock, which costs far less than a launch.
+inline hipError_t ensure_dynamic_lds(const void *kernel, int bytes) {
+  static std::mutex mu;
+  static std::vector<std::tuple<const void *, int, int>> done;  // kernel, device, bytes
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto &t : done)
+    if (std::get<0>(t) == kernel && std::get<1>(t) == dev && std::get<2>(t) >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.emplace_back(kernel, dev, bytes);
+  return e;
 }
 
 // Batch size from which the batched Q2_0 GEMV (single and fused gate/up) runs

@@ -27,6 +27,26 @@ int hip_status(hipError_t e, const char *what) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0u; }
 
+// True when the byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void *a, uint64_t na, const void *b, uint64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+uint64_t q8_bytes(uint32_t m, uint32_t k) {
+  const uint64_t kpad = ((uint64_t)k + 255u) / 256u * 256u;
+  return (uint64_t)m * kpad + (uint64_t)m * (kpad / 32u) * 4u;
+}
+
+uint64_t q2_bytes(uint32_t n, uint32_t k) { return (uint64_t)n * k / 4u + 2u * (uint64_t)n * (k / 128u); }
+
+uint64_t q4k_bytes(uint32_t n, uint32_t k) { return (uint64_t)n * (k / 256u) * 144u; }
+
+uint64_t bf16_bytes(uint64_t rows, uint64_t cols) { return 2u * rows * cols; }
+
+// bytes spanned by rows of n bf16 values at a row stride of ldc values
+uint64_t strided_bytes(uint32_t m, uint32_t n, uint32_t ldc) { return 2u * ((uint64_t)(m - 1u) * ldc + n); }
+
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
 constexpr uint32_t kMaxGridY = 65535u;
@@ -35,6 +55,11 @@ constexpr uint32_t kMaxGridY = 65535u;
   do {                             \
     if (!(cond)) return fail(status, __VA_ARGS__); \
   } while (0)
+
+// Output buffers must not overlap inputs (the kernels read inputs while other
+// workgroups write the output).
+#define REQUIRE_DISJOINT(name, out, nout, in, nin, what)                                      \
+  REQUIRE(!overlap(out, nout, in, nin), BQ_EINVAL, "%s: the output overlaps %s", name, what)
 
 }  // namespace
 
@@ -75,6 +100,7 @@ int quantize_act_q8_1(const void *act_bf16, void *out_q8, uint32_t m, uint32_t k
   const uint64_t kpad = ((uint64_t)k + 255u) / 256u * 256u;
   const uint64_t blocks = (uint64_t)m * ((kpad + 2047u) / 2048u);
   REQUIRE(blocks < (1ull << 31), BQ_EINVAL, "quantize_act_q8_1: m*k too large");
+  REQUIRE_DISJOINT("quantize_act_q8_1", out_q8, q8_bytes(m, k), act_bf16, bf16_bytes(m, k), "the input");
   return hip_status(bqmm::launch_quantize_act_q8_1(act_bf16, out_q8, m, k, as_stream(stream)),
                     "quantize_act_q8_1");
 }
@@ -88,17 +114,25 @@ int silu_mul_quantize_q8_1(const void *gate_bf16, const void *up_bf16, void *out
   const uint64_t kpad = ((uint64_t)k + 255u) / 256u * 256u;
   const uint64_t blocks = (uint64_t)m * ((kpad + 2047u) / 2048u);
   REQUIRE(blocks < (1ull << 31), BQ_EINVAL, "silu_mul_quantize_q8_1: m*k too large");
+  REQUIRE_DISJOINT("silu_mul_quantize_q8_1", out_q8, q8_bytes(m, k), gate_bf16, bf16_bytes(m, k), "gate");
+  REQUIRE_DISJOINT("silu_mul_quantize_q8_1", out_q8, q8_bytes(m, k), up_bf16, bf16_bytes(m, k), "up");
   return hip_status(bqmm::launch_silu_mul_quantize_q8_1(gate_bf16, up_bf16, out_q8, m, k, as_stream(stream)),
                     "silu_mul_quantize_q8_1");
 }
 
+// out_bytes: the span the call writes (0 = the plain [m][n] bf16 output;
+// ~0 = no range check here, the caller does it after its own checks)
 static int check_mmq(const char *name, const void *act_q8, const void *w, const void *out,
-                     uint32_t m, uint32_t n, uint32_t k, uint32_t kmult) {
+                     uint32_t m, uint32_t n, uint32_t k, uint32_t kmult, uint64_t out_bytes = 0) {
   REQUIRE(act_q8 && w && out, BQ_EINVAL, "%s: null pointer", name);
   REQUIRE(m >= 1 && n >= 1 && k >= 1, BQ_EINVAL, "%s: m=%u n=%u k=%u must be >= 1", name, m, n, k);
   REQUIRE(k % kmult == 0, BQ_EINVAL, "%s: k=%u must be a multiple of %u", name, k, kmult);
   REQUIRE(aligned16(act_q8) && aligned16(w) && aligned16(out), BQ_EALIGN, "%s: buffers must be 16-byte aligned", name);
   REQUIRE((m + 127u) / 128u <= kMaxGridY, BQ_EINVAL, "%s: m=%u too large", name, m);
+  if (out_bytes == ~0ull) return BQ_OK;  // the caller checks the ranges itself
+  const uint64_t nout = out_bytes ? out_bytes : bf16_bytes(m, n);
+  REQUIRE_DISJOINT(name, out, nout, act_q8, q8_bytes(m, k), "the q8_1 activations");
+  REQUIRE_DISJOINT(name, out, nout, w, kmult == 256u ? q4k_bytes(n, k) : q2_bytes(n, k), "the weight");
   return BQ_OK;
 }
 
@@ -113,9 +147,10 @@ int q2_0_mmq_gemm(const void *act_q8, const void *w_q2, void *out_bf16, uint32_t
 
 int q2_0_mmq_gemm_ldc(const void *act_q8, const void *w_q2, void *out_bf16, uint32_t m, uint32_t n,
                       uint32_t k, uint32_t ldc, void *stream) {
-  const int st = check_mmq("q2_0_mmq_gemm_ldc", act_q8, w_q2, out_bf16, m, n, k, 128u);
-  if (st != BQ_OK) return st;
   REQUIRE(ldc >= n, BQ_EINVAL, "q2_0_mmq_gemm_ldc: ldc=%u must be >= n=%u", ldc, n);
+  const int st = check_mmq("q2_0_mmq_gemm_ldc", act_q8, w_q2, out_bf16, m, n, k, 128u,
+                           m >= 1 && n >= 1 ? strided_bytes(m, n, ldc) : 0);
+  if (st != BQ_OK) return st;
   return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, out_bf16, nullptr, 0, 0, 0, 0, m, n, k, ldc,
                                           as_stream(stream)),
                     "q2_0_mmq_gemm_ldc");
@@ -132,9 +167,10 @@ int q4k_mmq_gemm(const void *act_q8, const void *w_q4k, void *out_bf16, uint32_t
 
 int q4k_mmq_gemm_ldc(const void *act_q8, const void *w_q4k, void *out_bf16, uint32_t m, uint32_t n,
                      uint32_t k, uint32_t ldc, void *stream) {
-  const int st = check_mmq("q4k_mmq_gemm_ldc", act_q8, w_q4k, out_bf16, m, n, k, 256u);
-  if (st != BQ_OK) return st;
   REQUIRE(ldc >= n, BQ_EINVAL, "q4k_mmq_gemm_ldc: ldc=%u must be >= n=%u", ldc, n);
+  const int st = check_mmq("q4k_mmq_gemm_ldc", act_q8, w_q4k, out_bf16, m, n, k, 256u,
+                           m >= 1 && n >= 1 ? strided_bytes(m, n, ldc) : 0);
+  if (st != BQ_OK) return st;
   return hip_status(bqmm::launch_q4k_mmq(act_q8, w_q4k, out_bf16, nullptr, 0, 0, 0, 0, m, n, k, ldc,
                                          as_stream(stream)),
                     "q4k_mmq_gemm_ldc");
@@ -143,12 +179,13 @@ int q4k_mmq_gemm_ldc(const void *act_q8, const void *w_q4k, void *out_bf16, uint
 static int check_blockdots(const char *name, const void *act_q8, const void *w, const int32_t *out,
                            uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m, uint32_t n,
                            uint32_t k, uint32_t kmult) {
-  const int st = check_mmq(name, act_q8, w, out, m, n, k, kmult);
+  int st = check_mmq(name, act_q8, w, out, m, n, k, kmult, ~0ull);
   if (st != BQ_OK) return st;
   REQUIRE(mt >= 1 && nt >= 1, BQ_EINVAL, "%s: empty window", name);
   REQUIRE((uint64_t)m0 + mt <= m && (uint64_t)n0 + nt <= n, BQ_EINVAL,
           "%s: window [%u,+%u) x [%u,+%u) outside [0,%u) x [0,%u)", name, m0, mt, n0, nt, m, n);
-  return BQ_OK;
+  // the window's block dots as int32, then the usual rule: no overlap with the inputs
+  return check_mmq(name, act_q8, w, out, m, n, k, kmult, 4u * (uint64_t)mt * nt * (k / 32u));
 }
 
 int q2_0_mmq_blockdots(const void *act_q8, const void *w_q2, int32_t *out, uint32_t m0, uint32_t mt,
@@ -177,6 +214,8 @@ static int check_gemv(const char *name, const void *act, const void *w, const vo
   REQUIRE(m >= 1, BQ_EINVAL, "%s: m must be >= 1", name);
   REQUIRE(m <= 8, BQ_EUNSUPPORTED, "%s: m=%u > 8 (use the MMQ path)", name, m);
   REQUIRE(aligned16(act) && aligned16(w) && aligned16(out), BQ_EALIGN, "%s: buffers must be 16-byte aligned", name);
+  REQUIRE_DISJOINT(name, out, bf16_bytes(m, n), act, bf16_bytes(m, k), "the activations");
+  REQUIRE_DISJOINT(name, out, bf16_bytes(m, n), w, q2_bytes(n, k), "the weight");
   return BQ_OK;
 }
 
@@ -202,7 +241,7 @@ int q2_0_gemv_gate_up_silu(const void *act_bf16, const void *w_gate_q2, const vo
   if (st != BQ_OK) return st;
   REQUIRE(w_up_q2, BQ_EINVAL, "q2_0_gemv_gate_up_silu: null pointer");
   REQUIRE(aligned16(w_up_q2), BQ_EALIGN, "q2_0_gemv_gate_up_silu: buffers must be 16-byte aligned");
-  REQUIRE(out_bf16 != act_bf16, BQ_EINVAL, "q2_0_gemv_gate_up_silu: out must not alias act");
+  REQUIRE_DISJOINT("q2_0_gemv_gate_up_silu", out_bf16, bf16_bytes(m, n), w_up_q2, q2_bytes(n, k), "the up weight");
   return hip_status(bqmm::launch_q2_0_gemv_gate_up_silu(act_bf16, w_gate_q2, w_up_q2, out_bf16, m, n, k,
                                                         as_stream(stream)),
                     "q2_0_gemv_gate_up_silu");
@@ -216,6 +255,8 @@ int q4k_gemv_vec(const void *act_bf16, const void *w_q4k, void *out_bf16, uint32
   REQUIRE(k <= 65536u, BQ_EUNSUPPORTED, "q4k_gemv_vec: k=%u > 65536", k);
   REQUIRE(aligned16(act_bf16) && aligned16(w_q4k) && aligned16(out_bf16), BQ_EALIGN,
           "q4k_gemv_vec: buffers must be 16-byte aligned");
+  REQUIRE_DISJOINT("q4k_gemv_vec", out_bf16, bf16_bytes(1, n), act_bf16, bf16_bytes(1, k), "the activations");
+  REQUIRE_DISJOINT("q4k_gemv_vec", out_bf16, bf16_bytes(1, n), w_q4k, q4k_bytes(n, k), "the weight");
   return hip_status(bqmm::launch_q4k_gemv(act_bf16, w_q4k, out_bf16, n, k, as_stream(stream)), "q4k_gemv_vec");
 }
 
@@ -225,6 +266,7 @@ int quantize_weight_q4k(const void *w_bf16, void *out_q4k, uint32_t n, uint32_t 
   REQUIRE(k % 256u == 0, BQ_EINVAL, "quantize_weight_q4k: k=%u must be a multiple of 256", k);
   REQUIRE(aligned16(w_bf16) && aligned16(out_q4k), BQ_EALIGN,
           "quantize_weight_q4k: buffers must be 16-byte aligned");
+  REQUIRE_DISJOINT("quantize_weight_q4k", out_q4k, q4k_bytes(n, k), w_bf16, bf16_bytes(n, k), "the input");
   return hip_status(bqmm::launch_quantize_weight_q4k(w_bf16, out_q4k, n, k, as_stream(stream)),
                     "quantize_weight_q4k");
 }
@@ -236,6 +278,8 @@ static int check_dequant(const void *w, const void *out, uint32_t n, uint32_t k,
           "dequant_q2_0_to_bf16: group=%u must be a positive multiple of 32", group);
   REQUIRE(k % group == 0, BQ_EINVAL, "dequant_q2_0_to_bf16: k=%u not a multiple of group=%u", k, group);
   REQUIRE(aligned16(w) && aligned16(out), BQ_EALIGN, "dequant_q2_0_to_bf16: buffers must be 16-byte aligned");
+  REQUIRE_DISJOINT("dequant_q2_0_to_bf16", out, bf16_bytes(n, k), w,
+                   (uint64_t)n * k / 4u + 2u * (uint64_t)n * (k / group), "the weight");
   return BQ_OK;
 }
 
@@ -253,6 +297,8 @@ static int check_dense(const void *a, const void *w, const void *out, uint32_t m
   REQUIRE(k % 64u == 0, BQ_EINVAL, "dense_gemm_bf16: k=%u must be a multiple of 64", k);
   REQUIRE(aligned16(a) && aligned16(w) && aligned16(out), BQ_EALIGN, "dense_gemm_bf16: buffers must be 16-byte aligned");
   REQUIRE((n + 127u) / 128u <= kMaxGridY, BQ_EINVAL, "dense_gemm_bf16: n=%u too large", n);
+  REQUIRE_DISJOINT("dense_gemm_bf16", out, bf16_bytes(m, n), a, bf16_bytes(m, k), "the activations");
+  REQUIRE_DISJOINT("dense_gemm_bf16", out, bf16_bytes(m, n), w, bf16_bytes(n, k), "the weight");
   return BQ_OK;
 }
 
@@ -274,6 +320,8 @@ int q2_0_prefill_gemm(const void *act_bf16, const void *w_q2, void *out_bf16, vo
     REQUIRE(aligned16(act_bf16), BQ_EALIGN, "q2_0_prefill_gemm: input must be 16-byte aligned");
     int st = check_mmq("q2_0_prefill_gemm", act_q8, w_q2, out_bf16, m, n, k, 128u);
     if (st != BQ_OK) return st;
+    REQUIRE_DISJOINT("q2_0_prefill_gemm", act_q8, q8_bytes(m, k), act_bf16, bf16_bytes(m, k), "the input");
+    REQUIRE_DISJOINT("q2_0_prefill_gemm", act_q8, q8_bytes(m, k), w_q2, q2_bytes(n, k), "the weight");
     st = hip_status(bqmm::launch_quantize_act_q8_1(act_bf16, act_q8, m, k, as_stream(stream)),
                     "q2_0_prefill_gemm (quantize)");
     if (st != BQ_OK) return st;
@@ -286,6 +334,9 @@ int q2_0_prefill_gemm(const void *act_bf16, const void *w_q2, void *out_bf16, vo
   if (st != BQ_OK) return st;
   st = check_dense(act_bf16, scratch_bf16, out_bf16, m, n, k);
   if (st != BQ_OK) return st;
+  REQUIRE_DISJOINT("q2_0_prefill_gemm", scratch_bf16, bf16_bytes(n, k), act_bf16, bf16_bytes(m, k), "the input");
+  REQUIRE_DISJOINT("q2_0_prefill_gemm", out_bf16, bf16_bytes(m, n), w_q2,
+                   (uint64_t)n * k / 4u + 2u * (uint64_t)n * (k / group), "the weight");
   st = hip_status(bqmm::launch_dequant_q2_0(w_q2, scratch_bf16, n, k, group, as_stream(stream)),
                   "q2_0_prefill_gemm (dequant)");
   if (st != BQ_OK) return st;
@@ -300,6 +351,9 @@ int silu_mul_bf16(const void *gate, const void *up, void *out, uint64_t count, v
   REQUIRE(((reinterpret_cast<uintptr_t>(gate) | reinterpret_cast<uintptr_t>(up) |
             reinterpret_cast<uintptr_t>(out)) & 1u) == 0u,
           BQ_EALIGN, "silu_mul_bf16: bf16 buffers must be 2-byte aligned");
+  REQUIRE(out == gate || !overlap(out, 2u * count, gate, 2u * count), BQ_EINVAL,
+          "silu_mul_bf16: the output overlaps gate (only out == gate is allowed)");
+  REQUIRE(!overlap(out, 2u * count, up, 2u * count), BQ_EINVAL, "silu_mul_bf16: the output overlaps up");
   return hip_status(bqmm::launch_silu_mul(gate, up, out, count, as_stream(stream)), "silu_mul_bf16");
 }
 

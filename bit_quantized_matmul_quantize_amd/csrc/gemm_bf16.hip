@@ -146,9 +146,8 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gemm_bf16_kernel(
 hipError_t launch_dense_gemm_bf16(const void *a, const void *w, void *out, uint32_t m, uint32_t n,
                                   uint32_t k, hipStream_t s) {
   // two stages (73.7 KB) exceed the 64 KB default dynamic-LDS limit
-  static const hipError_t attr_err = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(dense_gemm_bf16_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      2 * kStageBytes);
+  const hipError_t attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(dense_gemm_bf16_kernel),
+                                                 2 * kStageBytes);
   if (attr_err != hipSuccess) return attr_err;
   const dim3 grid((m + BM - 1) / BM, (n + BN - 1) / BN);
   hipLaunchKernelGGL(dense_gemm_bf16_kernel, grid, dim3(kThreads), 2 * kStageBytes, s,

@@ -219,10 +219,11 @@ template <int G, int R>
 hipError_t launch_g(const void *act, const void *w, void *out, uint32_t n, uint32_t k, hipStream_t s) {
   const uint32_t U = (k >> 8) * 4u, Upad = (U + G - 1) / G * G;
   const size_t lds = (size_t)Upad * kUnitDw * 4u;
-  static const hipError_t attr_err = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(q4k_gemv1_kernel<G, R>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)((size_t)(kMaxK / 64u) * kUnitDw * 4u));
-  if (attr_err != hipSuccess) return attr_err;
+  if (lds > 65536) {
+    const hipError_t attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(q4k_gemv1_kernel<G, R>),
+                                                   (int)((size_t)(kMaxK / 64u) * kUnitDw * 4u));
+    if (attr_err != hipSuccess) return attr_err;
+  }
   constexpr uint32_t rows_per_block = kThreads / G * R;
   const uint32_t blocks = (n + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL((q4k_gemv1_kernel<G, R>), dim3(blocks), dim3(kThreads), lds, s,

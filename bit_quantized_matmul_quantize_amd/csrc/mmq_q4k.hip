@@ -267,14 +267,9 @@ hipError_t launch_q4k_mmq(const void *act_q8, const void *w, void *out, int32_t 
                           uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m,
                           uint32_t n, uint32_t k, uint32_t ldc, hipStream_t s) {
   // Two stages exceed the 64 KB default dynamic-LDS limit; gfx950 allows 160 KB.
-  static const hipError_t attr_err = [] {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(q4k_mmq_kernel<false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void *>(q4k_mmq_kernel<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
-    return e;
-  }();
+  hipError_t attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(q4k_mmq_kernel<false>), 2 * kStageBytes);
+  if (attr_err == hipSuccess)
+    attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(q4k_mmq_kernel<true>), 2 * kStageBytes);
   if (attr_err != hipSuccess) return attr_err;
   if (dots == nullptr) {
     const dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);

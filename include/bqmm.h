@@ -44,11 +44,15 @@
  *
  * Alignment: weight, activation and q8_1 pointers must be 16-byte aligned
  * (BQ_EALIGN otherwise); bf16 row lengths used by vector loads are noted per
- * call.  Inputs and outputs must not overlap unless a call says so.
+ * call.  Inputs and outputs must not overlap unless a call says so; every
+ * call checks the byte ranges its shapes give and returns BQ_EINVAL when an
+ * output range shares a byte with an input range.
  *
  * Only a gfx950 code object is built; on other devices calls fail with
  * BQ_EHIP.  The library keeps no mutable state besides the per-thread error
- * message; calls from different threads are independent.
+ * message and a lock-protected record of the devices on which a kernel's
+ * dynamic-LDS limit has been raised; calls from different threads are
+ * independent.
  */
 #ifndef BQMM_H
 #define BQMM_H
@@ -156,7 +160,8 @@ int q2_0_gemv_vec_batchm(const void *act_bf16, const void *w_q2, void *out_bf16,
  * [page layers/dense_ffn_decode_batch.rs, fn forward_km_q2: gate and up
  *  GEMVs, then silu_mul into the gate buffer.]
  * act [m][k] bf16; w_gate, w_up: Q2_0 [n][k] group 128; out [m][n] bf16 and
- * must not alias act.  k % 128 == 0, n >= 1, m > 8 -> BQ_EUNSUPPORTED. */
+ * must not overlap act or either weight.  k % 128 == 0, n >= 1,
+ * m > 8 -> BQ_EUNSUPPORTED. */
 int q2_0_gemv_gate_up_silu(const void *act_bf16, const void *w_gate_q2, const void *w_up_q2,
                            void *out_bf16, uint32_t m, uint32_t n, uint32_t k, void *stream);
 

@@ -81,7 +81,8 @@ def _err(bq):
     (lambda l: l.q2_0_gemv_gate_up_silu(A, B, C, D, 9, 256, 512, None), -2, "m=9"),
     (lambda l: l.q2_0_gemv_gate_up_silu(A, B, None, D, 2, 256, 512, None), -1, "null"),
     (lambda l: l.q2_0_gemv_gate_up_silu(A, B, MIS, D, 2, 256, 512, None), -3, "aligned"),
-    (lambda l: l.q2_0_gemv_gate_up_silu(A, B, C, A, 2, 256, 512, None), -1, "alias"),
+    (lambda l: l.q2_0_gemv_gate_up_silu(A, B, C, A, 2, 256, 512, None), -1, "overlaps the activations"),
+    (lambda l: l.q2_0_gemv_gate_up_silu(A, B, C, P(0x30000 + 512), 2, 256, 512, None), -1, "overlaps the up weight"),
     (lambda l: l.q2_0_gemv_gate_up_silu(A, B, C, D, 2, 256, 300, None), -1, "group size 128"),
     (lambda l: l.dequant_q2_0_to_bf16(A, B, 4, 512, 48, None), -2, "multiple of 32"),
     (lambda l: l.dequant_q2_0_to_bf16(A, B, 4, 480, 128, None), -1, "not a multiple"),
@@ -105,6 +106,24 @@ def _err(bq):
     (lambda l: l.quantize_weight_q4k(A, None, 4, 512, None), -1, "null"),
     (lambda l: l.quantize_weight_q4k(A, MIS, 4, 512, None), -3, "aligned"),
     (lambda l: l.quantize_weight_q4k(A, B, 0, 512, None), -1, "n=0"),
+    # outputs overlapping inputs (byte extents from the shapes)
+    (lambda l: l.quantize_act_q8_1(A, P(0x10000 + 1024), 4, 512, None), -1, "overlaps the input"),
+    (lambda l: l.silu_mul_quantize_q8_1(A, B, P(0x20000 + 16), 4, 512, None), -1, "overlaps up"),
+    (lambda l: l.q2_0_mmq_gemm(A, B, P(0x20000 + 256), 4, 256, 512, None), -1, "overlaps the weight"),
+    (lambda l: l.q2_0_mmq_gemm(A, B, A, 4, 256, 512, None), -1, "overlaps the q8_1"),
+    # the row stride widens the written span: [m][n] alone would end before the weight
+    (lambda l: l.q2_0_mmq_gemm_ldc(A, B, P(0x20000 - 4096), 4, 256, 512, 1024, None), -1, "overlaps the weight"),
+    (lambda l: l.q4k_mmq_blockdots(A, B, P(0x20000 + 64), 0, 1, 0, 1, 4, 256, 512, None), -1, "overlaps the weight"),
+    (lambda l: l.q2_0_gemv_vec(A, B, A, 256, 512, None), -1, "overlaps the activations"),
+    (lambda l: l.q2_0_gemv_vec_batchm(A, B, P(0x20000 + 32), 3, 256, 512, None), -1, "overlaps the weight"),
+    (lambda l: l.q4k_gemv_vec(A, B, B, 256, 512, None), -1, "overlaps the weight"),
+    (lambda l: l.quantize_weight_q4k(A, A, 4, 512, None), -1, "overlaps the input"),
+    (lambda l: l.dequant_q2_0_to_bf16(A, P(0x10000 + 64), 4, 512, 128, None), -1, "overlaps the weight"),
+    (lambda l: l.dense_gemm_bf16(A, B, P(0x20000 + 128), 4, 4, 64, None), -1, "overlaps the weight"),
+    (lambda l: l.q2_0_prefill_gemm(A, B, C, None, P(0x10000 + 64), 4, 4, 512, 128, 1, None), -1, "overlaps the input"),
+    (lambda l: l.q2_0_prefill_gemm(A, B, C, P(0x10000 + 64), None, 4, 4, 512, 128, 0, None), -1, "overlaps the input"),
+    (lambda l: l.silu_mul_bf16(A, B, P(0x10000 + 16), 64, None), -1, "overlaps gate"),
+    (lambda l: l.silu_mul_bf16(A, B, B, 64, None), -1, "overlaps up"),
 ])
 def test_validation_rejects_before_any_hip_call(bq, call, status, needle):
     assert call(bq.lib()) == status

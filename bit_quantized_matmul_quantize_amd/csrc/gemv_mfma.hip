@@ -38,11 +38,11 @@
 // two 8-wave workgroups share a CU and all 363 fit at once (20.4 us, was 25.4
 // with T = 2 at 134 VGPRs, one workgroup per CU and 544 of them); narrow
 // (n = 5120) T = 2, 160 workgroups (24.7 us, was 31.2 with T = 1); fused
-// gate/up T = 3 of each weight (36.7 us, was 46.1 with T = 1).  There is no barrier in the main loop.
-// A wave's weight scales are staged once in LDS ([group][row], so one 8-byte
-// read gives the four rows of a lane's outputs).  Loads run P groups ahead,
-// unconditionally from clamped addresses.
-#include "bqmm_internal.h"
+// gate/up T = 3 of each weight (36.7 us, was 46.1 with T = 1).  There is no
+// barrier in the main loop.  A wave's weight scales are staged once in LDS
+// ([group][row], so one 8-byte read gives the four rows of a lane's
+// outputs).  Loads run P groups ahead, unconditionally from clamped addresses.
+#include "gemv_common.h"
 
 namespace bqmm {
 namespace {
@@ -50,16 +50,6 @@ namespace {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t vconst_(uint32_t c) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
-  return r;
-}
-
-__device__ __forceinline__ uint32_t and_or_(uint32_t x, uint32_t mask, uint32_t bits) {
-  return (x & mask) | bits;
-}
 
 __device__ __forceinline__ v8bf as_bf8(v4u x) { return __builtin_bit_cast(v8bf, x); }
 
@@ -146,10 +136,10 @@ __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint
 
   for (uint32_t base = 64u * kStageBatch; base < nst; base += 64u * kStageBatch) stage_round(base);
 
-  const uint32_t M0 = vconst_(0x00030003u), M1 = vconst_(0x000C000Cu), M2 = vconst_(0x00300030u),
-                 M3 = vconst_(0x00600060u);
-  const uint32_t G0 = vconst_(0x43004300u), G1 = vconst_(0x42004200u), G2 = vconst_(0x41004100u),
-                 G3 = vconst_(0x40804080u);
+  const uint32_t M0 = vconst(0x00030003u), M1 = vconst(0x000C000Cu), M2 = vconst(0x00300030u),
+                 M3 = vconst(0x00600060u);
+  const uint32_t G0 = vconst(0x43004300u), G1 = vconst(0x42004200u), G2 = vconst(0x41004100u),
+                 G3 = vconst(0x40804080u);
   // -(2^e_j + 2) = -130, -34, -10, -6 in bf16, eight per lane
   const v4u NK[4] = {v4u{0xC302C302u, 0xC302C302u, 0xC302C302u, 0xC302C302u},
                      v4u{0xC208C208u, 0xC208C208u, 0xC208C208u, 0xC208C208u},
@@ -174,11 +164,11 @@ __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint
       const uint32_t x0_ = __builtin_amdgcn_perm(cq[slot][t].x, cq[slot][t].x, 0x03010200u); \
       const uint32_t x1_ = __builtin_amdgcn_perm(cq[slot][t].y, cq[slot][t].y, 0x03010200u); \
       const uint32_t y0_ = x0_ >> 8, y1_ = x1_ >> 8;                                \
-      const v4u a0_ = {and_or_(x0_, M0, G0), and_or_(y0_, M0, G0), and_or_(x1_, M0, G0), and_or_(y1_, M0, G0)}; \
-      const v4u a1_ = {and_or_(x0_, M1, G1), and_or_(y0_, M1, G1), and_or_(x1_, M1, G1), and_or_(y1_, M1, G1)}; \
-      const v4u a2_ = {and_or_(x0_, M2, G2), and_or_(y0_, M2, G2), and_or_(x1_, M2, G2), and_or_(y1_, M2, G2)}; \
-      const v4u a3_ = {and_or_(x0_ >> 1, M3, G3), and_or_(y0_ >> 1, M3, G3),        \
-                       and_or_(x1_ >> 1, M3, G3), and_or_(y1_ >> 1, M3, G3)};       \
+      const v4u a0_ = {and_or(x0_, M0, G0), and_or(y0_, M0, G0), and_or(x1_, M0, G0), and_or(y1_, M0, G0)}; \
+      const v4u a1_ = {and_or(x0_, M1, G1), and_or(y0_, M1, G1), and_or(x1_, M1, G1), and_or(y1_, M1, G1)}; \
+      const v4u a2_ = {and_or(x0_, M2, G2), and_or(y0_, M2, G2), and_or(x1_, M2, G2), and_or(y1_, M2, G2)}; \
+      const v4u a3_ = {and_or(x0_ >> 1, M3, G3), and_or(y0_ >> 1, M3, G3),        \
+                       and_or(x1_ >> 1, M3, G3), and_or(y1_ >> 1, M3, G3)};       \
       v4f s_ = mfma(a0_, v4u{aq[slot][0].x, aq[slot][0].y, aq[slot][0].z, aq[slot][0].w}, nb_); \
       s_ = mfma(a1_, v4u{aq[slot][1].x, aq[slot][1].y, aq[slot][1].z, aq[slot][1].w}, s_);      \
       s_ = mfma(a2_, v4u{aq[slot][2].x, aq[slot][2].y, aq[slot][2].z, aq[slot][2].w}, s_);      \

@@ -459,6 +459,246 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__
   }
 }
 
+// ---- whole-vector pipelined kernel, m = 1..3 ------------------------------
+//
+// For the verify batches (and m = 1) when the activations of all M rows fit in
+// LDS: they are prepared once per workgroup (no per-slice barriers), and a
+// lane then walks its chunks li, li + G, ... of R rows with the next chunk's
+// weight loads in flight while the current one is computed.  Prep items are
+// (chunk, activation row): the four 32-byte runs of a chunk's 64 values are
+// loaded together (eight 16-byte loads), so a workgroup's prep takes few
+// memory round trips.  LDS per chunk as in the slice kernel (word-major
+// pairs, then the four partial biases; chunks padded so that 16 consecutive
+// chunks read by one instruction hit distinct bank quads); chunks past k hold
+// zero activations and biases, so their clamped weight loads add 0.
+template <int M, int G, int R, int NW>
+__global__ __launch_bounds__(kThreads) void q2_0_gemvp_kernel(const uint16_t *__restrict__ act,
+                                                              const uint8_t *__restrict__ w,
+                                                              const uint8_t *__restrict__ w2,
+                                                              uint16_t *__restrict__ out, uint32_t n,
+                                                              uint32_t k) {
+  static_assert(G == 16 || G == 32, "lane group of 16 or 32");
+  static_assert(NW == 1 || NW == 2, "one weight, or gate and up");
+  constexpr int RR = NW * R;
+  constexpr int CS = gemvm_chunk_dwords(M);
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+  const uint32_t C = k >> 6, Gk = k >> 7;
+  const uint32_t tid = threadIdx.x, li = tid % G, grp = tid / G;
+  const uint32_t iters = (C + G - 1) / G, Cpad = iters * G;
+  const uint32_t row_base = blockIdx.x * (kThreads / G * R) + grp * R;
+
+  const uint8_t *wrow[RR];
+  const uint16_t *srow[RR];
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const uint8_t *wv = v == 0 ? w : w2;
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(wv + (uint64_t)n * k / 4u);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t row = min(row_base + r, n - 1u);
+      wrow[v * R + r] = wv + (uint64_t)row * (k >> 2);
+      srow[v * R + r] = scales + (uint64_t)row * Gk;
+    }
+  }
+  auto load_unit = [&](uint32_t it, uint4 (&wq)[RR], uint32_t (&sc)[RR]) {
+    const uint32_t c = min(li + G * it, C - 1u);
+#pragma unroll
+    for (int r = 0; r < RR; ++r) {
+      wq[r] = *reinterpret_cast<const uint4 *>(wrow[r] + 16u * c);
+      sc[r] = srow[r][c >> 1];
+    }
+  };
+
+  // prep item (chunk c, activation row m): runs j = 0..3 of 16 values at
+  // k = 128 (c / 2) + 32 j + 16 (c % 2)
+  const uint32_t items = Cpad * M;
+  auto load_item = [&](uint32_t item, uint4 (&v)[8]) {
+    const uint32_t c = min(item / M, C - 1u), m = item % M;
+    const uint16_t *src = act + (uint64_t)m * k + 128u * (c >> 1) + 16u * (c & 1u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = *reinterpret_cast<const uint4 *>(src + 32 * j);
+      v[2 * j + 1] = *reinterpret_cast<const uint4 *>(src + 32 * j + 8);
+    }
+  };
+  auto prep_item = [&](uint32_t item, const uint4 (&v)[8]) {
+    const uint32_t c = item / M, m = item % M;
+    const bool live = c < C;
+    uint32_t *dst = smem + c * CS + m * kRowDw;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t D[8] = {v[2 * j].x, v[2 * j].y, v[2 * j].z, v[2 * j].w,
+                       v[2 * j + 1].x, v[2 * j + 1].y, v[2 * j + 1].z, v[2 * j + 1].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) D[i] = live ? D[i] : 0u;
+      uint32_t p[8];
+      act_pairs(D, p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint2 *>(dst + 8 * i + 2 * j) = make_uint2(p[2 * i], p[2 * i + 1]);
+      dst[32 + j] = __float_as_uint(field_bias(D, bias_weight((uint32_t)j)));
+    }
+  };
+
+  uint4 wq0[RR], wq1[RR];
+  uint32_t sc0[RR], sc1[RR];
+  {
+    // the first item's activation loads go out before the first weight loads
+    uint4 v[8];
+    const uint32_t first = min(tid, items - 1u);
+    load_item(first, v);
+    load_unit(0, wq0, sc0);
+    if (tid < items) prep_item(first, v);
+  }
+  for (uint32_t item = tid + kThreads; item < items; item += kThreads) {
+    uint4 v[8];
+    load_item(item, v);
+    prep_item(item, v);
+  }
+  __syncthreads();
+
+  const CodeConsts K = code_consts();
+  float oacc[RR][M];
+#pragma unroll
+  for (int r = 0; r < RR; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) oacc[r][m] = 0.0f;
+
+  // One chunk: per (word i, activation row m) 8 pairs from LDS feed 8 R dot2s;
+  // the next unit's reads are issued before this unit's dot2s, and an empty
+  // asm on the accumulators keeps the compiler from hoisting every read of the
+  // chunk (as in the slice kernel).
+  auto compute = [&](uint32_t it, const uint4 (&wq)[RR], const uint32_t (&sc)[RR]) {
+    uint32_t off = (li + G * it) * CS;
+    float acc[RR][M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint4 bq = *reinterpret_cast<const uint4 *>(smem + off + m * kRowDw + 32);
+      const float nb = -((__uint_as_float(bq.x) + __uint_as_float(bq.y)) +
+                         (__uint_as_float(bq.z) + __uint_as_float(bq.w)));
+#pragma unroll
+      for (int r = 0; r < RR; ++r) acc[r][m] = nb;
+    }
+    uint4 pa = *reinterpret_cast<const uint4 *>(smem + off);
+    uint4 pb = *reinterpret_cast<const uint4 *>(smem + off + 4);
+    uint32_t wp[RR][8];
+#pragma unroll
+    for (int u = 0; u < 4 * M; ++u) {
+      const int i = u / M, m = u % M;
+      if (m == 0) {
+#pragma unroll
+        for (int r = 0; r < RR; ++r) {
+          const uint32_t x = (i == 0) ? wq[r].x : (i == 1) ? wq[r].y : (i == 2) ? wq[r].z : wq[r].w;
+          word_pairs(x, K, wp[r]);
+        }
+      }
+      const uint32_t P[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+      if (u + 1 < 4 * M) {
+        const int i2 = (u + 1) / M, m2 = (u + 1) % M;
+        pa = *reinterpret_cast<const uint4 *>(smem + off + m2 * kRowDw + 8 * i2);
+        pb = *reinterpret_cast<const uint4 *>(smem + off + m2 * kRowDw + 8 * i2 + 4);
+      }
+#pragma unroll
+      for (int r = 0; r < RR; ++r)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[r][m] = dot2(wp[r][q], P[q], acc[r][m]);
+#pragma unroll
+      for (int r = 0; r < RR; ++r) asm volatile("" : "+v"(off) : "v"(acc[r][m]));
+    }
+#pragma unroll
+    for (int r = 0; r < RR; ++r) {
+      const float d = f16_bits_to_f32(sc[r]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) oacc[r][m] = fmaf(d, acc[r][m], oacc[r][m]);
+    }
+  };
+
+  // two register sets alternate; the last one or two chunks are peeled so
+  // that every prefetch is unconditional, and the scheduling barriers keep
+  // each prefetch above the wait for the chunk being computed
+  uint32_t it = 0;
+  for (; it + 2 < iters; it += 2) {
+    load_unit(it + 1, wq1, sc1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(it, wq0, sc0);
+    load_unit(it + 2, wq0, sc0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(it + 1, wq1, sc1);
+  }
+  if (it + 1 < iters) {
+    load_unit(it + 1, wq1, sc1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(it, wq0, sc0);
+    compute(it + 1, wq1, sc1);
+  } else {
+    compute(it, wq0, sc0);
+  }
+
+#pragma unroll
+  for (int r = 0; r < RR; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) oacc[r][m] = (G == 16) ? row16_sum(oacc[r][m]) : half_wave_sum(oacc[r][m]);
+  if (li == (uint32_t)G - 1u) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t row = row_base + r;
+      if (row < n) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          uint32_t h = f32_to_bf16_rne(oacc[r][m]);
+          if (NW == 2) {
+            const float g = bf16_to_f32(h), u = bf16_to_f32(f32_to_bf16_rne(oacc[R + r][m]));
+            h = f32_to_bf16_rne(silu_mul_f32(g, u));
+          }
+          out[(uint64_t)m * n + row] = (uint16_t)h;
+        }
+      }
+    }
+  }
+}
+
+// Launch shape (measured on the FFN shapes, m = 1..3): 16-lane groups; the
+// single kernel serves m rows per lane for m activation rows (each LDS read
+// then feeds m x m products), the fused gate/up kernel one row of each weight.
+// Against the slice kernel: gate [17408, 5120] m = 1/2/3 8.8/11.8/14.6 us
+// (was 10.3/13.5/16.1), down m = 1 12.0 us (was 16.2), fused gate/up m = 1/2/3
+// 13.6/18.2/23.7 us (was 19.6/25.3/30.0).  32-lane groups were slower at
+// m >= 2; with more than 64 KB of LDS (down at m = 2, 3) it is slower than
+// the slice kernel, which keeps those.
+#ifndef BQMM_GEMVP_G
+#define BQMM_GEMVP_G 16
+#endif
+#ifndef BQMM_GEMVP_MAX_LDS
+#define BQMM_GEMVP_MAX_LDS 65536
+#endif
+constexpr uint32_t kMaxLdsP = BQMM_GEMVP_MAX_LDS;
+
+// LDS bytes of the whole-vector kernel for m rows and k (0 if m > 3)
+__host__ __device__ inline uint32_t gemvp_lds_bytes(uint32_t m, uint32_t k) {
+  if (m < 1 || m > 3) return 0;
+  const uint32_t C = k >> 6, Cpad = (C + BQMM_GEMVP_G - 1) / BQMM_GEMVP_G * BQMM_GEMVP_G;
+  const uint32_t cs = m == 1 ? gemvm_chunk_dwords(1) : (m == 2 ? gemvm_chunk_dwords(2) : gemvm_chunk_dwords(3));
+  return Cpad * cs * 4u;
+}
+
+template <int M, int NW>
+hipError_t launch_gemvp(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
+                        hipStream_t s) {
+  constexpr int G = BQMM_GEMVP_G, R = NW == 2 ? 1 : M;
+  const uint32_t lds = gemvp_lds_bytes(M, k);
+  if (lds > 65536u) {
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(q2_0_gemvp_kernel<M, G, R, NW>),
+                                            (int)kMaxLdsP);
+    if (e != hipSuccess) return e;
+  }
+  constexpr uint32_t rows = kThreads / G * R;
+  const uint32_t blocks = (n + rows - 1) / rows;
+  hipLaunchKernelGGL((q2_0_gemvp_kernel<M, G, R, NW>), dim3(blocks), dim3(kThreads), lds, s,
+                     static_cast<const uint16_t *>(act), static_cast<const uint8_t *>(w),
+                     static_cast<const uint8_t *>(w2), static_cast<uint16_t *>(out), n, k);
+  return hipGetLastError();
+}
+
 // Launch shapes (measured): wide outputs (gate/up, n = 17408) take 16-lane
 // groups of three rows (48 rows per workgroup, one slice = 1024 k); narrow
 // outputs with a long k (down, n = 5120, k = 17408) take 32-lane groups of four
@@ -522,8 +762,30 @@ hipError_t launch_gemvm_gate_up(const void *act, const void *wg, const void *wu,
 
 }  // namespace
 
+#ifndef BQMM_GEMVP_ENABLE
+#define BQMM_GEMVP_ENABLE 1
+#endif
+#ifndef BQMM_GEMVP_M1_MIN_K
+#define BQMM_GEMVP_M1_MIN_K 4096
+#endif
+
+// The whole-vector kernel serves m <= 3 where its LDS fits (and m = 1 from
+// BQMM_GEMVP_M1_MIN_K on); the single and fused dispatch make the same choice.
+inline bool use_gemvp(uint32_t m, uint32_t k) {
+  if (!BQMM_GEMVP_ENABLE || m > 3) return false;
+  if (m == 1 && k < BQMM_GEMVP_M1_MIN_K) return false;
+  return gemvp_lds_bytes(m, k) <= kMaxLdsP;
+}
+
 hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
                             uint32_t k, hipStream_t s) {
+  if (use_gemvp(m, k)) {
+    switch (m) {
+      case 1: return launch_gemvp<1, 1>(act, w, nullptr, out, n, k, s);
+      case 2: return launch_gemvp<2, 1>(act, w, nullptr, out, n, k, s);
+      default: return launch_gemvp<3, 1>(act, w, nullptr, out, n, k, s);
+    }
+  }
   if (m == 1 && k <= kMaxK1) {
     const uint32_t blocks = (n + 8 * kRowsPerLane - 1) / (8 * kRowsPerLane);
     const size_t lds = (size_t)(k >> 6) * kChunkStride * 4u;
@@ -555,6 +817,13 @@ hipError_t launch_q2_0_gemv_gate_up_silu(const void *act, const void *w_gate, co
                                          hipStream_t s) {
   // One launch for every m, on the kernel the single GEMV uses for that m, so
   // the result equals GEMV, GEMV, silu_mul.
+  if (use_gemvp(m, k)) {
+    switch (m) {
+      case 1: return launch_gemvp<1, 2>(act, w_gate, w_up, out, n, k, s);
+      case 2: return launch_gemvp<2, 2>(act, w_gate, w_up, out, n, k, s);
+      default: return launch_gemvp<3, 2>(act, w_gate, w_up, out, n, k, s);
+    }
+  }
   if (m >= kMinMMfma && k <= kMaxKMfma)
     return launch_q2_0_gemv_mfma_gate_up(act, w_gate, w_up, out, m, n, k, s);
   switch (m) {

@@ -5,8 +5,8 @@
  * unless stated otherwise.  `stream` is a hipStream_t passed as void*; NULL
  * means the legacy default stream.  Every call enqueues its kernels on that
  * stream and returns without synchronizing: errors raised while the kernels
- * run surface at the caller's next synchronization.  No call allocates,
- * frees or synchronizes; all buffers belong to the caller (the reference
+ * run surface at the caller's next synchronization.  No call allocates or
+ * frees device memory or synchronizes; all buffers belong to the caller (the reference
  * dispatcher passes its scratch and q8_1 buffers in and "allocates nothing":
  * page layers/qwen3_ssm/init_q2.rs, fn qkvz_q2_prefill_gemm).
  *

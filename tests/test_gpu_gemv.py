@@ -51,7 +51,12 @@ def test_decode_qkvz_full(gpu):
                                         (6, 100, 512, 39), (6, 8192 + 16, 2048, 40),
                                         (4, 8192 + 16, 2048, 41),   # wide: 3 tiles per wave, last workgroup ragged
                                         (5, 1000, 1024, 42),        # narrow: 2 tiles per wave, ragged
-                                        (4, 151, 1152, 43)])
+                                        (4, 151, 1152, 43),
+                                        # whole-vector kernel (m <= 3): shortest k, and the largest
+                                        # k whose activations fit its LDS for each m, and one past it
+                                        (2, 5, 128, 44), (3, 49, 256, 45), (1, 77, 28672, 46),
+                                        (2, 65, 13312, 47), (3, 33, 9216, 48), (2, 33, 13440, 49),
+                                        (1, 4096 + 16, 4096, 50)])
 def test_ragged(gpu, m, n, k, seed):
     g = inputs.rng(seed)
     w = inputs.q2_0_weight(g, n, k)
@@ -184,9 +189,10 @@ def _chain_bits(gpu, act, wg, wu, m, n, k):
 
 @pytest.mark.parametrize("m,n,k,seed", [(2, 17408, 5120, 41), (3, 300, 1152, 42), (5, 8192 + 45, 2048, 43),
                                         (4, 33, 17408, 44), (8, 17408, 5120, 46), (6, 300, 1152, 47),
-                                        (7, 40, 512, 48)])
+                                        (7, 40, 512, 48), (3, 33, 9216, 49), (2, 5, 128, 50)])
 def test_fused_gate_up_equals_chain(gpu, m, n, k, seed):
     # m >= 2: the fused kernel sums every row exactly as the single GEMV does
+    # (same kernel family, lane-group width and chunk order for each m)
     g = inputs.rng(seed)
     wg, wu = inputs.q2_0_weight(g, n, k), inputs.q2_0_weight(g, n, k)
     act = inputs.activations(g, m, k, outliers=True)

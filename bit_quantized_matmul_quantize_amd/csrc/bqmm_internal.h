@@ -7,6 +7,7 @@
 
 #include <mutex>
 #include <tuple>
+#include <utility>
 #include <vector>
 
 namespace bqmm {
@@ -61,6 +62,27 @@ inline hipError_t ensure_dynamic_lds(const void *kernel, int bytes) {
   e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess) done.emplace_back(kernel, dev, bytes);
   return e;
+}
+
+// Compute units of the current device, queried once per device.
+inline hipError_t device_cu_count(int *cus) {
+  static std::mutex mu;
+  static std::vector<std::pair<int, int>> known;  // device, compute units
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto &p : known)
+    if (p.first == dev) {
+      *cus = p.second;
+      return hipSuccess;
+    }
+  int v = 0;
+  e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  known.emplace_back(dev, v);
+  *cus = v;
+  return hipSuccess;
 }
 
 // Batch size from which the batched Q2_0 GEMV (single and fused gate/up) runs

@@ -7,10 +7,12 @@
 // out[m][n] = sum_g dw[n][g] * sum_{b in g} da[m][b] * D[m][n][b],
 //   D[m][n][b] = sum_{t<32} (c - 2) * q   (exact int32, one 32-block).
 //
-// Tile 128 (n) x 128 (m), 256 lanes = 4 waves of 64 (n) x 64 (m).  Per
+// Tile BN (n) x 128 (m), 256 lanes = 4 waves, each of TN x TM 32 x 32
+// subtiles: 128 x 128 (waves of 64 x 64) by default, and 96 x 128 (waves of
+// 96 x 32) where that fills the chip in fewer rounds of workgroups.  Per
 // 128-wide k group the workgroup stages into LDS:
 //   * the q8_1 codes of its 128 rows (int8, 128 B per row),
-//   * the packed 2-bit codes of its 128 weight rows, unpacked once to signed
+//   * the packed 2-bit codes of its BN weight rows, unpacked once to signed
 //     int8 (c - 2) with a byte-permute lookup,
 //   * the group's weight scales (fp32) and, per activation row and block, an
 //     integer multiplier mu = da * 2^(30 - E) where E is the binary16
@@ -30,15 +32,13 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BN = 128;       // weight rows per tile
 constexpr int BM = 128;       // activation rows per tile
 constexpr int KG = 128;       // k per stage (one Q2_0 group = four q8_1 blocks)
 constexpr int LDS_STRIDE = KG + 16;  // bytes per staged row; the pad spreads banks
 constexpr int kThreads = 256;
-// one LDS stage: activation codes, unpacked weight codes, weight scales, multipliers
 constexpr int kActBytes = BM * LDS_STRIDE;
-constexpr int kWBytes = BN * LDS_STRIDE;
-constexpr int kStageBytes = kActBytes + kWBytes + BN * 4 + BM * 16;
+// one LDS stage: activation codes, unpacked weight codes, weight scales, multipliers
+__host__ __device__ constexpr int stage_bytes(int bn) { return kActBytes + bn * LDS_STRIDE + bn * 4 + BM * 16; }
 
 __device__ __forceinline__ int mad_i24(int a, int b, int c) {
   // a, b fit in 24 bits (|D| <= 8128, mu < 2^16); one v_mad_i32_i24.
@@ -52,11 +52,19 @@ __device__ __forceinline__ uint32_t unpack_signed(uint32_t word, int j) {
   return __builtin_amdgcn_perm(0u, 0x0100FFFEu, sel);
 }
 
-template <bool kDump>
+// TN x TM subtiles of 32 x 32 per wave, WN waves along n (4 / WN along m).
+template <bool kDump, int TN, int TM, int WN>
 __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
     const uint8_t *__restrict__ act_q8, const uint8_t *__restrict__ w, uint16_t *__restrict__ out,
     int32_t *__restrict__ dots, uint32_t m, uint32_t n, uint32_t k, uint32_t m0, uint32_t mt,
     uint32_t n0, uint32_t nt, uint32_t tile_n0, uint32_t tile_m0, uint32_t ldc) {
+  constexpr int WM = 4 / WN;
+  constexpr int BN = 32 * TN * WN;
+  static_assert(WN * WM == 4 && 32 * TM * WM == BM, "four waves cover 128 activation rows");
+  static_assert(2 * BN <= kThreads && BN + BM <= kThreads, "one staging thread per 16 weight bytes and per scale row");
+  constexpr int kWBytes = BN * LDS_STRIDE;
+  constexpr int kStageBytes = stage_bytes(BN);
+  constexpr int kSteps = 4 * TN * TM;  // (n-subtile, m-subtile, block) per group
   // Two LDS stages (dynamic shared memory, kStageBytes each): group g is
   // computed from stage g % 2 while group g + 1 is written into the other.
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -65,7 +73,7 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u, l32 = lane & 31u, hi = lane >> 5;
   const uint32_t wave = tid >> 6;
-  const uint32_t wn = wave & 1u, wm = wave >> 1;
+  const uint32_t wn = wave % WN, wm = wave / WN;
   const uint32_t n_base = (blockIdx.x + tile_n0) * BN;
   const uint32_t m_base = (blockIdx.y + tile_m0) * BM;
   const uint32_t kpad = (k + 255u) / 256u * 256u;
@@ -75,12 +83,16 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
   const uint16_t *wscale = reinterpret_cast<const uint16_t *>(w + (uint64_t)n * k / 4u);
 
   // Global -> register staging.  Rows past m or n read the last valid row
-  // (no branch around the loads); their results are never stored.
+  // (no branch around the loads); their results are never stored.  Threads
+  // beyond the 2 BN weight loaders and the BN + BM scale loaders load a
+  // valid row too and skip the LDS write.
   const uint32_t a_row[4] = {min(m_base + (tid >> 3), m - 1u), min(m_base + 32u + (tid >> 3), m - 1u),
                              min(m_base + 64u + (tid >> 3), m - 1u), min(m_base + 96u + (tid >> 3), m - 1u)};
   const uint32_t a_col = (tid & 7u) * 16u;
-  const uint32_t w_row = min(n_base + (tid >> 1), n - 1u), w_half = tid & 1u;
-  const uint32_t s_row = (tid < BN) ? min(n_base + tid, n - 1u) : min(m_base + tid - BN, m - 1u);
+  const bool w_stager = (2 * BN == kThreads) || tid < 2u * BN;
+  const bool s_stager = (BN + BM == kThreads) || tid < (uint32_t)(BN + BM);
+  const uint32_t w_row = min(n_base + (w_stager ? tid >> 1 : 0u), n - 1u), w_half = tid & 1u;
+  const uint32_t s_row = (tid < BN) ? min(n_base + tid, n - 1u) : min(m_base + (s_stager ? tid - BN : 0u), m - 1u);
 
   // Row exponent: binary16 exponent field of the largest block scale of the row.
   {
@@ -111,11 +123,11 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
       rds = *reinterpret_cast<const uint4 *>(ds + 4ull * ((uint64_t)s_row * nblk_pad + 4u * (g)));     \
   } while (0)
 
-  float acc_out[2][2][16];
+  float acc_out[TN][TM][16];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TN; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < TM; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_out[a][b][r] = 0.0f;
 
@@ -132,14 +144,16 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
     *reinterpret_cast<uint4 *>(a_lds + (1 * 32 + (tid >> 3)) * LDS_STRIDE + a_col) = ra1;                \
     *reinterpret_cast<uint4 *>(a_lds + (2 * 32 + (tid >> 3)) * LDS_STRIDE + a_col) = ra2;                \
     *reinterpret_cast<uint4 *>(a_lds + (3 * 32 + (tid >> 3)) * LDS_STRIDE + a_col) = ra3;                \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                      \
-      const uint4 sv = make_uint4(unpack_signed(rw.x, j), unpack_signed(rw.y, j),                        \
-                                  unpack_signed(rw.z, j), unpack_signed(rw.w, j));                       \
-      *reinterpret_cast<uint4 *>(w_lds + (tid >> 1) * LDS_STRIDE + 32 * j + 16 * w_half) = sv;           \
+    if (w_stager) {                                                                                      \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                    \
+        const uint4 sv = make_uint4(unpack_signed(rw.x, j), unpack_signed(rw.y, j),                      \
+                                    unpack_signed(rw.z, j), unpack_signed(rw.w, j));                     \
+        *reinterpret_cast<uint4 *>(w_lds + (tid >> 1) * LDS_STRIDE + 32 * j + 16 * w_half) = sv;         \
+      }                                                                                                  \
     }                                                                                                    \
     if (tid < BN) {                                                                                      \
       dw_lds[tid] = f16_bits_to_f32(rs16);                                                               \
-    } else {                                                                                             \
+    } else if (s_stager) {                                                                               \
       const int e = rowexp[tid - BN];                                                                    \
       int4 mu;                                                                                           \
       mu.x = (int)rintf(ldexpf(f16_bits_to_f32(rds.x & 0xFFFFu), 30 - e));                               \
@@ -173,11 +187,11 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
 
     // Operands of the group: both n-subtiles (weights, A) and both m-subtiles
     // (activations, B) for the four blocks, and the activation multipliers.
-    v4i A[2][4], B[2][4];
-    int mu[2][4];
+    v4i A[TN][4], B[TM][4];
+    int mu[TM][4];
 #pragma unroll
-    for (int sm = 0; sm < 2; ++sm) {
-      const uint32_t ml = wm * 64 + sm * 32 + l32;
+    for (int sm = 0; sm < TM; ++sm) {
+      const uint32_t ml = wm * (32 * TM) + sm * 32 + l32;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         B[sm][b] = *reinterpret_cast<const v4i *>(a_lds + ml * LDS_STRIDE + 32 * b + 16 * hi);
@@ -185,14 +199,18 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
       mu[sm][0] = t.x; mu[sm][1] = t.y; mu[sm][2] = t.z; mu[sm][3] = t.w;
     }
 #pragma unroll
-    for (int sn = 0; sn < 2; ++sn) {
-      const uint32_t nl = wn * 64 + sn * 32 + l32;
+    for (int sn = 0; sn < TN; ++sn) {
+      const uint32_t nl = wn * (32 * TN) + sn * 32 + l32;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         A[sn][b] = *reinterpret_cast<const v4i *>(w_lds + nl * LDS_STRIDE + 32 * b + 16 * hi);
     }
 
-    // 16 steps (sn, sm, b), software-pipelined by one: the MFMA of step i + 1
+    // The wave computing a group takes issue priority over the wave of the
+    // other workgroup on its SIMD (which is staging or waiting): measured 5%
+    // faster at m = 512 and the same at m = 2048.
+    __builtin_amdgcn_s_setprio(1);
+    // kSteps steps (sn, sm, b), software-pipelined by one: the MFMA of step i + 1
     // is issued before the epilogue of step i, so the matrix core runs while
     // the VALU folds the previous block; two result registers alternate.  A
     // scheduling barrier after each step keeps the compiler from clustering
@@ -201,9 +219,9 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
     int acc[16];
     float dwv[16];
 #pragma unroll
-    for (int i = 0; i <= 16; ++i) {
-      if (i < 16) {
-        const int sn = i >> 3, sm = (i >> 2) & 1, b = i & 3;
+    for (int i = 0; i <= kSteps; ++i) {
+      if (i < kSteps) {
+        const int sn = i / (4 * TM), sm = (i / 4) % TM, b = i & 3;
         D[i & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[sn][b], B[sm][b], zero16, 0, 0, 0);
         // issue the MFMA ahead of the previous step's epilogue: left to itself
         // the scheduler can sink it below, and the next step then waits for
@@ -212,23 +230,23 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
       }
       if (i > 0) {
         const int p = i - 1;
-        const int sn = p >> 3, sm = (p >> 2) & 1, b = p & 3;
+        const int sn = p / (4 * TM), sm = (p / 4) % TM, b = p & 3;
         const v16i &Dp = D[p & 1];
         if constexpr (kDump) {
-          const uint32_t mm = m_base + wm * 64 + sm * 32 + l32;
+          const uint32_t mm = m_base + wm * (32 * TM) + sm * 32 + l32;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const uint32_t nn = n_base + wn * 64 + sn * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const uint32_t nn = n_base + wn * (32 * TN) + sn * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
             if (mm >= m0 && mm < m0 + mt && nn >= n0 && nn < n0 + nt)
               dots[((uint64_t)(mm - m0) * nt + (nn - n0)) * (k / 32u) + 4u * g + b] = Dp[r];
           }
         } else {
-          if ((p & 7) == 0) {
+          if (p % (4 * TM) == 0) {
             // weight scales of n-subtile sn: loaded at its first step, after the
             // last flush of the previous n-subtile, three steps before first use
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float4 t = *reinterpret_cast<const float4 *>(dw_lds + wn * 64 + sn * 32 + 8 * q + 4 * hi);
+              const float4 t = *reinterpret_cast<const float4 *>(dw_lds + wn * (32 * TN) + sn * 32 + 8 * q + 4 * hi);
               dwv[4 * q + 0] = t.x; dwv[4 * q + 1] = t.y; dwv[4 * q + 2] = t.z; dwv[4 * q + 3] = t.w;
             }
           }
@@ -243,6 +261,7 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 #undef BQMM_FETCH
 #undef BQMM_STAGE
@@ -250,16 +269,16 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
   if constexpr (!kDump) {
     const bool full = (m_base + BM <= m) && (n_base + BN <= n) && (ldc % 4u) == 0u;
 #pragma unroll
-    for (int sm = 0; sm < 2; ++sm) {
-      const uint32_t mloc = wm * 64 + sm * 32 + l32;
+    for (int sm = 0; sm < TM; ++sm) {
+      const uint32_t mloc = wm * (32 * TM) + sm * 32 + l32;
       const uint32_t mm = m_base + mloc;
       const float scale = ldexpf(1.0f, rowexp[mloc] - 30);
       uint16_t *orow = out + (uint64_t)min(mm, m - 1u) * ldc;
 #pragma unroll
-      for (int sn = 0; sn < 2; ++sn)
+      for (int sn = 0; sn < TN; ++sn)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t nn = n_base + wn * 64 + sn * 32 + 8 * q + 4 * hi;
+          const uint32_t nn = n_base + wn * (32 * TN) + sn * 32 + 8 * q + 4 * hi;
           const float *v = &acc_out[sn][sm][4 * q];
           if (full) {
             *reinterpret_cast<uint2 *>(orow + nn) =
@@ -279,29 +298,53 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
   }
 }
 
+template <int TN, int TM, int WN>
+hipError_t launch_mmq_layout(const void *act_q8, const void *w, void *out, uint32_t m, uint32_t n, uint32_t k,
+                             uint32_t ldc, hipStream_t s) {
+  constexpr int BN = 32 * TN * WN;
+  constexpr int lds = 2 * stage_bytes(BN);
+  // Two stages exceed the 64 KB default dynamic-LDS limit; gfx950 allows 160 KB.
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(q2_0_mmq_kernel<false, TN, TM, WN>), lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);
+  hipLaunchKernelGGL((q2_0_mmq_kernel<false, TN, TM, WN>), grid, dim3(kThreads), lds, s,
+                     static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
+                     static_cast<uint16_t *>(out), nullptr, m, n, k, 0u, 0u, 0u, 0u, 0u, 0u, ldc);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+// The tile is chosen by how many rounds of resident workgroups (two per CU)
+// the grid takes: a 96 x 128 tile holds 3/4 of a 128 x 128 tile's work, so
+// it wins where it needs fewer than 4/3 as many rounds.  For m = 512,
+// n = 12288 on 256 CUs: 384 large tiles leave a quarter of the 512 slots
+// empty (one round), 512 small tiles fill them (one round of 3/4 the time).
 hipError_t launch_q2_0_mmq(const void *act_q8, const void *w, void *out, int32_t *dots,
                            uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m,
                            uint32_t n, uint32_t k, uint32_t ldc, hipStream_t s) {
-  // Two stages exceed the 64 KB default dynamic-LDS limit; gfx950 allows 160 KB.
-  hipError_t attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(q2_0_mmq_kernel<false>), 2 * kStageBytes);
-  if (attr_err == hipSuccess)
-    attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(q2_0_mmq_kernel<true>), 2 * kStageBytes);
-  if (attr_err != hipSuccess) return attr_err;
   if (dots == nullptr) {
-    const dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);
-    hipLaunchKernelGGL(q2_0_mmq_kernel<false>, grid, dim3(kThreads), 2 * kStageBytes, s,
-                       static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
-                       static_cast<uint16_t *>(out), nullptr, m, n, k, 0u, 0u, 0u, 0u, 0u, 0u, ldc);
-  } else {
-    const uint32_t tn0 = n0 / BN, tn1 = (n0 + nt - 1) / BN;
-    const uint32_t tm0 = m0 / BM, tm1 = (m0 + mt - 1) / BM;
-    const dim3 grid(tn1 - tn0 + 1, tm1 - tm0 + 1);
-    hipLaunchKernelGGL(q2_0_mmq_kernel<true>, grid, dim3(kThreads), 2 * kStageBytes, s,
-                       static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
-                       nullptr, dots, m, n, k, m0, mt, n0, nt, tn0, tm0, n);
+    int cus = 0;
+    const hipError_t e = device_cu_count(&cus);
+    if (e != hipSuccess) return e;
+    const uint64_t slots = 2ull * (uint64_t)(cus > 0 ? cus : 1);
+    const uint64_t tiles_m = (m + BM - 1) / BM;
+    const uint64_t rounds128 = ((n + 127ull) / 128ull * tiles_m + slots - 1) / slots;
+    const uint64_t rounds96 = ((n + 95ull) / 96ull * tiles_m + slots - 1) / slots;
+    if (3 * rounds96 < 4 * rounds128) return launch_mmq_layout<3, 1, 1>(act_q8, w, out, m, n, k, ldc, s);
+    return launch_mmq_layout<2, 2, 2>(act_q8, w, out, m, n, k, ldc, s);
   }
+  // Block dots of a window: the 128 x 128 layout.
+  constexpr int BN = 128;
+  constexpr int lds = 2 * stage_bytes(BN);
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(q2_0_mmq_kernel<true, 2, 2, 2>), lds);
+  if (e != hipSuccess) return e;
+  const uint32_t tn0 = n0 / BN, tn1 = (n0 + nt - 1) / BN;
+  const uint32_t tm0 = m0 / BM, tm1 = (m0 + mt - 1) / BM;
+  const dim3 grid(tn1 - tn0 + 1, tm1 - tm0 + 1);
+  hipLaunchKernelGGL((q2_0_mmq_kernel<true, 2, 2, 2>), grid, dim3(kThreads), lds, s,
+                     static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w), nullptr, dots, m, n,
+                     k, m0, mt, n0, nt, tn0, tm0, n);
   return hipGetLastError();
 }
 

@@ -108,6 +108,20 @@ def test_prefill_qkvz_sampled(gpu, m):
         assert np.array_equal(D, Dref)
 
 
+def test_large_grid_ragged(gpu):
+    # a grid large enough for the 128 x 128 tile (the small shapes above take
+    # 96 x 128 tiles), ragged in m and n, on sampled rows incl. the last tile
+    m, n, k = 1030, 5500, 256
+    g = inputs.rng(16)
+    w = inputs.q2_0_weight(g, n, k)
+    act = inputs.activations(g, m, k, outliers=True)
+    q8, q8d = _q8_dev(gpu, act, m, k)
+    y = _mmq(gpu, q8d, dev_u8(w, gpu), m, n, k)
+    rows = np.array([0, 127, 128, 700, 1023, 1024, 1029])
+    R = oracle.q2_0_mmq(_rows_sel(q8, m, k, rows), w, len(rows), n, k)
+    assert rounded_row_ok(y[rows], R)
+
+
 def _w_rows(w, n, k, r0, rt):
     """Q2_0 bytes of weight rows [r0, r0+rt) (layout-level copy, group 128)."""
     codes = w[: n * k // 4].reshape(n, k // 4)[r0:r0 + rt]
@@ -123,7 +137,9 @@ def _rows_sel(q8, m, k, rows):
 
 
 def test_batch_invariance(gpu):
-    # rows shared by the m = 512 and m = 2048 runs give identical outputs
+    # rows shared by the m = 512 and m = 2048 runs give identical outputs (the
+    # two runs use different tile shapes, 96 x 128 and 128 x 128 on 256 CUs:
+    # each output is folded in the same order by both)
     d = inputs.prefill_qkvz()
     n, k = d["n"], d["k"]
     wd = dev_u8(d["w"], gpu)

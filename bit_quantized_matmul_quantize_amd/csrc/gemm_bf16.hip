@@ -5,7 +5,9 @@
 //  dense_gemm_bf16_pipelined runs on the original bf16 input.]
 //
 // bf16 matrix cores (v_mfma_f32_32x32x16_bf16), fp32 accumulation, bf16 out.
-// Tile 128 (n) x 128 (m), 4 waves of 64 x 64, k staged KS = 64 at a time
+// Tile BN (n) x 128 (m): 128 x 128 with 4 waves of 64 x 64, or 96 x 128 with
+// 4 waves of 96 x 32 where that fills the chip in fewer rounds of
+// workgroups (the same choice as the MMQ's).  k is staged KS = 64 at a time
 // through two LDS stages: while stage s is multiplied, the registers holding
 // the global loads of step s + 1 are written into the other stage and the
 // loads of step s + 2 are already in flight, so one barrier per step and no
@@ -20,19 +22,27 @@ namespace {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int BN = 128, BM = 128, KS = 64;
+constexpr int BM = 128, KS = 64;
 constexpr int LDS_STRIDE = KS * 2 + 16;  // bytes per staged row; the pad spreads banks
 constexpr int kThreads = 256;
-constexpr int kTileBytes = BM * LDS_STRIDE;      // one operand tile (128 rows)
-constexpr int kStageBytes = 2 * kTileBytes;      // activation tile + weight tile
-constexpr int kLoads = BM * KS * 2 / 16 / kThreads;  // 16-byte loads per thread per operand (4)
+constexpr int kTileBytes = BM * LDS_STRIDE;      // the activation tile (128 rows)
+constexpr int kLoads = BM * KS * 2 / 16 / kThreads;  // 16-byte loads per thread per 128 rows (4)
+// one LDS stage: activation tile + weight tile of bn rows
+__host__ __device__ constexpr int stage_bytes(int bn) { return kTileBytes + bn * LDS_STRIDE; }
 
+// TN x TM subtiles of 32 x 32 per wave, WN waves along n (4 / WN along m).
+template <int TN, int TM, int WN>
 __global__ __launch_bounds__(kThreads, 2) void dense_gemm_bf16_kernel(
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ w, uint16_t *__restrict__ out,
     uint32_t m, uint32_t n, uint32_t k) {
+  constexpr int WM = 4 / WN;
+  constexpr int BN = 32 * TN * WN;
+  static_assert(WN * WM == 4 && 32 * TM * WM == BM, "four waves cover 128 activation rows");
+  static_assert(BN == 128 || BN == 96, "three or four 32-row weight loads per thread");
+  constexpr int kStageBytes = stage_bytes(BN);
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-  const uint32_t wn = wave & 1u, wm = wave >> 1;
+  const uint32_t wn = wave % WN, wm = wave / WN;
   // m tiles run consecutively (grid x), so the workgroups that share a weight
   // tile are co-resident and read it from L2 rather than from memory
   const uint32_t n_base = blockIdx.y * BN, m_base = blockIdx.x * BM;
@@ -66,7 +76,7 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gemm_bf16_kernel(
     rw0 = *reinterpret_cast<const uint4 *>(wp + wst[0] + o_);                         \
     rw1 = *reinterpret_cast<const uint4 *>(wp + wst[1] + o_);                         \
     rw2 = *reinterpret_cast<const uint4 *>(wp + wst[2] + o_);                         \
-    rw3 = *reinterpret_cast<const uint4 *>(wp + wst[3] + o_);                         \
+    if constexpr (BN == 128) rw3 = *reinterpret_cast<const uint4 *>(wp + wst[3] + o_); \
   } while (0)
 #define BQMM_STORE(st)                                                                \
   do {                                                                                \
@@ -78,14 +88,14 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gemm_bf16_kernel(
     *reinterpret_cast<uint4 *>(w_l) = rw0;                                            \
     *reinterpret_cast<uint4 *>(w_l + kRowStep) = rw1;                                 \
     *reinterpret_cast<uint4 *>(w_l + 2 * kRowStep) = rw2;                             \
-    *reinterpret_cast<uint4 *>(w_l + 3 * kRowStep) = rw3;                             \
+    if constexpr (BN == 128) *reinterpret_cast<uint4 *>(w_l + 3 * kRowStep) = rw3;    \
   } while (0)
 
-  v16f acc[2][2];
+  v16f acc[TN][TM];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TN; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TM; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -101,16 +111,17 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gemm_bf16_kernel(
     const uint8_t *a_l = lds + (s & 1u) * kStageBytes, *w_l = a_l + kTileBytes;
 #pragma unroll
     for (int kk = 0; kk < KS / 16; ++kk) {
-      v8bf A[2], B[2];
+      v8bf A[TN], B[TM];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        A[t] = *reinterpret_cast<const v8bf *>(w_l + (wn * 64 + t * 32 + (lane & 31)) * LDS_STRIDE + 32 * kk + 16 * (lane >> 5));
-        B[t] = *reinterpret_cast<const v8bf *>(a_l + (wm * 64 + t * 32 + (lane & 31)) * LDS_STRIDE + 32 * kk + 16 * (lane >> 5));
-      }
+      for (int t = 0; t < TN; ++t)
+        A[t] = *reinterpret_cast<const v8bf *>(w_l + (wn * (32 * TN) + t * 32 + (lane & 31)) * LDS_STRIDE + 32 * kk + 16 * (lane >> 5));
 #pragma unroll
-      for (int sn = 0; sn < 2; ++sn)
+      for (int t = 0; t < TM; ++t)
+        B[t] = *reinterpret_cast<const v8bf *>(a_l + (wm * (32 * TM) + t * 32 + (lane & 31)) * LDS_STRIDE + 32 * kk + 16 * (lane >> 5));
 #pragma unroll
-        for (int sm = 0; sm < 2; ++sm)
+      for (int sn = 0; sn < TN; ++sn)
+#pragma unroll
+        for (int sm = 0; sm < TM; ++sm)
           acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[sn], B[sm], acc[sn][sm], 0, 0, 0);
     }
   }
@@ -119,15 +130,15 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gemm_bf16_kernel(
 
   const bool vec = (n % 4u) == 0u;
 #pragma unroll
-  for (int sm = 0; sm < 2; ++sm) {
-    const uint32_t mm = m_base + wm * 64 + sm * 32 + (lane & 31);
+  for (int sm = 0; sm < TM; ++sm) {
+    const uint32_t mm = m_base + wm * (32 * TM) + sm * 32 + (lane & 31);
     if (mm >= m) continue;
     uint16_t *orow = out + (uint64_t)mm * n;
 #pragma unroll
-    for (int sn = 0; sn < 2; ++sn)
+    for (int sn = 0; sn < TN; ++sn)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t nn = n_base + wn * 64 + sn * 32 + 8 * q + 4 * (lane >> 5);
+        const uint32_t nn = n_base + wn * (32 * TN) + sn * 32 + 8 * q + 4 * (lane >> 5);
         const v16f &v = acc[sn][sm];
         if (vec && nn + 4 <= n) {
           *reinterpret_cast<uint2 *>(orow + nn) =
@@ -141,19 +152,36 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gemm_bf16_kernel(
   }
 }
 
+template <int TN, int TM, int WN>
+hipError_t launch_dense_layout(const void *a, const void *w, void *out, uint32_t m, uint32_t n, uint32_t k,
+                               hipStream_t s) {
+  constexpr int BN = 32 * TN * WN;
+  constexpr int lds = 2 * stage_bytes(BN);
+  // two stages (64.5 KB, 73.7 KB) exceed the 64 KB default dynamic-LDS limit
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(dense_gemm_bf16_kernel<TN, TM, WN>), lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid((m + BM - 1) / BM, (n + BN - 1) / BN);
+  hipLaunchKernelGGL((dense_gemm_bf16_kernel<TN, TM, WN>), grid, dim3(kThreads), lds, s,
+                     static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(w),
+                     static_cast<uint16_t *>(out), m, n, k);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_dense_gemm_bf16(const void *a, const void *w, void *out, uint32_t m, uint32_t n,
                                   uint32_t k, hipStream_t s) {
-  // two stages (73.7 KB) exceed the 64 KB default dynamic-LDS limit
-  const hipError_t attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(dense_gemm_bf16_kernel),
-                                                 2 * kStageBytes);
-  if (attr_err != hipSuccess) return attr_err;
-  const dim3 grid((m + BM - 1) / BM, (n + BN - 1) / BN);
-  hipLaunchKernelGGL(dense_gemm_bf16_kernel, grid, dim3(kThreads), 2 * kStageBytes, s,
-                     static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(w),
-                     static_cast<uint16_t *>(out), m, n, k);
-  return hipGetLastError();
+  int cus = 0;
+  const hipError_t e = device_cu_count(&cus);
+  if (e != hipSuccess) return e;
+  // Rounds of resident workgroups (two per CU); 96 x 128 tiles hold 3/4 of
+  // the work of 128 x 128 tiles.
+  const uint64_t slots = 2ull * (uint64_t)(cus > 0 ? cus : 1);
+  const uint64_t tiles_m = (m + BM - 1) / BM;
+  const uint64_t rounds128 = ((n + 127ull) / 128ull * tiles_m + slots - 1) / slots;
+  const uint64_t rounds96 = ((n + 95ull) / 96ull * tiles_m + slots - 1) / slots;
+  if (3 * rounds96 < 4 * rounds128) return launch_dense_layout<3, 1, 1>(a, w, out, m, n, k, s);
+  return launch_dense_layout<2, 2, 2>(a, w, out, m, n, k, s);
 }
 
 }  // namespace bqmm

@@ -24,16 +24,35 @@ def test_dequant_bit_exact(gpu, n, k, group, seed):
     assert np.array_equal(host_bits(out), oracle.dequant_q2_0_to_bf16(w, n, k, group))
 
 
-@pytest.mark.parametrize("m,n,k,seed", [(4, 256, 512, 41), (130, 200, 192, 42), (1, 1, 64, 43)])
+# small grids take 96 x 128 tiles on 256 CUs; (1030, 5500) is large enough
+# for 128 x 128 tiles, ragged in m and n
+@pytest.mark.parametrize("m,n,k,seed", [(4, 256, 512, 41), (130, 200, 192, 42), (1, 1, 64, 43),
+                                        (1030, 5500, 256, 44)])
 def test_dense_gemm_bf16(gpu, m, n, k, seed):
     g = inputs.rng(seed)
     a = inputs.activations(g, m, k)
     wb = inputs.activations(g, n, k)
     out = empty_bf16((m, n), gpu)
     bq.dense_gemm_bf16(dev_bf16(a, gpu), dev_bf16(wb, gpu), out, m, n, k)
-    R = oracle.dense_gemm_bf16(a, wb, m, n, k)
+    # large m: sampled rows, including both sides of tile boundaries and the last row
+    rows = np.arange(m) if m <= 256 else np.array([0, 127, 128, 700, 1023, 1024, m - 1])
+    R = oracle.dense_gemm_bf16(np.ascontiguousarray(a[rows]), wb, len(rows), n, k)
     # fp32 accumulation and one bf16 rounding of each output
-    assert rounded_row_ok(host_f64(out), R)
+    assert rounded_row_ok(host_f64(out)[rows], R)
+
+
+def test_dense_gemm_layouts_agree(gpu):
+    # the first 130 rows of an m = 1030 product (128 x 128 tiles) equal an
+    # m = 130 product (96 x 128 tiles) bit for bit: each output is summed over
+    # k in the same order by both layouts
+    n, k = 5500, 256
+    g = inputs.rng(45)
+    a = inputs.activations(g, 1030, k)
+    wd = dev_bf16(inputs.activations(g, n, k), gpu)
+    big, small = empty_bf16((1030, n), gpu), empty_bf16((130, n), gpu)
+    bq.dense_gemm_bf16(dev_bf16(a, gpu), wd, big, 1030, n, k)
+    bq.dense_gemm_bf16(dev_bf16(np.ascontiguousarray(a[:130]), gpu), wd, small, 130, n, k)
+    assert np.array_equal(host_bits(small), host_bits(big)[:130])
 
 
 def _prefill(gpu, act, w, m, n, k, group, use_mmq):

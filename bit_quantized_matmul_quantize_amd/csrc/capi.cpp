@@ -50,6 +50,10 @@ uint64_t strided_bytes(uint32_t m, uint32_t n, uint32_t ldc) { return 2u * ((uin
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
 constexpr uint32_t kMaxGridY = 65535u;
+// Bounds that keep every size and index computation inside its type: k values
+// per row (padded to 256 in 32 bits), and output rows n.
+constexpr uint32_t kMaxK = 1u << 30;
+constexpr uint32_t kMaxRows = 1u << 31;
 
 #define REQUIRE(cond, status, ...) \
   do {                             \
@@ -96,6 +100,7 @@ uint64_t q4k_weight_bytes(uint32_t n, uint32_t k) {
 int quantize_act_q8_1(const void *act_bf16, void *out_q8, uint32_t m, uint32_t k, void *stream) {
   REQUIRE(act_bf16 && out_q8, BQ_EINVAL, "quantize_act_q8_1: null pointer");
   REQUIRE(m >= 1 && k >= 1, BQ_EINVAL, "quantize_act_q8_1: m=%u k=%u must be >= 1", m, k);
+  REQUIRE(k <= kMaxK, BQ_EINVAL, "quantize_act_q8_1: k=%u too large", k);
   REQUIRE(aligned16(act_bf16) && aligned16(out_q8), BQ_EALIGN, "quantize_act_q8_1: buffers must be 16-byte aligned");
   const uint64_t kpad = ((uint64_t)k + 255u) / 256u * 256u;
   const uint64_t blocks = (uint64_t)m * ((kpad + 2047u) / 2048u);
@@ -109,6 +114,7 @@ int silu_mul_quantize_q8_1(const void *gate_bf16, const void *up_bf16, void *out
                            uint32_t k, void *stream) {
   REQUIRE(gate_bf16 && up_bf16 && out_q8, BQ_EINVAL, "silu_mul_quantize_q8_1: null pointer");
   REQUIRE(m >= 1 && k >= 1, BQ_EINVAL, "silu_mul_quantize_q8_1: m=%u k=%u must be >= 1", m, k);
+  REQUIRE(k <= kMaxK, BQ_EINVAL, "silu_mul_quantize_q8_1: k=%u too large", k);
   REQUIRE(aligned16(gate_bf16) && aligned16(up_bf16) && aligned16(out_q8), BQ_EALIGN,
           "silu_mul_quantize_q8_1: buffers must be 16-byte aligned");
   const uint64_t kpad = ((uint64_t)k + 255u) / 256u * 256u;
@@ -128,7 +134,8 @@ static int check_mmq(const char *name, const void *act_q8, const void *w, const 
   REQUIRE(m >= 1 && n >= 1 && k >= 1, BQ_EINVAL, "%s: m=%u n=%u k=%u must be >= 1", name, m, n, k);
   REQUIRE(k % kmult == 0, BQ_EINVAL, "%s: k=%u must be a multiple of %u", name, k, kmult);
   REQUIRE(aligned16(act_q8) && aligned16(w) && aligned16(out), BQ_EALIGN, "%s: buffers must be 16-byte aligned", name);
-  REQUIRE((m + 127u) / 128u <= kMaxGridY, BQ_EINVAL, "%s: m=%u too large", name, m);
+  REQUIRE(k <= kMaxK && n <= kMaxRows, BQ_EINVAL, "%s: n=%u k=%u too large", name, n, k);
+  REQUIRE(((uint64_t)m + 127u) / 128u <= kMaxGridY, BQ_EINVAL, "%s: m=%u too large", name, m);
   if (out_bytes == ~0ull) return BQ_OK;  // the caller checks the ranges itself
   const uint64_t nout = out_bytes ? out_bytes : bf16_bytes(m, n);
   REQUIRE_DISJOINT(name, out, nout, act_q8, q8_bytes(m, k), "the q8_1 activations");
@@ -211,6 +218,7 @@ static int check_gemv(const char *name, const void *act, const void *w, const vo
   REQUIRE(act && w && out, BQ_EINVAL, "%s: null pointer", name);
   REQUIRE(n >= 1 && k >= 1, BQ_EINVAL, "%s: n=%u k=%u must be >= 1", name, n, k);
   REQUIRE(k % 128u == 0, BQ_EINVAL, "%s: k=%u must be a multiple of the group size 128", name, k);
+  REQUIRE(k <= kMaxK && n <= kMaxRows, BQ_EINVAL, "%s: n=%u k=%u too large", name, n, k);
   REQUIRE(m >= 1, BQ_EINVAL, "%s: m must be >= 1", name);
   REQUIRE(m <= 8, BQ_EUNSUPPORTED, "%s: m=%u > 8 (use the MMQ path)", name, m);
   REQUIRE(aligned16(act) && aligned16(w) && aligned16(out), BQ_EALIGN, "%s: buffers must be 16-byte aligned", name);
@@ -253,6 +261,7 @@ int q4k_gemv_vec(const void *act_bf16, const void *w_q4k, void *out_bf16, uint32
   REQUIRE(n >= 1 && k >= 1, BQ_EINVAL, "q4k_gemv_vec: n=%u k=%u must be >= 1", n, k);
   REQUIRE(k % 256u == 0, BQ_EINVAL, "q4k_gemv_vec: k=%u must be a multiple of 256", k);
   REQUIRE(k <= 65536u, BQ_EUNSUPPORTED, "q4k_gemv_vec: k=%u > 65536", k);
+  REQUIRE(n <= kMaxRows, BQ_EINVAL, "q4k_gemv_vec: n=%u too large", n);
   REQUIRE(aligned16(act_bf16) && aligned16(w_q4k) && aligned16(out_bf16), BQ_EALIGN,
           "q4k_gemv_vec: buffers must be 16-byte aligned");
   REQUIRE_DISJOINT("q4k_gemv_vec", out_bf16, bf16_bytes(1, n), act_bf16, bf16_bytes(1, k), "the activations");
@@ -264,6 +273,10 @@ int quantize_weight_q4k(const void *w_bf16, void *out_q4k, uint32_t n, uint32_t 
   REQUIRE(w_bf16 && out_q4k, BQ_EINVAL, "quantize_weight_q4k: null pointer");
   REQUIRE(n >= 1 && k >= 1, BQ_EINVAL, "quantize_weight_q4k: n=%u k=%u must be >= 1", n, k);
   REQUIRE(k % 256u == 0, BQ_EINVAL, "quantize_weight_q4k: k=%u must be a multiple of 256", k);
+  REQUIRE(k <= kMaxK && n <= kMaxRows, BQ_EINVAL, "quantize_weight_q4k: n=%u k=%u too large", n, k);
+  // eight lanes per super-block, 256 lanes per workgroup, one grid dimension
+  REQUIRE(((uint64_t)n * (k / 256u) * 8u + 255u) / 256u < (1ull << 31), BQ_EINVAL,
+          "quantize_weight_q4k: n=%u k=%u too large", n, k);
   REQUIRE(aligned16(w_bf16) && aligned16(out_q4k), BQ_EALIGN,
           "quantize_weight_q4k: buffers must be 16-byte aligned");
   REQUIRE_DISJOINT("quantize_weight_q4k", out_q4k, q4k_bytes(n, k), w_bf16, bf16_bytes(n, k), "the input");
@@ -277,6 +290,7 @@ static int check_dequant(const void *w, const void *out, uint32_t n, uint32_t k,
   REQUIRE(group >= 32u && group % 32u == 0, BQ_EUNSUPPORTED,
           "dequant_q2_0_to_bf16: group=%u must be a positive multiple of 32", group);
   REQUIRE(k % group == 0, BQ_EINVAL, "dequant_q2_0_to_bf16: k=%u not a multiple of group=%u", k, group);
+  REQUIRE(k <= kMaxK && n <= kMaxRows, BQ_EINVAL, "dequant_q2_0_to_bf16: n=%u k=%u too large", n, k);
   REQUIRE(aligned16(w) && aligned16(out), BQ_EALIGN, "dequant_q2_0_to_bf16: buffers must be 16-byte aligned");
   REQUIRE_DISJOINT("dequant_q2_0_to_bf16", out, bf16_bytes(n, k), w,
                    (uint64_t)n * k / 4u + 2u * (uint64_t)n * (k / group), "the weight");
@@ -296,7 +310,8 @@ static int check_dense(const void *a, const void *w, const void *out, uint32_t m
   REQUIRE(m >= 1 && n >= 1 && k >= 1, BQ_EINVAL, "dense_gemm_bf16: m=%u n=%u k=%u must be >= 1", m, n, k);
   REQUIRE(k % 64u == 0, BQ_EINVAL, "dense_gemm_bf16: k=%u must be a multiple of 64", k);
   REQUIRE(aligned16(a) && aligned16(w) && aligned16(out), BQ_EALIGN, "dense_gemm_bf16: buffers must be 16-byte aligned");
-  REQUIRE((n + 127u) / 128u <= kMaxGridY, BQ_EINVAL, "dense_gemm_bf16: n=%u too large", n);
+  REQUIRE(k <= kMaxK && m <= kMaxRows, BQ_EINVAL, "dense_gemm_bf16: m=%u k=%u too large", m, k);
+  REQUIRE(((uint64_t)n + 127u) / 128u <= kMaxGridY, BQ_EINVAL, "dense_gemm_bf16: n=%u too large", n);
   REQUIRE_DISJOINT("dense_gemm_bf16", out, bf16_bytes(m, n), a, bf16_bytes(m, k), "the activations");
   REQUIRE_DISJOINT("dense_gemm_bf16", out, bf16_bytes(m, n), w, bf16_bytes(n, k), "the weight");
   return BQ_OK;

@@ -160,7 +160,7 @@ hipError_t launch_dense_layout(const void *a, const void *w, void *out, uint32_t
   // two stages (64.5 KB, 73.7 KB) exceed the 64 KB default dynamic-LDS limit
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(dense_gemm_bf16_kernel<TN, TM, WN>), lds);
   if (e != hipSuccess) return e;
-  const dim3 grid((m + BM - 1) / BM, (n + BN - 1) / BN);
+  const dim3 grid((uint32_t)(((uint64_t)m + BM - 1) / BM), (uint32_t)(((uint64_t)n + BN - 1) / BN));
   hipLaunchKernelGGL((dense_gemm_bf16_kernel<TN, TM, WN>), grid, dim3(kThreads), lds, s,
                      static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(w),
                      static_cast<uint16_t *>(out), m, n, k);
@@ -177,10 +177,12 @@ hipError_t launch_dense_gemm_bf16(const void *a, const void *w, void *out, uint3
   // Rounds of resident workgroups (two per CU); 96 x 128 tiles hold 3/4 of
   // the work of 128 x 128 tiles.
   const uint64_t slots = 2ull * (uint64_t)(cus > 0 ? cus : 1);
-  const uint64_t tiles_m = (m + BM - 1) / BM;
+  const uint64_t tiles_m = ((uint64_t)m + BM - 1) / BM;
+  const uint64_t tiles96 = (n + 95ull) / 96ull;
   const uint64_t rounds128 = ((n + 127ull) / 128ull * tiles_m + slots - 1) / slots;
-  const uint64_t rounds96 = ((n + 95ull) / 96ull * tiles_m + slots - 1) / slots;
-  if (3 * rounds96 < 4 * rounds128) return launch_dense_layout<3, 1, 1>(a, w, out, m, n, k, s);
+  const uint64_t rounds96 = (tiles96 * tiles_m + slots - 1) / slots;
+  // (n tiles are the second grid dimension, at most 65535)
+  if (3 * rounds96 < 4 * rounds128 && tiles96 <= 65535u) return launch_dense_layout<3, 1, 1>(a, w, out, m, n, k, s);
   return launch_dense_layout<2, 2, 2>(a, w, out, m, n, k, s);
 }
 

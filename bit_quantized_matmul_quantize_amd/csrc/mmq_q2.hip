@@ -306,7 +306,7 @@ hipError_t launch_mmq_layout(const void *act_q8, const void *w, void *out, uint3
   // Two stages exceed the 64 KB default dynamic-LDS limit; gfx950 allows 160 KB.
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(q2_0_mmq_kernel<false, TN, TM, WN>), lds);
   if (e != hipSuccess) return e;
-  const dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);
+  const dim3 grid((uint32_t)(((uint64_t)n + BN - 1) / BN), (uint32_t)(((uint64_t)m + BM - 1) / BM));
   hipLaunchKernelGGL((q2_0_mmq_kernel<false, TN, TM, WN>), grid, dim3(kThreads), lds, s,
                      static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
                      static_cast<uint16_t *>(out), nullptr, m, n, k, 0u, 0u, 0u, 0u, 0u, 0u, ldc);
@@ -328,7 +328,7 @@ hipError_t launch_q2_0_mmq(const void *act_q8, const void *w, void *out, int32_t
     const hipError_t e = device_cu_count(&cus);
     if (e != hipSuccess) return e;
     const uint64_t slots = 2ull * (uint64_t)(cus > 0 ? cus : 1);
-    const uint64_t tiles_m = (m + BM - 1) / BM;
+    const uint64_t tiles_m = ((uint64_t)m + BM - 1) / BM;
     const uint64_t rounds128 = ((n + 127ull) / 128ull * tiles_m + slots - 1) / slots;
     const uint64_t rounds96 = ((n + 95ull) / 96ull * tiles_m + slots - 1) / slots;
     if (3 * rounds96 < 4 * rounds128) return launch_mmq_layout<3, 1, 1>(act_q8, w, out, m, n, k, ldc, s);

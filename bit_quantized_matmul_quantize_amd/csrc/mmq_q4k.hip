@@ -272,7 +272,7 @@ hipError_t launch_q4k_mmq(const void *act_q8, const void *w, void *out, int32_t 
     attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(q4k_mmq_kernel<true>), 2 * kStageBytes);
   if (attr_err != hipSuccess) return attr_err;
   if (dots == nullptr) {
-    const dim3 grid((n + BN - 1) / BN, (m + BM - 1) / BM);
+    const dim3 grid((uint32_t)(((uint64_t)n + BN - 1) / BN), (uint32_t)(((uint64_t)m + BM - 1) / BM));
     hipLaunchKernelGGL(q4k_mmq_kernel<false>, grid, dim3(kThreads), 2 * kStageBytes, s,
                        static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
                        static_cast<uint16_t *>(out), nullptr, m, n, k, 0u, 0u, 0u, 0u, 0u, 0u, ldc);

@@ -48,11 +48,17 @@
  * call checks the byte ranges its shapes give and returns BQ_EINVAL when an
  * output range shares a byte with an input range.
  *
+ * Size limits (BQ_EINVAL beyond them): k <= 2^30 and output rows n <= 2^31
+ * for every call; the MMQs take m <= 65535*128 and the dense GEMM n <=
+ * 65535*128 (tile counts in the second grid dimension); the Q4_K weight
+ * quantizer takes n*k/256 super-blocks below 2^36 (one grid dimension).
+ *
  * Only a gfx950 code object is built; on other devices calls fail with
  * BQ_EHIP.  The library keeps no mutable state besides the per-thread error
- * message and a lock-protected record of the devices on which a kernel's
- * dynamic-LDS limit has been raised; calls from different threads are
- * independent.
+ * message and two lock-protected per-device records: the kernels whose
+ * dynamic-LDS limit has been raised, and the compute-unit count (the MMQ and
+ * the dense GEMM choose their tile shape from it; results do not depend on
+ * the choice).  Calls from different threads are independent.
  */
 #ifndef BQMM_H
 #define BQMM_H

@@ -106,6 +106,19 @@ def _err(bq):
     (lambda l: l.quantize_weight_q4k(A, None, 4, 512, None), -1, "null"),
     (lambda l: l.quantize_weight_q4k(A, MIS, 4, 512, None), -3, "aligned"),
     (lambda l: l.quantize_weight_q4k(A, B, 0, 512, None), -1, "n=0"),
+    # sizes whose tile counts or padded row lengths would not fit 32 bits
+    (lambda l: l.q2_0_mmq_gemm(A, B, C, 0xFFFFFFFF, 256, 512, None), -1, "too large"),
+    (lambda l: l.q2_0_mmq_gemm(A, B, C, 4, 256, (1 << 30) + 128, None), -1, "too large"),
+    (lambda l: l.q4k_mmq_gemm(A, B, C, 4, (1 << 31) + 1, 512, None), -1, "too large"),
+    (lambda l: l.quantize_act_q8_1(A, B, 4, (1 << 30) + 1, None), -1, "too large"),
+    (lambda l: l.silu_mul_quantize_q8_1(A, B, C, 4, 0xFFFFFFFF, None), -1, "too large"),
+    (lambda l: l.q2_0_gemv_vec(A, B, C, 256, (1 << 30) + 128, None), -1, "too large"),
+    (lambda l: l.q2_0_gemv_vec(A, B, C, (1 << 31) + 1, 512, None), -1, "too large"),
+    (lambda l: l.q4k_gemv_vec(A, B, C, (1 << 31) + 1, 512, None), -1, "too large"),
+    (lambda l: l.quantize_weight_q4k(A, B, 1 << 30, 1 << 20, None), -1, "too large"),
+    (lambda l: l.dequant_q2_0_to_bf16(A, B, 4, (1 << 30) + 128, 128, None), -1, "too large"),
+    (lambda l: l.dense_gemm_bf16(A, B, C, 4, 0xFFFFFFFF, 64, None), -1, "too large"),
+    (lambda l: l.dense_gemm_bf16(A, B, C, (1 << 31) + 1, 4, 64, None), -1, "too large"),
     # outputs overlapping inputs (byte extents from the shapes)
     (lambda l: l.quantize_act_q8_1(A, P(0x10000 + 1024), 4, 512, None), -1, "overlaps the input"),
     (lambda l: l.silu_mul_quantize_q8_1(A, B, P(0x20000 + 16), 4, 512, None), -1, "overlaps up"),

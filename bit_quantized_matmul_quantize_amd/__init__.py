@@ -123,102 +123,178 @@ def q4k_weight_bytes(n: int, k: int) -> int:
 
 
 # ---- calls (same names as the C ABI) -----------------------------------------
+#
+# Each wrapper checks, before anything reaches the library: dtypes, that every
+# tensor holds at least the bytes its shape arguments address (the C ABI sees
+# plain pointers and cannot), and that all tensors are contiguous device
+# tensors on one device.
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need(t, nbytes: int, what: str):
+    if t is not None and _nbytes(t) < nbytes:
+        raise ValueError(f"{what}: {_nbytes(t)} bytes, the shape arguments address {nbytes}")
+    return t
+
+
+def _same_device(*tensors):
+    devs = {t.device for t in tensors if t is not None and t.is_cuda}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(str(d) for d in devs)}")
+
+
+def _ptrs(*tensors):
+    """Device pointers of the given contiguous tensors (None passes through), all on one device."""
+    _same_device(*tensors)
+    return [_ptr(t) for t in tensors]
+
+
+def _bf(m: int, k: int) -> int:
+    return 2 * m * k
+
 
 def quantize_act_q8_1(act, out_q8, m: int, k: int, stream=None):
-    _check(lib().quantize_act_q8_1(_ptr(_bf16(act, "act")), _ptr(_u8(out_q8, "out_q8")), m, k, _stream(stream)))
+    _need(_bf16(act, "act"), _bf(m, k), "act")
+    _need(_u8(out_q8, "out_q8"), q8_1_act_bytes(m, k), "out_q8")
+    _check(lib().quantize_act_q8_1(*_ptrs(act, out_q8), m, k, _stream(stream)))
 
 
 def silu_mul_quantize_q8_1(gate, up, out_q8, m: int, k: int, stream=None):
-    _check(lib().silu_mul_quantize_q8_1(_ptr(_bf16(gate, "gate")), _ptr(_bf16(up, "up")),
-                                        _ptr(_u8(out_q8, "out_q8")), m, k, _stream(stream)))
+    _need(_bf16(gate, "gate"), _bf(m, k), "gate")
+    _need(_bf16(up, "up"), _bf(m, k), "up")
+    _need(_u8(out_q8, "out_q8"), q8_1_act_bytes(m, k), "out_q8")
+    _check(lib().silu_mul_quantize_q8_1(*_ptrs(gate, up, out_q8), m, k, _stream(stream)))
 
 
 def q2_0_mmq_gemm(act_q8, w_q2, out, m: int, n: int, k: int, stream=None):
-    _check(lib().q2_0_mmq_gemm(_ptr(_u8(act_q8, "act_q8")), _ptr(_u8(w_q2, "w_q2")), _ptr(_bf16(out, "out")),
-                               m, n, k, _stream(stream)))
+    _need(_u8(act_q8, "act_q8"), q8_1_act_bytes(m, k), "act_q8")
+    _need(_u8(w_q2, "w_q2"), q2_0_weight_bytes(n, k), "w_q2")
+    _need(_bf16(out, "out"), _bf(m, n), "out")
+    _check(lib().q2_0_mmq_gemm(*_ptrs(act_q8, w_q2, out), m, n, k, _stream(stream)))
 
 
 def _ptr_rows(t, m: int, n: int, ldc: int, what):
     """A [m, n] bf16 view whose rows are ldc elements apart (a column range of a wider buffer)."""
     _bf16(t, what)
-    if not t.is_cuda:
-        raise ValueError("expected a device tensor")
     if tuple(t.shape) != (m, n) or (m > 1 and t.stride(0) != ldc) or (n > 1 and t.stride(1) != 1):
         raise ValueError(f"{what}: expected an [{m}, {n}] view with row stride {ldc}")
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
     return ctypes.c_void_p(t.data_ptr())
 
 
 def q2_0_mmq_gemm_ldc(act_q8, w_q2, out, m: int, n: int, k: int, ldc: int, stream=None):
-    _check(lib().q2_0_mmq_gemm_ldc(_ptr(_u8(act_q8, "act_q8")), _ptr(_u8(w_q2, "w_q2")),
-                                   _ptr_rows(out, m, n, ldc, "out"), m, n, k, ldc, _stream(stream)))
+    _need(_u8(act_q8, "act_q8"), q8_1_act_bytes(m, k), "act_q8")
+    _need(_u8(w_q2, "w_q2"), q2_0_weight_bytes(n, k), "w_q2")
+    out_p = _ptr_rows(out, m, n, ldc, "out")
+    _same_device(act_q8, w_q2, out)
+    a_p, w_p = _ptrs(act_q8, w_q2)
+    _check(lib().q2_0_mmq_gemm_ldc(a_p, w_p, out_p, m, n, k, ldc, _stream(stream)))
 
 
 def q4k_mmq_gemm_ldc(act_q8, w_q4k, out, m: int, n: int, k: int, ldc: int, stream=None):
-    _check(lib().q4k_mmq_gemm_ldc(_ptr(_u8(act_q8, "act_q8")), _ptr(_u8(w_q4k, "w_q4k")),
-                                  _ptr_rows(out, m, n, ldc, "out"), m, n, k, ldc, _stream(stream)))
+    _need(_u8(act_q8, "act_q8"), q8_1_act_bytes(m, k), "act_q8")
+    _need(_u8(w_q4k, "w_q4k"), q4k_weight_bytes(n, k), "w_q4k")
+    out_p = _ptr_rows(out, m, n, ldc, "out")
+    _same_device(act_q8, w_q4k, out)
+    a_p, w_p = _ptrs(act_q8, w_q4k)
+    _check(lib().q4k_mmq_gemm_ldc(a_p, w_p, out_p, m, n, k, ldc, _stream(stream)))
 
 
 def q2_0_gemv_vec(act, w_q2, out, n: int, k: int, stream=None):
-    _check(lib().q2_0_gemv_vec(_ptr(_bf16(act, "act")), _ptr(_u8(w_q2, "w_q2")), _ptr(_bf16(out, "out")),
-                               n, k, _stream(stream)))
+    _need(_bf16(act, "act"), _bf(1, k), "act")
+    _need(_u8(w_q2, "w_q2"), q2_0_weight_bytes(n, k), "w_q2")
+    _need(_bf16(out, "out"), _bf(1, n), "out")
+    _check(lib().q2_0_gemv_vec(*_ptrs(act, w_q2, out), n, k, _stream(stream)))
 
 
 def q2_0_gemv_vec_batchm(act, w_q2, out, m: int, n: int, k: int, stream=None):
-    _check(lib().q2_0_gemv_vec_batchm(_ptr(_bf16(act, "act")), _ptr(_u8(w_q2, "w_q2")),
-                                      _ptr(_bf16(out, "out")), m, n, k, _stream(stream)))
+    _need(_bf16(act, "act"), _bf(m, k), "act")
+    _need(_u8(w_q2, "w_q2"), q2_0_weight_bytes(n, k), "w_q2")
+    _need(_bf16(out, "out"), _bf(m, n), "out")
+    _check(lib().q2_0_gemv_vec_batchm(*_ptrs(act, w_q2, out), m, n, k, _stream(stream)))
 
 
 def q2_0_gemv_gate_up_silu(act, w_gate, w_up, out, m: int, n: int, k: int, stream=None):
-    _check(lib().q2_0_gemv_gate_up_silu(_ptr(_bf16(act, "act")), _ptr(_u8(w_gate, "w_gate")),
-                                        _ptr(_u8(w_up, "w_up")), _ptr(_bf16(out, "out")), m, n, k,
-                                        _stream(stream)))
+    _need(_bf16(act, "act"), _bf(m, k), "act")
+    _need(_u8(w_gate, "w_gate"), q2_0_weight_bytes(n, k), "w_gate")
+    _need(_u8(w_up, "w_up"), q2_0_weight_bytes(n, k), "w_up")
+    _need(_bf16(out, "out"), _bf(m, n), "out")
+    _check(lib().q2_0_gemv_gate_up_silu(*_ptrs(act, w_gate, w_up, out), m, n, k, _stream(stream)))
 
 
 def dequant_q2_0_to_bf16(w_q2, out, n: int, k: int, group: int = 128, stream=None):
-    _check(lib().dequant_q2_0_to_bf16(_ptr(_u8(w_q2, "w_q2")), _ptr(_bf16(out, "out")), n, k, group,
-                                      _stream(stream)))
+    _need(_u8(w_q2, "w_q2"), q2_0_weight_bytes(n, k, group), "w_q2")
+    _need(_bf16(out, "out"), _bf(n, k), "out")
+    _check(lib().dequant_q2_0_to_bf16(*_ptrs(w_q2, out), n, k, group, _stream(stream)))
 
 
 def dense_gemm_bf16(a, w, out, m: int, n: int, k: int, stream=None):
-    _check(lib().dense_gemm_bf16(_ptr(_bf16(a, "a")), _ptr(_bf16(w, "w")), _ptr(_bf16(out, "out")),
-                                 m, n, k, _stream(stream)))
+    _need(_bf16(a, "a"), _bf(m, k), "a")
+    _need(_bf16(w, "w"), _bf(n, k), "w")
+    _need(_bf16(out, "out"), _bf(m, n), "out")
+    _check(lib().dense_gemm_bf16(*_ptrs(a, w, out), m, n, k, _stream(stream)))
 
 
 def q2_0_prefill_gemm(act, w_q2, out, scratch, act_q8, m: int, n: int, k: int, group: int = 128,
                       use_mmq: bool = True, stream=None):
-    _check(lib().q2_0_prefill_gemm(_ptr(_bf16(act, "act")), _ptr(_u8(w_q2, "w_q2")), _ptr(_bf16(out, "out")),
-                                   _ptr(scratch), _ptr(act_q8), m, n, k, group, int(bool(use_mmq)),
-                                   _stream(stream)))
+    _need(_bf16(act, "act"), _bf(m, k), "act")
+    _need(_u8(w_q2, "w_q2"), q2_0_weight_bytes(n, k, group), "w_q2")
+    _need(_bf16(out, "out"), _bf(m, n), "out")
+    if use_mmq and group == 128:  # the MMQ branch writes act_q8, the dequant branch scratch
+        _need(act_q8, q8_1_act_bytes(m, k), "act_q8")
+    else:
+        _need(scratch, _bf(n, k), "scratch")
+    _check(lib().q2_0_prefill_gemm(*_ptrs(act, w_q2, out, scratch, act_q8), m, n, k, group,
+                                   int(bool(use_mmq)), _stream(stream)))
 
 
 def q4k_mmq_gemm(act_q8, w_q4k, out, m: int, n: int, k: int, stream=None):
-    _check(lib().q4k_mmq_gemm(_ptr(_u8(act_q8, "act_q8")), _ptr(_u8(w_q4k, "w_q4k")), _ptr(_bf16(out, "out")),
-                              m, n, k, _stream(stream)))
+    _need(_u8(act_q8, "act_q8"), q8_1_act_bytes(m, k), "act_q8")
+    _need(_u8(w_q4k, "w_q4k"), q4k_weight_bytes(n, k), "w_q4k")
+    _need(_bf16(out, "out"), _bf(m, n), "out")
+    _check(lib().q4k_mmq_gemm(*_ptrs(act_q8, w_q4k, out), m, n, k, _stream(stream)))
 
 
 def q4k_gemv_vec(act, w_q4k, out, n: int, k: int, stream=None):
-    _check(lib().q4k_gemv_vec(_ptr(_bf16(act, "act")), _ptr(_u8(w_q4k, "w_q4k")), _ptr(_bf16(out, "out")),
-                              n, k, _stream(stream)))
+    _need(_bf16(act, "act"), _bf(1, k), "act")
+    _need(_u8(w_q4k, "w_q4k"), q4k_weight_bytes(n, k), "w_q4k")
+    _need(_bf16(out, "out"), _bf(1, n), "out")
+    _check(lib().q4k_gemv_vec(*_ptrs(act, w_q4k, out), n, k, _stream(stream)))
 
 
 def quantize_weight_q4k(w, out_q4k, n: int, k: int, stream=None):
-    _check(lib().quantize_weight_q4k(_ptr(_bf16(w, "w")), _ptr(_u8(out_q4k, "out_q4k")), n, k,
-                                     _stream(stream)))
+    _need(_bf16(w, "w"), _bf(n, k), "w")
+    _need(_u8(out_q4k, "out_q4k"), q4k_weight_bytes(n, k), "out_q4k")
+    _check(lib().quantize_weight_q4k(*_ptrs(w, out_q4k), n, k, _stream(stream)))
 
 
 def silu_mul_bf16(gate, up, out, count: int | None = None, stream=None):
     count = gate.numel() if count is None else count
-    _check(lib().silu_mul_bf16(_ptr(_bf16(gate, "gate")), _ptr(_bf16(up, "up")), _ptr(_bf16(out, "out")),
-                               count, _stream(stream)))
+    for t, what in ((gate, "gate"), (up, "up"), (out, "out")):
+        _need(_bf16(t, what), 2 * count, what)
+    _check(lib().silu_mul_bf16(*_ptrs(gate, up, out), count, _stream(stream)))
+
+
+def _blockdots(fn, act_q8, w, w_bytes, out_i32, m0, mt, n0, nt, m, n, k, stream):
+    import torch
+    _need(_u8(act_q8, "act_q8"), q8_1_act_bytes(m, k), "act_q8")
+    _need(_u8(w, "w"), w_bytes, "w")
+    if out_i32.dtype != torch.int32:
+        raise TypeError(f"out_i32: expected int32, got {out_i32.dtype}")
+    _need(out_i32, 4 * mt * nt * (k // 32), "out_i32")
+    _check(fn(*_ptrs(act_q8, w, out_i32), m0, mt, n0, nt, m, n, k, _stream(stream)))
 
 
 def q2_0_mmq_blockdots(act_q8, w_q2, out_i32, m0: int, mt: int, n0: int, nt: int, m: int, n: int, k: int,
                        stream=None):
-    _check(lib().q2_0_mmq_blockdots(_ptr(_u8(act_q8, "act_q8")), _ptr(_u8(w_q2, "w_q2")), _ptr(out_i32),
-                                    m0, mt, n0, nt, m, n, k, _stream(stream)))
+    _blockdots(lib().q2_0_mmq_blockdots, act_q8, w_q2, q2_0_weight_bytes(n, k), out_i32, m0, mt, n0, nt,
+               m, n, k, stream)
 
 
 def q4k_mmq_blockdots(act_q8, w_q4k, out_i32, m0: int, mt: int, n0: int, nt: int, m: int, n: int, k: int,
                       stream=None):
-    _check(lib().q4k_mmq_blockdots(_ptr(_u8(act_q8, "act_q8")), _ptr(_u8(w_q4k, "w_q4k")), _ptr(out_i32),
-                                   m0, mt, n0, nt, m, n, k, _stream(stream)))
+    _blockdots(lib().q4k_mmq_blockdots, act_q8, w_q4k, q4k_weight_bytes(n, k), out_i32, m0, mt, n0, nt,
+               m, n, k, stream)

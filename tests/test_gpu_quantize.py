@@ -48,6 +48,44 @@ def test_quantize_edge_values(gpu):
     assert np.array_equal(_run(gpu, act, m, k), ref)
 
 
+def _near_ties(seed, count):
+    """Block maxima amax (which fix d = fp16(amax/127)) with the bf16 values x,
+    |x| <= amax, whose binary32 quotient x/d lies within 2^-12 of a
+    half-integer (exact ties included), where roundf's tie rule and the
+    division's last bit decide the code."""
+    F = np.float32
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    x = (bits << 16).view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) <= 2047) & (x != 0)].astype(F)
+    g = np.random.default_rng(seed)
+    found = []
+    while len(found) < count:
+        amax = F(np.abs(g.choice(x)))
+        d = F(np.float16(amax / F(127)))
+        if d == 0:
+            continue
+        with np.errstate(over="ignore"):
+            t = np.abs((x / d).astype(F))
+        sel = (np.abs(x) <= amax) & (np.abs(t - np.floor(t) - F(0.5)) < F(2.0 ** -12))
+        if sel.any():
+            found.append((amax, x[sel]))
+    return found
+
+
+def test_quantize_near_ties(gpu):
+    # blocks whose quotients x/d sit on or within 2^-12 of a half-integer
+    rows = []
+    for amax, xs in _near_ties(23, 64):
+        vals = np.resize(xs, 31)
+        rows.append(np.concatenate([[amax], vals * np.where(np.arange(31) % 2, -1, 1)]).astype(np.float32))
+    x = np.stack(rows).reshape(8, -1)  # 8 rows of 8 blocks of 32
+    m, k = x.shape
+    act = inputs.f32_to_bf16_bits(x)
+    ref, flagged = oracle.quantize_act_q8_1(act, m, k)
+    assert flagged == 0
+    assert np.array_equal(_run(gpu, act, m, k), ref)
+
+
 def test_quantize_prefill_full_size(gpu):
     # m = 2048, k = 2048 qkvz prefill input (with outlier channels), whole buffer
     d = inputs.prefill_qkvz()

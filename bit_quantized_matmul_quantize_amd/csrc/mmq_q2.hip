@@ -206,10 +206,12 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
         A[sn][b] = *reinterpret_cast<const v4i *>(w_lds + nl * LDS_STRIDE + 32 * b + 16 * hi);
     }
 
-    // The wave computing a group takes issue priority over the wave of the
-    // other workgroup on its SIMD (which is staging or waiting): measured 5%
-    // faster at m = 512 and the same at m = 2048.
-    __builtin_amdgcn_s_setprio(1);
+    // In the 96 x 128 layout the wave computing a group takes issue priority
+    // over the wave of the other workgroup on its SIMD (which is staging or
+    // waiting): 5% faster at m = 512.  On the 128 x 128 layout it measured
+    // the same at m = 2048 and 1-3% slower on the FFN shapes, so it is off.
+    constexpr bool kPrio = TM == 1;
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
     // kSteps steps (sn, sm, b), software-pipelined by one: the MFMA of step i + 1
     // is issued before the epilogue of step i, so the matrix core runs while
     // the VALU folds the previous block; two result registers alternate.  A
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
   }
 #undef BQMM_FETCH
 #undef BQMM_STAGE

@@ -94,14 +94,26 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
   const uint32_t w_row = min(n_base + (w_stager ? tid >> 1 : 0u), n - 1u), w_half = tid & 1u;
   const uint32_t s_row = (tid < BN) ? min(n_base + tid, n - 1u) : min(m_base + (s_stager ? tid - BN : 0u), m - 1u);
 
-  // Row exponent: binary16 exponent field of the largest block scale of the row.
+  // Row exponent: binary16 exponent field of the largest block scale of the
+  // row.  Two lanes per row read its (d, s) pairs as 16-byte chunks of four
+  // blocks (k % 128 == 0, so the row holds whole chunks), eight loads in
+  // flight per batch: one memory round trip per batch instead of one per
+  // block.  Chunk indices past the row's end are clamped to its last chunk,
+  // which leaves the maximum unchanged.
   {
     const uint32_t r = tid >> 1, part = tid & 1u;
-    const uint32_t *pairs =
-        reinterpret_cast<const uint32_t *>(ds) + (uint64_t)min(m_base + r, m - 1u) * nblk_pad;
-    const uint32_t nb = k / 32u;
+    const uint4 *chunks =
+        reinterpret_cast<const uint4 *>(ds + 4ull * (uint64_t)min(m_base + r, m - 1u) * nblk_pad);
+    const uint32_t nq = k / 128u;
     uint32_t mx = 0;
-    for (uint32_t b = part; b < nb; b += 2) mx = max(mx, pairs[b] & 0x7FFFu);
+    for (uint32_t c0 = part; c0 < nq; c0 += 16u) {
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = chunks[min(c0 + 2u * j, nq - 1u)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        mx = max(mx, max(max(v[j].x & 0x7FFFu, v[j].y & 0x7FFFu), max(v[j].z & 0x7FFFu, v[j].w & 0x7FFFu)));
+    }
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
     if (part == 0) rowexp[r] = (int)(mx >> 10);
   }

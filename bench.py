@@ -48,12 +48,15 @@ BF16_PEAK_TFLOPS = 2516.0    # MI355X dense bf16 MFMA, published
 DECODE_CALLS = 1000
 DECODE_COPIES = 80
 COPY_BYTES = 256 << 20
-# Per-dispatch HBM traffic of the decode GEMV, measured with rocprofv3 counters
-# (FETCH_SIZE + WRITE_SIZE, scaled by the same counters on the copy leg).  The
-# figure is reported only while the kernel source still matches the hash the
-# counters were taken with.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_gemv_n12288_k2048.txt")
-GEMV_SOURCE = os.path.join(ROOT, "bit_quantized_matmul_quantize_amd", "csrc", "gemv.hip")
+# Per-dispatch HBM traffic of the decode GEMV and of the m = 2048 MMQ, measured
+# with rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled by the same counters
+# on the copy leg).  A figure is reported only while the kernel source still
+# matches the hash the counters were taken with.
+_CSRC = os.path.join(ROOT, "bit_quantized_matmul_quantize_amd", "csrc")
+TRAFFIC_DECODE = (os.path.join(ROOT, "profiles", "hbm_traffic_decode_gemv_n12288_k2048.txt"),
+                  os.path.join(_CSRC, "gemv.hip"))
+TRAFFIC_MMQ = (os.path.join(ROOT, "profiles", "hbm_traffic_q2_0_mmq_m2048_n12288_k2048.txt"),
+               os.path.join(_CSRC, "mmq_q2.hip"))
 
 
 def parse():
@@ -171,9 +174,10 @@ def verify_leg(bq, dev, W, act, m, H, I):
         bq.q2_0_gemv_vec_batchm(g_, wd, o_, m, H, I)
 
     work = wg.numel() + wu.numel() + wd.numel() + m * (6 * H + 12 * I)
-    kname = "q2_0_gemv_mfma_kernel" if m >= 6 else "q2_0_gemvm_kernel"
+    kname = (f"q2_0_gemv_mfma_kernel<{m}> x3 + silu_mul" if m >= 4 else
+             f"q2_0_gemvp_kernel<{m}> gate, up + silu_mul + q2_0_gemvm_kernel<{m}> down")
     return Leg(f"verify_ffn_m{m}", fn, [wg, wu, wd, x, g_, u_, o_], 4, work, "GB/s",
-               f"{kname}<{m}> x3 + silu_mul", HBM_PEAK_GBS, "hbm")
+               kname, HBM_PEAK_GBS, "hbm")
 
 
 def verify_fused_leg(bq, dev, W, act, m, H, I):
@@ -189,9 +193,10 @@ def verify_fused_leg(bq, dev, W, act, m, H, I):
         bq.q2_0_gemv_vec_batchm(h_, wd, o_, m, H, I)
 
     work = wg.numel() + wu.numel() + wd.numel() + m * (2 * H + 4 * I)
-    kname = "q2_0_gemv_mfma_kernel" if m >= 6 else "q2_0_gemvm_kernel"
+    kname = (f"q2_0_gemv_mfma_kernel<{m}> gate+up+silu, q2_0_gemv_mfma_kernel<{m}> down" if m >= 4 else
+             f"q2_0_gemvp_kernel<{m}> gate+up+silu, q2_0_gemvm_kernel<{m}> down")
     return Leg(f"verify_ffn_fused_m{m}", fn, [wg, wu, wd, x, h_, o_], 2, work, "GB/s",
-               f"{kname}<{m}> gate+up+silu, {kname}<{m}> down", HBM_PEAK_GBS, "hbm")
+               kname, HBM_PEAK_GBS, "hbm")
 
 
 def copy_leg(dev):
@@ -203,13 +208,15 @@ def copy_leg(dev):
                "device copy", HBM_PEAK_GBS, "hbm")
 
 
-def measured_traffic():
-    """Bytes per decode GEMV dispatch from the committed counter summary, or
-    None when it is missing or was taken on another version of the kernel."""
+def measured_traffic(summary):
+    """Bytes per dispatch from a committed counter summary (path, kernel
+    source), or None when it is missing or was taken on another version of
+    the kernel."""
     import hashlib
+    path, source = summary
     try:
-        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
-        digest = hashlib.sha256(open(GEMV_SOURCE, "rb").read()).hexdigest()
+        fields = dict(line.split(":", 1) for line in open(path) if ":" in line)
+        digest = hashlib.sha256(open(source, "rb").read()).hexdigest()
         if fields.get("kernel_source_sha256", "").strip() != digest:
             return None
         return int(fields["traffic_bytes_per_launch"].strip())
@@ -370,7 +377,7 @@ def main():
         s = summaries["decode_gemv_m1"]
         result["value"] = s["value"]
         result["roofline"] = {"bound": "hbm", "achieved": s["value"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": s["frac_of_peak"], "traffic": measured_traffic(),
+                              "frac": s["frac_of_peak"], "traffic": measured_traffic(TRAFFIC_DECODE),
                               "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                               "copy-calibrated)",
                               "kernel": s["kernel"], "us_per_launch": s["us_per_launch"],
@@ -380,7 +387,12 @@ def main():
         result["prefill"] = {"metric": "Q2_0 MMQ prefill int8 TOPS (2mnk / kernel time), m=2048 n=12288 k=2048",
                              "value": s["value"], "unit": "TOPS", "dtype": "i8",
                              "roofline": {"bound": "mfma", "achieved": s["value"], "peak": INT8_PEAK_TOPS,
-                                          "unit": "TOP/s", "frac": s["frac_of_peak"], "traffic": None}}
+                                          "unit": "TOP/s", "frac": s["frac_of_peak"],
+                                          "traffic": measured_traffic(TRAFFIC_MMQ),
+                                          "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + "
+                                                          "WRITE_SIZE, copy-calibrated)",
+                                          "ops_per_launch": 2 * 2048 * 12288 * 2048,
+                                          "algorithmic_bytes_per_launch": 61734912}}
     result["legs"] = summaries
 
     # ---- CPU oracle baseline (rank 0, N = 1) -----------------------------------

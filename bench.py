@@ -314,7 +314,7 @@ def q4k_legs(bq, dev, Q):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: the path has no inter-GPU "
+        print(json.dumps({"error": "the library runs on one GPU: the path has no inter-GPU "
                           "sharding (--gpus must be 1)", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

@@ -471,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvm_kernel(const uint16_t *__
 // pairs, then the four partial biases; chunks padded so that 16 consecutive
 // chunks read by one instruction hit distinct bank quads); chunks past k hold
 // zero activations and biases, so their clamped weight loads add 0.
-template <int M, int G, int R, int NW>
+template <int M, int G, int R, int NW, int PD>
 __global__ __launch_bounds__(kThreads) void q2_0_gemvp_kernel(const uint16_t *__restrict__ act,
                                                               const uint8_t *__restrict__ w,
                                                               const uint8_t *__restrict__ w2,
@@ -479,6 +479,7 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvp_kernel(const uint16_t *__
                                                               uint32_t k) {
   static_assert(G == 16 || G == 32, "lane group of 16 or 32");
   static_assert(NW == 1 || NW == 2, "one weight, or gate and up");
+  static_assert(PD == 2 || PD == 3, "two or three weight register sets");
   constexpr int RR = NW * R;
   constexpr int CS = gemvm_chunk_dwords(M);
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
@@ -540,14 +541,15 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvp_kernel(const uint16_t *__
     }
   };
 
-  uint4 wq0[RR], wq1[RR];
-  uint32_t sc0[RR], sc1[RR];
+  uint4 wq[PD][RR];
+  uint32_t sc[PD][RR];
   {
     // the first item's activation loads go out before the first weight loads
     uint4 v[8];
     const uint32_t first = min(tid, items - 1u);
     load_item(first, v);
-    load_unit(0, wq0, sc0);
+#pragma unroll
+    for (int p = 0; p + 1 < PD; ++p) load_unit(p, wq[p], sc[p]);
     if (tid < items) prep_item(first, v);
   }
   for (uint32_t item = tid + kThreads; item < items; item += kThreads) {
@@ -613,25 +615,39 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemvp_kernel(const uint16_t *__
     }
   };
 
-  // two register sets alternate; the last one or two chunks are peeled so
-  // that every prefetch is unconditional, and the scheduling barriers keep
-  // each prefetch above the wait for the chunk being computed
-  uint32_t it = 0;
-  for (; it + 2 < iters; it += 2) {
-    load_unit(it + 1, wq1, sc1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(it, wq0, sc0);
-    load_unit(it + 2, wq0, sc0);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(it + 1, wq1, sc1);
-  }
-  if (it + 1 < iters) {
-    load_unit(it + 1, wq1, sc1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(it, wq0, sc0);
-    compute(it + 1, wq1, sc1);
+  if constexpr (PD == 2) {
+    // two register sets alternate; the last one or two chunks are peeled so
+    // that every prefetch is unconditional, and the scheduling barriers keep
+    // each prefetch above the wait for the chunk being computed
+    uint32_t it = 0;
+    for (; it + 2 < iters; it += 2) {
+      load_unit(it + 1, wq[1], sc[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(it, wq[0], sc[0]);
+      load_unit(it + 2, wq[0], sc[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(it + 1, wq[1], sc[1]);
+    }
+    if (it + 1 < iters) {
+      load_unit(it + 1, wq[1], sc[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(it, wq[0], sc[0]);
+      compute(it + 1, wq[1], sc[1]);
+    } else {
+      compute(it, wq[0], sc[0]);
+    }
   } else {
-    compute(it, wq0, sc0);
+    // three sets rotate (long rows): unit it + 2 is loaded while unit it is
+    // computed; loads past the last unit read the clamped last chunk and are
+    // not computed
+    for (uint32_t it = 0; it < iters; it += PD) {
+#pragma unroll
+      for (int p = 0; p < PD; ++p) {
+        load_unit(it + p + PD - 1, wq[(p + PD - 1) % PD], sc[(p + PD - 1) % PD]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (it + p < iters) compute(it + p, wq[p], sc[p]);
+      }
+    }
   }
 
 #pragma unroll
@@ -681,22 +697,33 @@ __host__ __device__ inline uint32_t gemvp_lds_bytes(uint32_t m, uint32_t k) {
   return Cpad * cs * 4u;
 }
 
-template <int M, int NW>
-hipError_t launch_gemvp(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
-                        hipStream_t s) {
+template <int M, int NW, int PD>
+hipError_t launch_gemvp_pd(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
+                           hipStream_t s) {
   constexpr int G = BQMM_GEMVP_G, R = NW == 2 ? 1 : M;
   const uint32_t lds = gemvp_lds_bytes(M, k);
   if (lds > 65536u) {
-    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(q2_0_gemvp_kernel<M, G, R, NW>),
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(q2_0_gemvp_kernel<M, G, R, NW, PD>),
                                             (int)kMaxLdsP);
     if (e != hipSuccess) return e;
   }
   constexpr uint32_t rows = kThreads / G * R;
   const uint32_t blocks = (n + rows - 1) / rows;
-  hipLaunchKernelGGL((q2_0_gemvp_kernel<M, G, R, NW>), dim3(blocks), dim3(kThreads), lds, s,
+  hipLaunchKernelGGL((q2_0_gemvp_kernel<M, G, R, NW, PD>), dim3(blocks), dim3(kThreads), lds, s,
                      static_cast<const uint16_t *>(act), static_cast<const uint8_t *>(w),
                      static_cast<const uint8_t *>(w2), static_cast<uint16_t *>(out), n, k);
   return hipGetLastError();
+}
+
+// A third weight register set pays off for one activation row and long rows:
+// down [5120, 17408] m = 1 (17 chunks per lane) 12.0 -> 11.3 us, while every
+// k = 5120 shape (5 chunks per lane) measured slower with it.
+template <int M, int NW>
+hipError_t launch_gemvp(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
+                        hipStream_t s) {
+  if (M == 1 && NW == 1 && (k >> 6) >= 12u * BQMM_GEMVP_G)
+    return launch_gemvp_pd<M, NW, 3>(act, w, w2, out, n, k, s);
+  return launch_gemvp_pd<M, NW, 2>(act, w, w2, out, n, k, s);
 }
 
 // Launch shapes (measured): wide outputs (gate/up, n = 17408) take 16-lane

@@ -56,7 +56,10 @@ def test_decode_qkvz_full(gpu):
                                         # k whose activations fit its LDS for each m, and one past it
                                         (2, 5, 128, 44), (3, 49, 256, 45), (1, 77, 28672, 46),
                                         (2, 65, 13312, 47), (3, 33, 9216, 48), (2, 33, 13440, 49),
-                                        (1, 4096 + 16, 4096, 50)])
+                                        (1, 4096 + 16, 4096, 50),
+                                        # whole-vector kernel, m = 1 with three weight register sets
+                                        # (k >= 12288): 12 chunks per lane, and 13 with a ragged last
+                                        (1, 41, 12288, 51), (1, 29, 12416, 52)])
 def test_ragged(gpu, m, n, k, seed):
     g = inputs.rng(seed)
     w = inputs.q2_0_weight(g, n, k)

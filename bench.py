@@ -337,8 +337,10 @@ def main():
             legs.append(verify_leg(bq, dev, W, f["act"], m, f["hidden"], f["inter"]))
         for m in (2, 3, 4, 8):
             legs.append(verify_fused_leg(bq, dev, W, f["act"], m, f["hidden"], f["inter"]))
+    prefill_ctx = None
     if "prefill" in legs_wanted:
-        legs += prefill_legs(bq, dev, inputs.prefill_qkvz())
+        prefill_ctx = inputs.prefill_qkvz()
+        legs += prefill_legs(bq, dev, prefill_ctx)
     if "ffn" in legs_wanted:
         legs += ffn_legs(bq, dev, inputs.prefill_ffn())
     if "q4k" in legs_wanted:
@@ -395,14 +397,15 @@ def main():
                                           "algorithmic_bytes_per_launch": 61734912}}
     result["legs"] = summaries
 
-    # ---- CPU oracle baseline (rank 0, N = 1) -----------------------------------
-    if not args.no_cpu_baseline and "decode_gemv_m1" in summaries:
-        import oracle
-        d = decode_ctx["d"]
+    # ---- CPU oracle baselines (rank 0, N = 1), on one pinned host core ----------
+    if not args.no_cpu_baseline:
         try:
             os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
         except Exception:
             pass
+    if not args.no_cpu_baseline and "decode_gemv_m1" in summaries:
+        import oracle
+        d = decode_ctx["d"]
         calls, t_cpu = 0, 0.0
         while t_cpu < args.cpu_seconds and calls < 200:
             t1 = time.perf_counter()
@@ -413,6 +416,23 @@ def main():
         result["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                                   "sample": f"{calls} decode GEMV calls (n=12288, k=2048) of the oracle, "
                                             f"{t_cpu:.1f} s on one pinned host core of {os.cpu_count()}"}
+    # ---- CPU oracle baseline of the MMQ: 16 of the 2048 rows, all n -----------
+    if not args.no_cpu_baseline and prefill_ctx is not None and "prefill" in result:
+        import oracle
+        p, rows = prefill_ctx, 16
+        n, k = p["n"], p["k"]
+        q8_rows, _ = oracle.quantize_act_q8_1(np.ascontiguousarray(p["act"][:rows]), rows, k)
+        calls, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds / 4 and calls < 50:
+            t1 = time.perf_counter()
+            oracle.q2_0_mmq(q8_rows, p["w"], rows, n, k)
+            t_cpu += time.perf_counter() - t1
+            calls += 1
+        result["prefill"]["cpu_baseline"] = {
+            "value": round(2.0 * rows * n * k * calls / t_cpu / 1e12, 6), "unit": "TOPS", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{calls} oracle MMQ calls on {rows} of the 2048 activation rows (n=12288, k=2048; the "
+                      f"oracle's cost is linear in rows), {t_cpu:.1f} s on one pinned host core of {os.cpu_count()}"}
     print(json.dumps(result), flush=True)
 
 

@@ -8,10 +8,10 @@
 // Tile BN (n) x 128 (m): 128 x 128 with 4 waves of 64 x 64, or 96 x 128 with
 // 4 waves of 96 x 32 where that fills the chip in fewer rounds of
 // workgroups (the same choice as the MMQ's).  k is staged KS = 64 at a time
-// through two LDS stages: while stage s is multiplied, the registers holding
-// the global loads of step s + 1 are written into the other stage and the
-// loads of step s + 2 are already in flight, so one barrier per step and no
-// exposed load latency.  The weight is the A operand so that a lane's 16
+// through two LDS stages: after stage s's operands are read, the registers
+// holding the global loads of step s + 1 are written into the other stage and
+// the loads of step s + 2 are issued, so one barrier per step and no exposed
+// load latency.  The weight is the A operand so that a lane's 16
 // accumulators share one output row and are stored as four 8-byte runs.
 // Rows past m or n load the last valid row and are not stored.
 #include "bqmm_internal.h"
@@ -104,26 +104,34 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gemm_bf16_kernel(
   if (nsteps > 1) BQMM_GLOAD(1u);
   for (uint32_t s = 0; s < nsteps; ++s) {
     __syncthreads();  // stage s is complete; nobody still reads stage s + 1's buffer
+    const uint8_t *a_l = lds + (s & 1u) * kStageBytes, *w_l = a_l + kTileBytes;
+    // Per step: every operand of the step is read from LDS first, then the
+    // next stage is written from registers (its LDS writes queue behind the
+    // reads, so the first MFMA does not wait for them; 11-13% faster than
+    // writing first), then the MFMAs run.
+    v8bf A[KS / 16][TN], B[KS / 16][TM];
+#pragma unroll
+    for (int kk = 0; kk < KS / 16; ++kk) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+        A[kk][t] = *reinterpret_cast<const v8bf *>(w_l + (wn * (32 * TN) + t * 32 + (lane & 31)) * LDS_STRIDE + 32 * kk + 16 * (lane >> 5));
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+        B[kk][t] = *reinterpret_cast<const v8bf *>(a_l + (wm * (32 * TM) + t * 32 + (lane & 31)) * LDS_STRIDE + 32 * kk + 16 * (lane >> 5));
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (s + 1 < nsteps) {
       BQMM_STORE((s + 1) & 1u);
       if (s + 2 < nsteps) BQMM_GLOAD(s + 2);
     }
-    const uint8_t *a_l = lds + (s & 1u) * kStageBytes, *w_l = a_l + kTileBytes;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < KS / 16; ++kk) {
-      v8bf A[TN], B[TM];
-#pragma unroll
-      for (int t = 0; t < TN; ++t)
-        A[t] = *reinterpret_cast<const v8bf *>(w_l + (wn * (32 * TN) + t * 32 + (lane & 31)) * LDS_STRIDE + 32 * kk + 16 * (lane >> 5));
-#pragma unroll
-      for (int t = 0; t < TM; ++t)
-        B[t] = *reinterpret_cast<const v8bf *>(a_l + (wm * (32 * TM) + t * 32 + (lane & 31)) * LDS_STRIDE + 32 * kk + 16 * (lane >> 5));
+    for (int kk = 0; kk < KS / 16; ++kk)
 #pragma unroll
       for (int sn = 0; sn < TN; ++sn)
 #pragma unroll
         for (int sm = 0; sm < TM; ++sm)
-          acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[sn], B[sm], acc[sn][sm], 0, 0, 0);
-    }
+          acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kk][sn], B[kk][sm], acc[sn][sm], 0, 0, 0);
   }
 #undef BQMM_GLOAD
 #undef BQMM_STORE

@@ -721,8 +721,9 @@ hipError_t launch_gemvp_pd(const void *act, const void *w, const void *w2, void 
 template <int M, int NW>
 hipError_t launch_gemvp(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
                         hipStream_t s) {
-  if (M == 1 && NW == 1 && (k >> 6) >= 12u * BQMM_GEMVP_G)
-    return launch_gemvp_pd<M, NW, 3>(act, w, w2, out, n, k, s);
+  if constexpr (M == 1 && NW == 1) {
+    if ((k >> 6) >= 12u * BQMM_GEMVP_G) return launch_gemvp_pd<M, NW, 3>(act, w, w2, out, n, k, s);
+  }
   return launch_gemvp_pd<M, NW, 2>(act, w, w2, out, n, k, s);
 }
 

@@ -111,6 +111,10 @@ hipError_t launch_q4k_gemv(const void *act, const void *w, void *out, uint32_t n
                            hipStream_t s);
 hipError_t launch_quantize_weight_q4k(const void *w_bf16, void *out, uint32_t n, uint32_t k,
                                       hipStream_t s);
+// True when the matrix-core GEMV's staged weight scales fit 64 KB of LDS for
+// this shape (nw = 1 single weight, 2 fused gate/up); the dispatcher falls
+// back to the vector kernel otherwise.
+bool q2_0_gemv_mfma_fits(uint32_t n, uint32_t k, int nw);
 hipError_t launch_q2_0_gemv_mfma(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
                                  uint32_t k, hipStream_t s);
 hipError_t launch_q2_0_gemv_mfma_gate_up(const void *act, const void *w_gate, const void *w_up,

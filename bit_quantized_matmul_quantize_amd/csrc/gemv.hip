@@ -89,7 +89,6 @@ __device__ __forceinline__ float field_bias(const uint32_t D[8], uint32_t bw) {
 constexpr int kRowsPerLane = BQMM_GEMV_ROWS;
 constexpr int kChunkStride = 36;  // dwords per chunk in LDS: 32 pairs, 4 partial biases
 constexpr uint32_t kMaxK1 = 32768;
-constexpr uint32_t kMaxKMfma = 65536;
 constexpr uint32_t kMinMMfma = BQMM_GEMV_MIN_M_MFMA;
 
 __global__ __launch_bounds__(kThreads) void q2_0_gemv1_kernel(const uint16_t *__restrict__ act,
@@ -805,6 +804,13 @@ inline bool use_gemvp(uint32_t m, uint32_t k) {
   return gemvp_lds_bytes(m, k) <= kMaxLdsP;
 }
 
+// The matrix-core kernel serves m >= kMinMMfma where the fused gate/up
+// launch's staged scales fit its LDS (the stricter of the two launches), so
+// that the single and the fused call take the same kernel for every shape.
+inline bool use_gemv_mfma(uint32_t m, uint32_t n, uint32_t k) {
+  return m >= kMinMMfma && q2_0_gemv_mfma_fits(n, k, 2);
+}
+
 hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
                             uint32_t k, hipStream_t s) {
   if (use_gemvp(m, k)) {
@@ -816,7 +822,11 @@ hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t 
   }
   if (m == 1 && k <= kMaxK1) {
     const uint32_t blocks = (n + 8 * kRowsPerLane - 1) / (8 * kRowsPerLane);
-    const size_t lds = (size_t)(k >> 6) * kChunkStride * 4u;
+    const size_t lds = (size_t)(k >> 6) * kChunkStride * 4u;  // 72 KB at kMaxK1
+    if (lds > 65536u) {
+      const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(q2_0_gemv1_kernel), (int)lds);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(q2_0_gemv1_kernel, dim3(blocks), dim3(kThreads), lds, s,
                        static_cast<const uint16_t *>(act), static_cast<const uint8_t *>(w),
                        static_cast<uint16_t *>(out), n, k);
@@ -826,7 +836,7 @@ hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t 
   // the matrix-core kernel is faster (its staged scales bound k); measured on
   // the FFN shapes, m = 4 is about even on gate/up and 7% faster on down,
   // m = 5 20-30% faster.
-  if (m >= kMinMMfma && k <= kMaxKMfma) return launch_q2_0_gemv_mfma(act, w, out, m, n, k, s);
+  if (use_gemv_mfma(m, n, k)) return launch_q2_0_gemv_mfma(act, w, out, m, n, k, s);
   switch (m) {
     case 1: return launch_gemvm<1>(act, w, out, n, k, s);
     case 2: return launch_gemvm<2>(act, w, out, n, k, s);
@@ -852,7 +862,7 @@ hipError_t launch_q2_0_gemv_gate_up_silu(const void *act, const void *w_gate, co
       default: return launch_gemvp<3, 2>(act, w_gate, w_up, out, n, k, s);
     }
   }
-  if (m >= kMinMMfma && k <= kMaxKMfma)
+  if (use_gemv_mfma(m, n, k))
     return launch_q2_0_gemv_mfma_gate_up(act, w_gate, w_up, out, m, n, k, s);
   switch (m) {
     case 1: return launch_gemvm_gate_up<1>(act, w_gate, w_up, out, n, k, s);

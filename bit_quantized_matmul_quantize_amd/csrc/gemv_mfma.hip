@@ -223,16 +223,22 @@ __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint
   }
 }
 
-template <int M, int W, int T, int NW, int MINW>
-hipError_t launch_w(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
-                    hipStream_t s) {
-  constexpr int P = BQMM_GEMVX_P;
+// Dynamic LDS of a launch with W waves of T tiles: the staged weight scales
+// of a wave's groups, or the partial sums of the final reduction.
+inline size_t lds_bytes(int W, int T, int NW, uint32_t k) {
   const uint32_t G = k >> 7;
   const uint32_t gmax = (G + W - 1) / W;
   const size_t sc_bytes = (size_t)W * NW * 16 * T * gmax * 2;
   const size_t red_bytes = (size_t)W * NW * T * 4 * 64 * 4;
-  const size_t lds = sc_bytes > red_bytes ? sc_bytes : red_bytes;
-  if (lds > 65536) return hipErrorInvalidValue;  // k too large for the staged scales
+  return sc_bytes > red_bytes ? sc_bytes : red_bytes;
+}
+
+template <int M, int W, int T, int NW, int MINW>
+hipError_t launch_w(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
+                    hipStream_t s) {
+  constexpr int P = BQMM_GEMVX_P;
+  const size_t lds = lds_bytes(W, T, NW, k);
+  if (lds > 65536) return hipErrorInvalidValue;  // the dispatcher checks q2_0_gemv_mfma_fits first
   const uint32_t blocks = (n + 16 * T - 1) / (16 * T);
   hipLaunchKernelGGL((q2_0_gemv_mfma_kernel<M, T, W, P, NW, MINW>), dim3(blocks), dim3(64 * W), lds, s,
                      static_cast<const uint16_t *>(act), static_cast<const uint8_t *>(w),
@@ -263,6 +269,17 @@ hipError_t launch_w(const void *act, const void *w, const void *w2, void *out, u
 #ifndef BQMM_GEMVX_MINW_FUSED
 #define BQMM_GEMVX_MINW_FUSED 2
 #endif
+// The launch shape launch_m picks for (n, k): waves W and tiles per wave T.
+inline void launch_shape(uint32_t n, uint32_t k, int NW, int &W, int &T) {
+  if ((k >> 7) >= 8) {
+    W = 8;
+    T = NW == 2 ? BQMM_GEMVX_T_FUSED : (n >= BQMM_GEMVX_WIDE_N ? BQMM_GEMVX_T_WIDE : BQMM_GEMVX_T_NARROW);
+  } else {
+    W = 1;
+    T = 2;
+  }
+}
+
 template <int M, int NW>
 hipError_t launch_m(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
                     hipStream_t s) {
@@ -301,6 +318,12 @@ hipError_t launch_any_m(const void *act, const void *w, const void *w2, void *ou
 }
 
 }  // namespace
+
+bool q2_0_gemv_mfma_fits(uint32_t n, uint32_t k, int nw) {
+  int W = 1, T = 1;
+  launch_shape(n, k, nw, W, T);
+  return lds_bytes(W, T, nw, k) <= 65536;
+}
 
 hipError_t launch_q2_0_gemv_mfma(const void *act, const void *w, void *out, uint32_t m, uint32_t n,
                                  uint32_t k, hipStream_t s) {

@@ -16,14 +16,29 @@
 //     int8 (c - 2) with a byte-permute lookup,
 //   * the group's weight scales (fp32) and, per activation row and block, an
 //     integer multiplier mu = da * 2^(30 - E) where E is the binary16
-//     exponent of the row's largest scale (exact whenever the block's scale
-//     is within 2^5 of the row maximum; otherwise rounded to 16 bits).
+//     exponent of the row's largest scale.
 // Each wave then runs v_mfma_i32_32x32x32_i8 (K = 32 = one q8_1 block) with
 // the weights as the A operand and the activations as B, so a lane's 16
 // accumulators share one activation row: the activation multiplier is one
 // lane value.  Per block: acc += mu * D (24-bit integer multiply-add, exact
 // int32 accumulation over the 128-group); per group: out += dw * float(acc);
 // at the end out *= 2^(E - 30) and is rounded to bf16.
+//
+// mu is exact when the block's binary16 exponent is at most 5 below E: the
+// 11-bit significand shifted left by at most 5 stays below 2^16, and four
+// products of |D| <= 8128 with it fit int32.  A block exactly 6 below gets
+// its significand halved and rounded to nearest: its scale is applied with a
+// relative error of at most 2^-10 (twice the binary16 rounding d itself
+// carried), no more.  The workloads' rows stay within that span of 6 (with
+// 1% outlier channels about 3% of rows reach it).  For a row whose nonzero
+// block scales spread wider, the tile runs the k loop once per band of seven
+// exponents: pass p takes E_p = E - 7p, gives mu = da * 2^(30 - E_p) to the
+// blocks whose exponent lies in [E_p - 6, E_p] and 0 to every other block,
+// and carries the factor 2^-7p in the staged weight scales, so the passes add
+// up to the whole product and no block's scale is rounded by more than the
+// above or dropped (at most five passes cover the binary16 range).  The
+// prologue finds the number of passes; a tile of rows within the span takes
+// one.
 #include "bqmm_internal.h"
 
 namespace bqmm {
@@ -52,6 +67,18 @@ __device__ __forceinline__ uint32_t unpack_signed(uint32_t word, int j) {
   return __builtin_amdgcn_perm(0u, 0x0100FFFEu, sel);
 }
 
+// Exponent field of a binary16 scale (low 16 bits of h), at least 1: a
+// subnormal's significand is scaled like field 1's.
+__device__ __forceinline__ uint32_t exp_field(uint32_t h) { return max((h >> 10) & 31u, 1u); }
+
+// Integer multiplier of block scale h in the pass whose top exponent is ep:
+// da * 2^(30 - ep) when the block's exponent lies in [ep - 6, ep], else 0
+// (a zero scale gives 0 either way).
+__device__ __forceinline__ int band_mu(uint32_t h, int ep) {
+  const float v = ldexpf(f16_bits_to_f32(h & 0xFFFFu), 30 - ep);
+  return (uint32_t)(ep - (int)exp_field(h)) <= 6u ? (int)rintf(v) : 0;
+}
+
 // TN x TM subtiles of 32 x 32 per wave, WN waves along n (4 / WN along m).
 template <bool kDump, int TN, int TM, int WN>
 __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
@@ -68,7 +95,10 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
   // Two LDS stages (dynamic shared memory, kStageBytes each): group g is
   // computed from stage g % 2 while group g + 1 is written into the other.
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int rowexp[BM];
+  // Per tile row: the binary16 exponent field E of its largest block scale.
+  __shared__ int mmq_rowexp[BM];
+  // Passes of the k loop the tile needs (one per band of seven exponents).
+  __shared__ int mmq_passes;
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u, l32 = lane & 31u, hi = lane >> 5;
@@ -94,29 +124,43 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
   const uint32_t w_row = min(n_base + (w_stager ? tid >> 1 : 0u), n - 1u), w_half = tid & 1u;
   const uint32_t s_row = (tid < BN) ? min(n_base + tid, n - 1u) : min(m_base + (s_stager ? tid - BN : 0u), m - 1u);
 
-  // Row exponent: binary16 exponent field of the largest block scale of the
-  // row.  Two lanes per row read its (d, s) pairs as 16-byte chunks of four
+  // Row exponent: exponent field E (exp_field) of the largest block scale of
+  // the row, and the smallest field among its nonzero block scales, which
+  // give the row's band passes (E - min) / 7 + 1; the tile takes the most of
+  // its rows.  Two lanes per row read its (d, s) pairs as 16-byte chunks of four
   // blocks (k % 128 == 0, so the row holds whole chunks), eight loads in
   // flight per batch: one memory round trip per batch instead of one per
   // block.  Chunk indices past the row's end are clamped to its last chunk,
-  // which leaves the maximum unchanged.
+  // which leaves both extremes unchanged.
+  if (tid == 0) mmq_passes = 1;
   {
     const uint32_t r = tid >> 1, part = tid & 1u;
     const uint4 *chunks =
         reinterpret_cast<const uint4 *>(ds + 4ull * (uint64_t)min(m_base + r, m - 1u) * nblk_pad);
     const uint32_t nq = k / 128u;
-    uint32_t mx = 0;
+    uint32_t mx = 0, mn = 31u;
+    // exponent field of a nonzero scale; 31, above every field, for a zero one
+    auto nz_field = [](uint32_t h) { return (h & 0x7FFFu) == 0u ? 31u : exp_field(h); };
     for (uint32_t c0 = part; c0 < nq; c0 += 16u) {
       uint4 v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = chunks[min(c0 + 2u * j, nq - 1u)];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 8; ++j) {
         mx = max(mx, max(max(v[j].x & 0x7FFFu, v[j].y & 0x7FFFu), max(v[j].z & 0x7FFFu, v[j].w & 0x7FFFu)));
+        mn = min(mn, min(min(nz_field(v[j].x), nz_field(v[j].y)), min(nz_field(v[j].z), nz_field(v[j].w))));
+      }
     }
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
-    if (part == 0) rowexp[r] = (int)(mx >> 10);
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, 1));
+    __syncthreads();  // mmq_passes initialised
+    if (part == 0) {
+      const int e = (int)exp_field(mx);
+      mmq_rowexp[r] = e;
+      if ((int)mn < e - 6) atomicMax(&mmq_passes, (e - (int)mn) / 7 + 1);
+    }
   }
+  __syncthreads();  // mmq_rowexp and mmq_passes visible
 
   // Prefetch registers for one group (next group's data is in flight while
   // the current group computes).
@@ -145,8 +189,8 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
 
   const v16i zero16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-  // Write the prefetched group into LDS stage `st`.
-#define BQMM_STAGE(st)                                                                                   \
+  // Write the prefetched group into LDS stage `st`, for band pass `pass`.
+#define BQMM_STAGE(st, pass)                                                                                 \
   do {                                                                                                   \
     uint8_t *a_lds = lds + (st) * kStageBytes;                                                           \
     uint8_t *w_lds = a_lds + kActBytes;                                                                  \
@@ -164,35 +208,48 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
       }                                                                                                  \
     }                                                                                                    \
     if (tid < BN) {                                                                                      \
-      dw_lds[tid] = f16_bits_to_f32(rs16);                                                               \
+      dw_lds[tid] = ldexpf(f16_bits_to_f32(rs16), -7 * (int)(pass));                                     \
     } else if (s_stager) {                                                                               \
-      const int e = rowexp[tid - BN];                                                                    \
-      int4 mu;                                                                                           \
-      mu.x = (int)rintf(ldexpf(f16_bits_to_f32(rds.x & 0xFFFFu), 30 - e));                               \
-      mu.y = (int)rintf(ldexpf(f16_bits_to_f32(rds.y & 0xFFFFu), 30 - e));                               \
-      mu.z = (int)rintf(ldexpf(f16_bits_to_f32(rds.z & 0xFFFFu), 30 - e));                               \
-      mu.w = (int)rintf(ldexpf(f16_bits_to_f32(rds.w & 0xFFFFu), 30 - e));                               \
+      const int ep = mmq_rowexp[tid - BN] - 7 * (int)(pass);                                             \
+      const int4 mu = make_int4(band_mu(rds.x, ep), band_mu(rds.y, ep), band_mu(rds.z, ep),              \
+                                band_mu(rds.w, ep));                                                     \
       *reinterpret_cast<int4 *>(mu_lds + (tid - BN) * 4) = mu;                                           \
     }                                                                                                    \
   } while (0)
 
+  // Group stream: step t computes group t % ngroups of pass t / ngroups (one
+  // pass for a tile of ordinary rows).  (g, p) is the group and pass of step
+  // t, (g1, p1) of step t + 1, (g2, p2) of step t + 2, advanced without
+  // division.
+  const uint32_t passes = kDump ? 1u : __builtin_amdgcn_readfirstlane(mmq_passes);
+  const uint32_t nsteps = ngroups * passes;
+  uint32_t g = 0, g1 = 0, p1 = 0, g2 = 0, p2 = 0;
+  auto next = [ngroups](uint32_t &gg, uint32_t &pp) {
+    if (++gg == ngroups) {
+      gg = 0;
+      ++pp;
+    }
+  };
+  next(g1, p1);
+  g2 = g1;
+  p2 = p1;
+  next(g2, p2);
   BQMM_FETCH(0u);
-  __syncthreads();  // rowexp visible
-  BQMM_STAGE(0);
-  if (ngroups > 1) BQMM_FETCH(1u);
-  // Loop body: one barrier, then stage group g + 1 into the other LDS stage and
-  // start the loads of group g + 2, then compute group g.  The barrier both
-  // publishes stage g and guarantees that every wave has finished reading the
-  // stage about to be overwritten (it held group g - 1).  The compute is last
+  BQMM_STAGE(0, 0u);
+  if (nsteps > 1) BQMM_FETCH(g1);
+  // Loop body: one barrier, then stage step t + 1 into the other LDS stage and
+  // start the loads of step t + 2, then compute step t.  The barrier both
+  // publishes stage t and guarantees that every wave has finished reading the
+  // stage about to be overwritten (it held step t - 1).  The compute is last
   // in the body: placed before a barrier, its epilogue gets sunk below it and
   // all MFMA results of a group stay alive across the barrier.
-  for (uint32_t g = 0; g < ngroups; ++g) {
+  for (uint32_t t = 0; t < nsteps; ++t, g = g1, g1 = g2, p1 = p2, next(g2, p2)) {
     __syncthreads();
-    if (g + 1 < ngroups) {
-      BQMM_STAGE((g + 1) & 1u);
-      if (g + 2 < ngroups) BQMM_FETCH(g + 2);
+    if (t + 1 < nsteps) {
+      BQMM_STAGE((t + 1) & 1u, p1);
+      if (t + 2 < nsteps) BQMM_FETCH(g2);
     }
-    const uint8_t *a_lds = lds + (g & 1u) * kStageBytes;
+    const uint8_t *a_lds = lds + (t & 1u) * kStageBytes;
     const uint8_t *w_lds = a_lds + kActBytes;
     const float *dw_lds = reinterpret_cast<const float *>(w_lds + kWBytes);
     const int *mu_lds = reinterpret_cast<const int *>(dw_lds + BN);
@@ -286,7 +343,7 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
     for (int sm = 0; sm < TM; ++sm) {
       const uint32_t mloc = wm * (32 * TM) + sm * 32 + l32;
       const uint32_t mm = m_base + mloc;
-      const float scale = ldexpf(1.0f, rowexp[mloc] - 30);
+      const float scale = ldexpf(1.0f, mmq_rowexp[mloc] - 30);
       uint16_t *orow = out + (uint64_t)min(mm, m - 1u) * ldc;
 #pragma unroll
       for (int sn = 0; sn < TN; ++sn)

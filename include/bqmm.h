@@ -6,9 +6,10 @@
  * means the legacy default stream.  Every call enqueues its kernels on that
  * stream and returns without synchronizing: errors raised while the kernels
  * run surface at the caller's next synchronization.  No call allocates or
- * frees device memory or synchronizes; all buffers belong to the caller (the reference
- * dispatcher passes its scratch and q8_1 buffers in and "allocates nothing":
- * page layers/qwen3_ssm/init_q2.rs, fn qkvz_q2_prefill_gemm).
+ * frees device memory or synchronizes; all buffers belong to the caller (the
+ * reference dispatcher takes its scratch and q8_1 buffers from its caller
+ * rather than allocating them: page layers/qwen3_ssm/init_q2.rs, fn
+ * qkvz_q2_prefill_gemm).
  *
  * Errors are values, never aborts (the reference returns an error carrying a
  * message when a kernel or weight is missing: page
@@ -153,7 +154,15 @@ int q2_0_gemv_vec(const void *act_bf16, const void *w_q2, void *out_bf16,
 /* Q2_0 GEMV for m = 1..8 rows (small verify batches): act [m][k] bf16,
  * out [m][n] bf16.  [page layers/dense_ffn_decode_batch.rs, fn forward_km_q2:
  *  q2_0_gemv_vec_batchm(inp, w, out, m).]  m > 8 -> BQ_EUNSUPPORTED.
- * Group 128; k % 128 == 0. */
+ * Group 128; k % 128 == 0.
+ * Kernels: m = 1..3 run on the vector ALU only (packed bf16 dot products, no
+ * matrix cores).  From m = 4 on, where the per-code multiply-adds outweigh
+ * the code unpacking, the products run on bf16 matrix cores
+ * (v_mfma_f32_16x16x32_bf16, codes and activations exact in bf16, fp32
+ * accumulation): a deliberate exception to keeping the GEMV a pure
+ * bandwidth kernel, taken because it measured faster at these m.  Where the
+ * matrix-core kernel's staged weight scales would exceed 64 KB of LDS in the
+ * fused gate/up launch (k above 43008), both calls use the vector kernel. */
 int q2_0_gemv_vec_batchm(const void *act_bf16, const void *w_q2, void *out_bf16,
                          uint32_t m, uint32_t n, uint32_t k, void *stream);
 

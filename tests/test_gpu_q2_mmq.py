@@ -8,7 +8,7 @@ import torch
 import inputs
 import oracle
 import bit_quantized_matmul_quantize_amd as bq
-from parity_helpers import ROW_TOL, dev_bf16, dev_u8, empty_bf16, host_f64, rounded_row_ok, row_error
+from parity_helpers import ROW_TOL, dev_bf16, dev_u8, empty_bf16, host_f64, rows_ok, row_error
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def test_ragged_shapes(gpu, m, n, k, seed):
     q8, q8d = _q8_dev(gpu, act, m, k)
     wd = dev_u8(w, gpu)
     R = oracle.q2_0_mmq(q8, w, m, n, k)
-    assert rounded_row_ok(_mmq(gpu, q8d, wd, m, n, k), R)
+    assert rows_ok(_mmq(gpu, q8d, wd, m, n, k), R)
     mt, nt = min(m, 40), min(n, 70)
     m0, n0 = m - mt, n - nt
     D = _dots(gpu, q8d, wd, m0, mt, n0, nt, m, n, k)
@@ -119,7 +119,7 @@ def test_large_grid_ragged(gpu):
     y = _mmq(gpu, q8d, dev_u8(w, gpu), m, n, k)
     rows = np.array([0, 127, 128, 700, 1023, 1024, 1029])
     R = oracle.q2_0_mmq(_rows_sel(q8, m, k, rows), w, len(rows), n, k)
-    assert rounded_row_ok(y[rows], R)
+    assert rows_ok(y[rows], R)
 
 
 def _w_rows(w, n, k, r0, rt):
@@ -186,3 +186,80 @@ def test_strided_output(gpu, m, n, k, ldc, off, seed):
     mask = torch.ones_like(big, dtype=torch.bool)
     mask[:, off:off + n] = False
     assert bool((big[mask] == -3.0).all())
+
+
+# ---- rows whose q8_1 block scales span far more than the integer fold's 2^5 ----
+
+def _wide_span_case(m, n, k, seed, spans):
+    """Activations where some rows hold one dominant block (a single value of
+    2000 in a block of zeros) and small blocks whose scales sit about 2^s
+    below it, for s in `spans`; the dominant blocks sit at block 0 (sharing a
+    128-group with small blocks) or block 4 (a group of its own), and every
+    weight row has code 2 (weight 0) under both, so those rows' products come
+    from the small blocks alone.  Other rows are ordinary N(0,1) activations
+    with outlier channels."""
+    g = inputs.rng(seed)
+    x = g.standard_normal((m, k)).astype(np.float32)
+    x[:, g.choice(k, max(1, k // 100), replace=False)] *= 20.0
+    wide_rows = []
+    r = 0
+    for s in spans:
+        for dom in (0, 4):
+            row = g.standard_normal(k).astype(np.float32) * np.float32(2000.0 * 2.0 ** -s / 2.5)
+            row[32 * dom:32 * dom + 32] = 0.0
+            row[32 * dom + 7] = 2000.0
+            x[r] = row
+            wide_rows.append(r)
+            r += 3  # spread the wide rows over the first tile, with ordinary rows between
+    act = inputs.f32_to_bf16_bits(x)
+    w = inputs.q2_0_weight(g, n, k)
+    codes = w[: n * k // 4].reshape(n, k // 4)
+    # byte t of group 0 holds k-offsets t, t+32, t+64, t+96 in bit fields 0..3:
+    # field 0 of group 0 is block 0, field 0 of group 1 is block 4
+    for grp in (0, 1):
+        b = codes[:, 32 * grp:32 * grp + 32]
+        b &= np.uint8(0xFC)
+        b |= np.uint8(0x02)
+    return act, w, np.array(wide_rows)
+
+
+@pytest.mark.parametrize("m,n,k,seed", [(130, 384, 1024, 17),     # 96 x 128 tiles, one tile with wide rows
+                                        (1030, 5500, 512, 18)])   # 128 x 128 tiles
+def test_fold_wide_block_scale_spans(gpu, m, n, k, seed):
+    act, w, wide = _wide_span_case(m, n, k, seed, spans=(6, 12, 20, 24))
+    q8, q8d = _q8_dev(gpu, act, m, k)
+    _, ds = _planes(q8, m, k)
+    d = ds[:, :, 0].copy().view(np.float16).astype(np.float64)  # block scales
+    for r in wide:  # the spans asked for are really there
+        nz = d[r][d[r] > 0]
+        assert nz.max() / nz.min() >= 2.0 ** 5
+    assert max(d[r][d[r] > 0].max() / d[r][d[r] > 0].min() for r in wide) >= 2.0 ** 20
+    y = _mmq(gpu, q8d, dev_u8(w, gpu), m, n, k)
+    rows = np.unique(np.concatenate([wide, [1, 2, 127, 128, m - 1], inputs.rng(seed).choice(m, 6, replace=False)]))
+    R = oracle.q2_0_mmq(_rows_sel(q8, m, k, rows), w, len(rows), n, k)
+    # the dominant blocks contribute nothing: every product comes from the small blocks
+    assert np.all(np.linalg.norm(R[np.isin(rows, wide)], axis=1) > 0)
+    assert row_error(y[rows], R) <= ROW_TOL
+    # the block dots of a window over the wide rows are still exact
+    D = _dots(gpu, q8d, dev_u8(w, gpu), 0, 32, n - 40, 40, m, n, k)
+    Dref = oracle.q2_0_blockdots(_rows_q8(q8, m, k, 0, 32), _w_rows(w, n, k, n - 40, 40), 32, 40, k)
+    assert np.array_equal(D, Dref)
+
+
+def _planes(q8, m, k):
+    """codes [m][kpad] (int8 bytes) and the (d, s) bit pairs [m][kpad/32][2]."""
+    kp = (k + 255) // 256 * 256
+    return q8[: m * kp].reshape(m, kp), q8[m * kp:].copy().view(np.uint16).reshape(m, kp // 32, 2)
+
+
+def test_fold_wide_span_rows_do_not_change_other_tiles(gpu):
+    # an m-tile of ordinary rows gives the same bits whether or not another
+    # tile of the same call holds wide rows (tiles fold independently)
+    m, n, k = 256, 384, 1024
+    act, w, _ = _wide_span_case(m, n, k, 19, spans=(20,))
+    plain = act.copy()
+    plain[:128] = inputs.activations(inputs.rng(20), 128, k)
+    q8a, q8ad = _q8_dev(gpu, act, m, k)
+    q8b, q8bd = _q8_dev(gpu, plain, m, k)
+    wd = dev_u8(w, gpu)
+    assert np.array_equal(_mmq(gpu, q8ad, wd, m, n, k)[128:], _mmq(gpu, q8bd, wd, m, n, k)[128:])

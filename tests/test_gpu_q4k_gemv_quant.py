@@ -9,7 +9,7 @@ import inputs
 import oracle
 import bit_quantized_matmul_quantize_amd as bq
 from parity_helpers import (ROW_TOL, bf16_ulp_distance, dev_bf16, dev_u8, empty_bf16, host_bits, host_f64,
-                            rounded_row_ok, row_error)
+                            rows_ok, row_error)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def test_gemv_edge_shapes(gpu, n, k, seed):
     a = inputs.activations(g, 1, k, outliers=True)
     y = host_f64(_gemv(gpu, a, w, n, k))
     R = oracle.q4k_gemv(a, w, 1, n, k)[0]
-    assert rounded_row_ok(y, R)
+    assert rows_ok(y, R)
 
 
 def test_gemv_zero_activations(gpu):
@@ -138,3 +138,28 @@ def test_quantize_then_gemv(gpu):
     bq.q4k_gemv_vec(dev_bf16(a, gpu), wq, out, n, k)
     R = oracle.q4k_gemv(a, w_ref, 1, n, k)[0]
     assert row_error(host_f64(out), R) <= ROW_TOL
+
+
+def test_quantize_near_ties(gpu):
+    """Super-blocks whose sub-scale, sub-min and code quotients sit exactly on
+    halves (the CPU pin's tie block, scaled by powers of two so the ties stay
+    exact) and copies with about a third of their nonzero values moved one
+    bf16 step up or down (quotients just off the halves): the device bytes
+    equal the oracle's."""
+    from test_oracle_q4k_gemv_quant import _tie_block
+    tie_bits, _ = _tie_block()
+    tie = inputs.bf16_bits_to_f32(tie_bits)
+    g = inputs.rng(129)
+    blocks = []
+    for s in range(-1, 15):  # d = 2^(s - 13): binary16 normal throughout
+        exact = inputs.f32_to_bf16_bits(tie * np.float32(2.0 ** s))
+        blocks.append(exact)
+        for _ in range(3):
+            pick = (g.random(256) < 0.3) & ((exact & 0x7FFF) != 0)
+            step = g.choice(np.array([-1, 1], np.int32), size=256)
+            blocks.append(np.where(pick, (exact.astype(np.int32) + step).astype(np.uint16), exact))
+    n, k = len(blocks) // 4, 1024  # 16 rows of 4 super-blocks
+    x = np.stack(blocks).reshape(n, k)
+    ref, flagged = oracle.quantize_weight_q4k(x, n, k)
+    assert flagged == 0
+    assert np.array_equal(_quantize(gpu, x, n, k), ref)

@@ -154,3 +154,96 @@ def test_quantize_range_flag():
     x[1, 300] = 3.0e38                              # d overflows binary16
     _, f = oracle.quantize_weight_q4k(_bf16(x), 2, 512)
     assert f == 2
+
+
+# --- the quantizer's rounding of exact ties ----------------------------------
+
+def _round_half_away(q):
+    """Nearest integer to the Fraction q, halves away from zero."""
+    from fractions import Fraction
+    f = q.numerator // q.denominator
+    r = q - f
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and q > 0):
+        return f + 1
+    if r == Fraction(1, 2) and q < 0:
+        return f
+    return f if r < Fraction(1, 2) else f + 1
+
+
+def _round_half_even(q):
+    from fractions import Fraction
+    f = q.numerator // q.denominator
+    r = q - f
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and f % 2 == 1):
+        return f + 1
+    return f
+
+
+def _tie_block():
+    """A super-block whose sub-scale, sub-min and code quotients land exactly
+    on halves, with every value and intermediate exact (values in units of
+    u = 2^-13, all with <= 8 significant bits, so exact in bf16; d and dmin
+    come out as u exactly).  Returns (bf16 bits [256], the sub-blocks' values
+    as Fractions in units of u, the number of exact ties)."""
+    from fractions import Fraction as F
+    h = F(1, 2)
+    # per sub-block: the values in units of u (the extremes first)
+    sub = [
+        [F(-49), F(896), F(0), F(448)],          # S = 63u, M = 49u: sets d = u
+        [F(-63), F(57), F(-43), F(-27), F(-11), F(-59), F(53)],  # M = 63u sets dmin = u; sc = 8,
+                                                 # codes (x + 63) / 8 = 2.5, 4.5, 6.5, 0.5, 14.5
+        [F(0), F(255) * h, F(45) * h, F(9)],     # S = 8.5u -> sc = 9 (tie); codes 2.5 and 1
+        [F(-21) * h, F(129) * h, F(0)],          # M = 10.5u -> m = 11 (tie); S = 5u
+        [F(-105) * h, F(255), F(0)],             # S = 20.5u -> sc = 21, M = 52.5u -> m = 53 (both ties)
+        [F(0), F(60), F(30)],                    # S = 4u, codes 15 and 7.5 -> 8 (tie)
+        [F(-5), F(25), F(1)],                    # S = 2u, M = 5u: codes (1 + 5) / 2 = 3
+        [F(0)],                                  # a zero sub-block
+    ]
+    vals = []
+    for j, v in enumerate(sub):
+        vals.append((v + [v[-1]] * 32)[:32])
+    x = np.array([float(v) * 2.0 ** -13 for blk in vals for v in blk], np.float64)
+    bits = inputs.f32_to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(inputs.bf16_bits_to_f32(bits).astype(np.float64), x)  # exact in bf16
+    return bits, vals
+
+
+def _expected_tie_bytes(vals, rnd):
+    """The quantizer's rule in exact rationals (units of u) with rounding rnd."""
+    from fractions import Fraction as F
+    lo = [min(F(0), min(v)) for v in vals]
+    hi = [max(l, max(v)) for l, v in zip(lo, vals)]
+    S = [(h - l) / 15 for h, l in zip(hi, lo)]
+    M = [-l for l in lo]
+    d, dmin = max(S) / 63, max(M) / 63
+    assert d == 1 and dmin == 1  # both exactly u, so fp16(u) = u
+    sc = [min(63, rnd(s / d)) for s in S]
+    mn = [min(63, rnd(m_ / dmin)) for m_ in M]
+    codes, ties = [], 0
+    for j, v in enumerate(vals):
+        for x in v:
+            step = d * sc[j]
+            q = 0 if step == 0 else max(0, min(15, rnd((x + dmin * mn[j]) / step)))
+            if step != 0 and ((x + dmin * mn[j]) / step).denominator == 2:
+                ties += 1
+            codes.append(q)
+    ties += sum(1 for s in S if (s / d).denominator == 2) + sum(1 for m_ in M if (m_ / dmin).denominator == 2)
+    return q4k_pack.pack_block(2.0 ** -13, 2.0 ** -13, sc, mn, np.array(codes)), ties
+
+
+def test_quantize_ties_away_from_zero():
+    # exact halves in S_j/d, M_j/dmin and the code quotients round away from
+    # zero (roundf), as the quantizer's reading fixes; the same block under
+    # ties-to-even gives other bytes, so the pin tells the two rules apart
+    bits, vals = _tie_block()
+    expect, ties = _expected_tie_bytes(vals, _round_half_away)
+    other, _ = _expected_tie_bytes(vals, _round_half_even)
+    assert ties >= 40
+    assert not np.array_equal(expect, other)
+    got, flagged = oracle.quantize_weight_q4k(bits, 1, 256)
+    assert flagged == 0
+    assert np.array_equal(got, expect)
+    # the sub-scale and sub-min ties themselves: sc_2 = 9 (8.5), m_3 = 11 (10.5),
+    # sc_4 = 21 (20.5), m_4 = 53 (52.5; a j >= 4 sub-block, so its high bits too)
+    _, _, sc, mn = q4k_pack.fields(got, 1, 256)
+    assert sc[0, 0, 2] == 9 and mn[0, 0, 3] == 11 and sc[0, 0, 4] == 21 and mn[0, 0, 4] == 53

@@ -39,6 +39,7 @@ EXPORTS = {
     "dequant_q2_0_to_bf16": (_I, [_P, _P, _U32, _U32, _U32, _P]),
     "dense_gemm_bf16": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
     "q2_0_prefill_gemm": (_I, [_P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _I, _P]),
+    "q2_0_prefill_gemm_noalloc": (_I, [_P, _P, _P, _U32, _U32, _U32, _U32, _I, _P]),
     "q4k_mmq_gemm": (_I, [_P, _P, _P, _U32, _U32, _U32, _P]),
     "q4k_gemv_vec": (_I, [_P, _P, _P, _U32, _U32, _P]),
     "quantize_weight_q4k": (_I, [_P, _P, _U32, _U32, _P]),
@@ -249,6 +250,15 @@ def q2_0_prefill_gemm(act, w_q2, out, scratch, act_q8, m: int, n: int, k: int, g
         _need(scratch, _bf(n, k), "scratch")
     _check(lib().q2_0_prefill_gemm(*_ptrs(act, w_q2, out, scratch, act_q8), m, n, k, group,
                                    int(bool(use_mmq)), _stream(stream)))
+
+
+def q2_0_prefill_gemm_noalloc(act, w_q2, out, m: int, n: int, k: int, group: int = 128,
+                              use_mmq: bool = True, stream=None):
+    _need(_bf16(act, "act"), _bf(m, k), "act")
+    _need(_u8(w_q2, "w_q2"), q2_0_weight_bytes(n, k, group), "w_q2")
+    _need(_bf16(out, "out"), _bf(m, n), "out")
+    _check(lib().q2_0_prefill_gemm_noalloc(*_ptrs(act, w_q2, out), m, n, k, group, int(bool(use_mmq)),
+                                           _stream(stream)))
 
 
 def q4k_mmq_gemm(act_q8, w_q4k, out, m: int, n: int, k: int, stream=None):

@@ -325,39 +325,134 @@ int dense_gemm_bf16(const void *a_bf16, const void *w_bf16, void *out_bf16, uint
                     "dense_gemm_bf16");
 }
 
-int q2_0_prefill_gemm(const void *act_bf16, const void *w_q2, void *out_bf16, void *scratch_bf16,
-                      void *act_q8, uint32_t m, uint32_t n, uint32_t k, uint32_t group, int use_mmq,
-                      void *stream) {
-  REQUIRE(act_bf16 && w_q2 && out_bf16, BQ_EINVAL, "q2_0_prefill_gemm: null input, weight or output");
-  if (use_mmq && group == 128u) {
-    REQUIRE(act_q8, BQ_EINVAL, "q2_0_prefill_gemm: MMQ branch needs the act_q8 buffer");
-    REQUIRE(m >= 1 && k >= 1, BQ_EINVAL, "q2_0_prefill_gemm: m=%u k=%u must be >= 1", m, k);
-    REQUIRE(aligned16(act_bf16), BQ_EALIGN, "q2_0_prefill_gemm: input must be 16-byte aligned");
-    int st = check_mmq("q2_0_prefill_gemm", act_q8, w_q2, out_bf16, m, n, k, 128u);
+// Checks of the prefill dispatcher's arguments; the branch's workspace
+// (act_q8 for MMQ, scratch_bf16 for the dequant branch) must be given.
+static int check_prefill(const char *name, const void *act_bf16, const void *w_q2, const void *out_bf16,
+                         const void *scratch_bf16, const void *act_q8, uint32_t m, uint32_t n, uint32_t k,
+                         uint32_t group, bool mmq) {
+  REQUIRE(act_bf16 && w_q2 && out_bf16, BQ_EINVAL, "%s: null input, weight or output", name);
+  if (mmq) {
+    REQUIRE(act_q8, BQ_EINVAL, "%s: MMQ branch needs the act_q8 buffer", name);
+    REQUIRE(m >= 1 && k >= 1, BQ_EINVAL, "%s: m=%u k=%u must be >= 1", name, m, k);
+    REQUIRE(aligned16(act_bf16), BQ_EALIGN, "%s: input must be 16-byte aligned", name);
+    const int st = check_mmq(name, act_q8, w_q2, out_bf16, m, n, k, 128u);
     if (st != BQ_OK) return st;
-    REQUIRE_DISJOINT("q2_0_prefill_gemm", act_q8, q8_bytes(m, k), act_bf16, bf16_bytes(m, k), "the input");
-    REQUIRE_DISJOINT("q2_0_prefill_gemm", act_q8, q8_bytes(m, k), w_q2, q2_bytes(n, k), "the weight");
-    st = hip_status(bqmm::launch_quantize_act_q8_1(act_bf16, act_q8, m, k, as_stream(stream)),
-                    "q2_0_prefill_gemm (quantize)");
-    if (st != BQ_OK) return st;
-    return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, out_bf16, nullptr, 0, 0, 0, 0, m, n, k, n,
-                                            as_stream(stream)),
-                      "q2_0_prefill_gemm (mmq)");
+    REQUIRE_DISJOINT(name, act_q8, q8_bytes(m, k), act_bf16, bf16_bytes(m, k), "the input");
+    REQUIRE_DISJOINT(name, act_q8, q8_bytes(m, k), w_q2, q2_bytes(n, k), "the weight");
+    return BQ_OK;
   }
-  REQUIRE(scratch_bf16, BQ_EINVAL, "q2_0_prefill_gemm: dequant branch needs the bf16 scratch buffer");
+  REQUIRE(scratch_bf16, BQ_EINVAL, "%s: dequant branch needs the bf16 scratch buffer", name);
   int st = check_dequant(w_q2, scratch_bf16, n, k, group);
   if (st != BQ_OK) return st;
   st = check_dense(act_bf16, scratch_bf16, out_bf16, m, n, k);
   if (st != BQ_OK) return st;
-  REQUIRE_DISJOINT("q2_0_prefill_gemm", scratch_bf16, bf16_bytes(n, k), act_bf16, bf16_bytes(m, k), "the input");
-  REQUIRE_DISJOINT("q2_0_prefill_gemm", out_bf16, bf16_bytes(m, n), w_q2,
+  REQUIRE_DISJOINT(name, scratch_bf16, bf16_bytes(n, k), act_bf16, bf16_bytes(m, k), "the input");
+  REQUIRE_DISJOINT(name, out_bf16, bf16_bytes(m, n), w_q2,
                    (uint64_t)n * k / 4u + 2u * (uint64_t)n * (k / group), "the weight");
-  st = hip_status(bqmm::launch_dequant_q2_0(w_q2, scratch_bf16, n, k, group, as_stream(stream)),
-                  "q2_0_prefill_gemm (dequant)");
+  return BQ_OK;
+}
+
+// The prefill dispatcher's launches, after check_prefill.
+static int launch_prefill(const char *name, const void *act_bf16, const void *w_q2, void *out_bf16,
+                          void *scratch_bf16, void *act_q8, uint32_t m, uint32_t n, uint32_t k, uint32_t group,
+                          bool mmq, hipStream_t s) {
+  char what[96];
+  if (mmq) {
+    std::snprintf(what, sizeof(what), "%s (quantize)", name);
+    const int st = hip_status(bqmm::launch_quantize_act_q8_1(act_bf16, act_q8, m, k, s), what);
+    if (st != BQ_OK) return st;
+    std::snprintf(what, sizeof(what), "%s (mmq)", name);
+    return hip_status(bqmm::launch_q2_0_mmq(act_q8, w_q2, out_bf16, nullptr, 0, 0, 0, 0, m, n, k, n, s), what);
+  }
+  std::snprintf(what, sizeof(what), "%s (dequant)", name);
+  const int st = hip_status(bqmm::launch_dequant_q2_0(w_q2, scratch_bf16, n, k, group, s), what);
   if (st != BQ_OK) return st;
-  return hip_status(bqmm::launch_dense_gemm_bf16(act_bf16, scratch_bf16, out_bf16, m, n, k,
-                                                 as_stream(stream)),
-                    "q2_0_prefill_gemm (dense gemm)");
+  std::snprintf(what, sizeof(what), "%s (dense gemm)", name);
+  return hip_status(bqmm::launch_dense_gemm_bf16(act_bf16, scratch_bf16, out_bf16, m, n, k, s), what);
+}
+
+int q2_0_prefill_gemm(const void *act_bf16, const void *w_q2, void *out_bf16, void *scratch_bf16,
+                      void *act_q8, uint32_t m, uint32_t n, uint32_t k, uint32_t group, int use_mmq,
+                      void *stream) {
+  const bool mmq = use_mmq && group == 128u;
+  const int st = check_prefill("q2_0_prefill_gemm", act_bf16, w_q2, out_bf16, scratch_bf16, act_q8, m, n, k,
+                               group, mmq);
+  if (st != BQ_OK) return st;
+  return launch_prefill("q2_0_prefill_gemm", act_bf16, w_q2, out_bf16, scratch_bf16, act_q8, m, n, k, group,
+                        mmq, as_stream(stream));
+}
+
+}  // extern "C"
+
+// ---- the prefill dispatcher without a workspace argument ------------------
+//
+// Its workspace is this file-scope device array: every GPU the library runs
+// on holds one copy, allocated when the library's code object is loaded there
+// and kept until the process ends.  In host code the name `scratch` stands
+// for the host-side shadow of the variable, not a device address; the
+// device address is looked up once per device (scratch_address) and only
+// that address is ever handed to kernels.
+namespace {
+
+constexpr uint64_t kScratchBytes = 64ull << 20;
+constexpr uintptr_t kScratchAlign = 256;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up with that
+// device current on its first use and remembered per device.
+hipError_t scratch_address(void **ptr) {
+  static std::mutex mu;
+  static std::vector<std::pair<int, void *>> known;  // device, address
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto &p : known)
+    if (p.first == dev) {
+      *ptr = p.second;
+      return hipSuccess;
+    }
+  void *addr = nullptr;
+  e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (addr == nullptr) return hipErrorInvalidSymbol;
+  known.emplace_back(dev, addr);
+  *ptr = addr;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q2_0_prefill_gemm_noalloc(const void *act_bf16, const void *w_q2, void *out_bf16, uint32_t m, uint32_t n,
+                              uint32_t k, uint32_t group, int use_mmq, void *stream) {
+  const char *name = "q2_0_prefill_gemm_noalloc";
+  const bool mmq = use_mmq && group == 128u;
+  // The workspace the branch needs must fit the array.  The shared argument
+  // checks then run with a stand-in workspace address (non-null, aligned,
+  // below every caller buffer) so that, as for every call, a rejected call
+  // makes no HIP call; the array's real address is looked up after them.
+  const uint64_t need = mmq ? q8_bytes(m, k) : bf16_bytes(n, k);
+  REQUIRE(need <= kScratchBytes, BQ_EUNSUPPORTED,
+          "%s: the %s needs %llu bytes of workspace, more than the %llu this entry point holds "
+          "(use q2_0_prefill_gemm with a caller buffer)",
+          name, mmq ? "q8_1 activation buffer" : "bf16 dequant buffer", (unsigned long long)need,
+          (unsigned long long)kScratchBytes);
+  void *const stand_in = reinterpret_cast<void *>(uintptr_t{kScratchAlign});
+  int st = check_prefill(name, act_bf16, w_q2, out_bf16, mmq ? nullptr : stand_in, mmq ? stand_in : nullptr,
+                         m, n, k, group, mmq);
+  if (st != BQ_OK) return st;
+  void *ws = nullptr;
+  st = hip_status(scratch_address(&ws), "q2_0_prefill_gemm_noalloc (workspace address)");
+  if (st != BQ_OK) return st;
+  return launch_prefill(name, act_bf16, w_q2, out_bf16, mmq ? nullptr : ws, mmq ? ws : nullptr, m, n, k, group,
+                        mmq, as_stream(stream));
 }
 
 int silu_mul_bf16(const void *gate, const void *up, void *out, uint64_t count, void *stream) {

@@ -204,6 +204,23 @@ int q2_0_prefill_gemm(const void *act_bf16, const void *w_q2, void *out_bf16,
                       void *scratch_bf16, void *act_q8, uint32_t m, uint32_t n, uint32_t k,
                       uint32_t group, int use_mmq, void *stream);
 
+/* The prefill dispatcher for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same branches, kernels and results as q2_0_prefill_gemm, with the branch's
+ * workspace (the q8_1 buffer, or the bf16 dequant buffer) taken from a
+ * 64 MiB device array the library holds on every GPU it runs on, from the
+ * code object's load until the process ends.  The call itself allocates
+ * nothing.  Limits: the MMQ branch needs q8_1_act_bytes(m, k) <= 64 MiB
+ * (m * kpad <= 59,652,323, e.g. m = 4096 at k = 14336), the dequant branch
+ * n * k * 2 <= 64 MiB (n * k <= 33,554,432); larger shapes return
+ * BQ_EUNSUPPORTED before any HIP call.  Every call on a GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (two streams, or two
+ * host threads) race on it and must be ordered by the caller.  The array's
+ * contents are not cleared; each branch writes every byte it reads. */
+int q2_0_prefill_gemm_noalloc(const void *act_bf16, const void *w_q2, void *out_bf16,
+                              uint32_t m, uint32_t n, uint32_t k, uint32_t group, int use_mmq,
+                              void *stream);
+
 /* Q4_K MMQ: out[m][n] (bf16) = sum_k deq(act_q8)[m][k] * deq_q4k(w)[n][k].
  * [page layers/ops/q4k_mmq.rs, fn q4k_mmq_gemm: C[m, n] = A[m, k] x W[n, k],
  *  A in q8_1, W in block_q4_K, BF16 store; any n.]  k % 256 == 0. */

@@ -92,6 +92,12 @@ def _err(bq):
     (lambda l: l.q2_0_prefill_gemm(A, B, C, None, None, 4, 4, 512, 128, 1, None), -1, "act_q8"),
     (lambda l: l.q2_0_prefill_gemm(A, B, C, None, None, 4, 4, 512, 128, 0, None), -1, "scratch"),
     (lambda l: l.q2_0_prefill_gemm(A, B, C, None, None, 4, 4, 512, 64, 1, None), -1, "scratch"),
+    (lambda l: l.q2_0_prefill_gemm_noalloc(A, B, C, 4096, 64, 16384, 128, 1, None), -2, "workspace"),
+    (lambda l: l.q2_0_prefill_gemm_noalloc(A, B, C, 4, 8192, 8192, 128, 0, None), -2, "workspace"),
+    (lambda l: l.q2_0_prefill_gemm_noalloc(None, B, C, 4, 4, 512, 128, 1, None), -1, "null"),
+    (lambda l: l.q2_0_prefill_gemm_noalloc(A, B, C, 4, 4, 500, 128, 1, None), -1, "multiple of 128"),
+    (lambda l: l.q2_0_prefill_gemm_noalloc(A, B, C, 4, 4, 480, 64, 0, None), -1, "not a multiple"),
+    (lambda l: l.q2_0_prefill_gemm_noalloc(A, B, P(0x20000 + 64), 4, 4, 512, 128, 1, None), -1, "overlaps the weight"),
     (lambda l: l.silu_mul_bf16(A, B, C, 0, None), -1, "count"),
     (lambda l: l.silu_mul_bf16(A, B, P(0x30001), 8, None), -3, "aligned"),
     (lambda l: l.q2_0_mmq_blockdots(A, B, C, 4, 1, 0, 1, 4, 256, 512, None), -1, "outside"),

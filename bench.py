@@ -7,12 +7,15 @@ input, every leg on the current stream, each leg captured once into a HIP
 graph and replayed between HIP events:
   decode   : 1000 x q2_0_gemv_vec, qkvz n=12288 k=2048 (m=1), the weight
              rotated through 80 copies (537 MB > the 256 MB Infinity Cache) so
-             that every call streams its weight from HBM;
+             that every call streams its weight from HBM; and the same calls
+             on one copy (warm, served from the Infinity Cache);
   verify   : q2_0_gemv_vec_batchm chain gate -> up -> silu_mul -> down,
              FFN [17408, 5120] / [5120, 17408], m in {2, 3, 4, 8}; and the same
              step with q2_0_gemv_gate_up_silu in place of the first three calls;
-  prefill  : quantize_act_q8_1 + q2_0_mmq_gemm, qkvz n=12288 k=2048, m in
-             {512, 2048}; and the bf16 fallback (dequant + dense GEMM) at m=512;
+             both rotated through 8 copies of the three weights (568 MB);
+  prefill  : quantize_act_q8_1 and q2_0_mmq_gemm, qkvz n=12288 k=2048, m in
+             {512, 2048}, apart and end to end; and the bf16 fallback
+             (dequant + dense GEMM) at both m;
   ffn      : m=4096 FFN prefill, Q2_0 and Q4_K: quantize, gate and up MMQ
              (sharing the quantized input), silu_mul fused into the down
              projection's quantization, down MMQ;
@@ -20,12 +23,20 @@ graph and replayed between HIP events:
              [5120, 17408] shapes, each weight rotated through 8 copies
              (401 MB); and the Q4_K weight quantizer on a bf16 [17408, 5120]
              weight (two input/output pairs alternate);
+  ceilings : what the GPU reaches on each path alone (ceilings/ceilings.hip,
+             a library of its own): an empty kernel (the launch floor, one
+             workgroup and the decode GEMV's grid), a cold streaming read of
+             the decode GEMV's 6,713,344 bytes per launch with its grid
+             (rotated through 80 buffers), back-to-back int8 MFMAs, and
+             back-to-back 24-bit integer multiply-adds on the vector ALU;
   copy     : (not in the default set) a plain 256 MiB device-to-device copy,
              the known-size reference for the HBM byte counters.
 The JSON line reports the decode GEMV (the workload the headline metric is
-quoted on) as `value`, with its roofline and the CPU oracle beside it; the
-other legs are reported under "legs".  Inputs are resident in HBM before the
-timed region starts.
+quoted on) as `value`, with its roofline (against the published peak and
+against the measured streaming ceiling) and the CPU oracle beside it; the
+m = 2048 MMQ under "prefill" the same way; every other leg under "legs" and
+the oracle's figures for the other workloads under "cpu_baselines".  Inputs
+are resident in HBM before the timed region starts.
 """
 from __future__ import annotations
 
@@ -44,10 +55,13 @@ METRIC = "Q2_0 MMQ prefill int8 TOPS + GEMV decode HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5033.0      # MI355X dense int8 MFMA, published (no sparsity)
 BF16_PEAK_TFLOPS = 2516.0    # MI355X dense bf16 MFMA, published
+VALU_PEAK_GINSTR = 256 * 4 * 2.4e9 / 4 / 1e9  # wave64 VALU instructions/s: 4 SIMDs/CU, 4 cycles each
 
 DECODE_CALLS = 1000
 DECODE_COPIES = 80
+VERIFY_COPIES = 8
 COPY_BYTES = 256 << 20
+DECODE_BYTES = 12288 * 2048 * 17 // 64 + 2 * 2048 + 2 * 12288  # 6,713,344
 # Per-dispatch HBM traffic of the decode GEMV and of the m = 2048 MMQ, measured
 # with rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled by the same counters
 # on the copy leg).  A figure is reported only while the kernel source still
@@ -65,9 +79,9 @@ def parse():
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="target CPU time of the oracle sample")
-    p.add_argument("--legs", default="decode,verify,prefill,ffn,q4k")
+    p.add_argument("--cpu-seconds", type=float, default=24.0,
+                   help="target CPU time of all the oracle samples together")
+    p.add_argument("--legs", default="decode,verify,prefill,ffn,q4k,ceilings")
     return p.parse_args()
 
 
@@ -83,7 +97,7 @@ class Leg:
     later capture begins, so a tensor without a live reference would be
     unmapped under an earlier graph."""
 
-    def __init__(self, name, fn, keep, launches, work, unit, kernel, peak, bound, min_ms=2.0):
+    def __init__(self, name, fn, keep, launches, work, unit, kernel, peak, bound, min_ms=2.0, peak_unit=None):
         import torch
         self.name, self.fn, self.keep = name, fn, list(keep)
         self.unit, self.kernel, self.peak, self.bound = unit, kernel, peak, bound
@@ -133,15 +147,31 @@ class Leg:
         ms = float(np.mean(self.ms))
         per_launch_us = ms * 1e3 / self.launches
         rate = self.work / (ms * 1e-3)  # units per second
-        scale = 1e9 if self.unit == "GB/s" else 1e12
+        scale = {"GB/s": 1e9, "TOPS": 1e12, "Ginstr/s": 1e9, "launches/s": 1.0}[self.unit]
         achieved = rate / scale
-        return dict(name=self.name, ms=round(ms, 4), reps=self.reps, us_per_launch=round(per_launch_us, 3),
-                    value=round(achieved, 2), unit=self.unit, kernel=self.kernel,
-                    frac_of_peak=round(achieved / self.peak, 4), bound=self.bound)
+        out = dict(name=self.name, ms=round(ms, 4), reps=self.reps, us_per_launch=round(per_launch_us, 3),
+                   value=round(achieved, 2), unit=self.unit, kernel=self.kernel, bound=self.bound)
+        if self.peak:
+            out["frac_of_peak"] = round(achieved / self.peak, 4)
+        return out
 
 
-def decode_leg(bq, dev, d):
-    """1000 m=1 GEMV calls, weight rotated through DECODE_COPIES copies."""
+class Rotation:
+    """Cycles through weight copies, one per call at capture time, so a graph
+    of many calls reads every copy in turn."""
+
+    def __init__(self, copies):
+        self.copies, self.i = copies, 0
+
+    def next(self):
+        c = self.copies[self.i % len(self.copies)]
+        self.i += 1
+        return c
+
+
+def decode_legs(bq, dev, d):
+    """1000 m=1 GEMV calls: weight rotated through DECODE_COPIES copies (cold)
+    and on one copy (warm)."""
     import torch
     n, k = d["n"], d["k"]
     w0 = torch.from_numpy(d["w"]).to(dev)
@@ -149,54 +179,64 @@ def decode_leg(bq, dev, d):
     x = torch.from_numpy(d["act"][0].copy().view(np.int16)).to(dev).view(torch.bfloat16)
     y = torch.empty((n,), dtype=torch.bfloat16, device=dev)
 
-    def fn():
+    def cold():
         for i in range(DECODE_CALLS):
             bq.q2_0_gemv_vec(x, wcopies[i % DECODE_COPIES], y, n, k)
 
+    def warm():
+        for _ in range(DECODE_CALLS):
+            bq.q2_0_gemv_vec(x, w0, y, n, k)
+
     bytes_per_call = w0.numel() + 2 * k + 2 * n
-    leg = Leg("decode_gemv_m1", fn, wcopies + [x, y], DECODE_CALLS, DECODE_CALLS * bytes_per_call, "GB/s",
-              "q2_0_gemv1_kernel", HBM_PEAK_GBS, "hbm")
-    return leg, bytes_per_call
+    assert bytes_per_call == DECODE_BYTES
+    return [Leg("decode_gemv_m1", cold, wcopies + [x, y], DECODE_CALLS, DECODE_CALLS * bytes_per_call, "GB/s",
+                "q2_0_gemv1_kernel", HBM_PEAK_GBS, "hbm"),
+            Leg("decode_gemv_m1_warm", warm, [w0, x, y], DECODE_CALLS, DECODE_CALLS * bytes_per_call, "GB/s",
+                "q2_0_gemv1_kernel (one weight copy, Infinity Cache)", HBM_PEAK_GBS, "hbm")]
 
 
-def verify_leg(bq, dev, W, act, m, H, I):
+def verify_leg(bq, dev, Wcopies, act, m, H, I):
     import torch
-    wg, wu, wd = W
     x = torch.from_numpy(np.ascontiguousarray(act[:m]).view(np.int16)).to(dev).view(torch.bfloat16)
     g_ = torch.empty((m, I), dtype=torch.bfloat16, device=dev)
     u_ = torch.empty((m, I), dtype=torch.bfloat16, device=dev)
     o_ = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
+    rot = Rotation(Wcopies)
 
     def fn():
+        wg, wu, wd = rot.next()
         bq.q2_0_gemv_vec_batchm(x, wg, g_, m, I, H)
         bq.q2_0_gemv_vec_batchm(x, wu, u_, m, I, H)
         bq.silu_mul_bf16(g_, u_, g_, m * I)
         bq.q2_0_gemv_vec_batchm(g_, wd, o_, m, H, I)
 
+    wg, wu, wd = Wcopies[0]
     work = wg.numel() + wu.numel() + wd.numel() + m * (6 * H + 12 * I)
     kname = (f"q2_0_gemv_mfma_kernel<{m}> x3 + silu_mul" if m >= 4 else
              f"q2_0_gemvp_kernel<{m}> gate, up + silu_mul + q2_0_gemvm_kernel<{m}> down")
-    return Leg(f"verify_ffn_m{m}", fn, [wg, wu, wd, x, g_, u_, o_], 4, work, "GB/s",
-               kname, HBM_PEAK_GBS, "hbm")
+    keep = [t for c in Wcopies for t in c] + [x, g_, u_, o_]
+    return Leg(f"verify_ffn_m{m}", fn, keep, 4, work, "GB/s", kname, HBM_PEAK_GBS, "hbm")
 
 
-def verify_fused_leg(bq, dev, W, act, m, H, I):
+def verify_fused_leg(bq, dev, Wcopies, act, m, H, I):
     """The same FFN step with gate, up and silu_mul fused into one launch."""
     import torch
-    wg, wu, wd = W
     x = torch.from_numpy(np.ascontiguousarray(act[:m]).view(np.int16)).to(dev).view(torch.bfloat16)
     h_ = torch.empty((m, I), dtype=torch.bfloat16, device=dev)
     o_ = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
+    rot = Rotation(Wcopies)
 
     def fn():
+        wg, wu, wd = rot.next()
         bq.q2_0_gemv_gate_up_silu(x, wg, wu, h_, m, I, H)
         bq.q2_0_gemv_vec_batchm(h_, wd, o_, m, H, I)
 
+    wg, wu, wd = Wcopies[0]
     work = wg.numel() + wu.numel() + wd.numel() + m * (2 * H + 4 * I)
     kname = (f"q2_0_gemv_mfma_kernel<{m}> gate+up+silu, q2_0_gemv_mfma_kernel<{m}> down" if m >= 4 else
              f"q2_0_gemvp_kernel<{m}> gate+up+silu, q2_0_gemvm_kernel<{m}> down")
-    return Leg(f"verify_ffn_fused_m{m}", fn, [wg, wu, wd, x, h_, o_], 2, work, "GB/s",
-               kname, HBM_PEAK_GBS, "hbm")
+    keep = [t for c in Wcopies for t in c] + [x, h_, o_]
+    return Leg(f"verify_ffn_fused_m{m}", fn, keep, 2, work, "GB/s", kname, HBM_PEAK_GBS, "hbm")
 
 
 def copy_leg(dev):
@@ -228,26 +268,29 @@ def prefill_legs(bq, dev, p):
     import torch
     n, k = p["n"], p["k"]
     w = torch.from_numpy(p["w"]).to(dev)
+    scratch = torch.empty((n * k,), dtype=torch.bfloat16, device=dev)
+    bq.dequant_q2_0_to_bf16(w, scratch, n, k, 128)  # the dense GEMM legs read the dequantized weight
     legs = []
     for m in (512, 2048):
         x = torch.from_numpy(np.ascontiguousarray(p["act"][:m]).view(np.int16)).to(dev).view(torch.bfloat16)
         q8 = torch.empty((bq.q8_1_act_bytes(m, k),), dtype=torch.uint8, device=dev)
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         bq.quantize_act_q8_1(x, q8, m, k)
+        keep = [w, x, q8, y]
         legs.append(Leg(f"prefill_mmq_m{m}", lambda m=m, q8=q8, y=y: bq.q2_0_mmq_gemm(q8, w, y, m, n, k),
-                        [w, q8, y], 1, 2.0 * m * n * k, "TOPS", "q2_0_mmq_kernel", INT8_PEAK_TOPS, "mfma"))
+                        keep, 1, 2.0 * m * n * k, "TOPS", "q2_0_mmq_kernel", INT8_PEAK_TOPS, "mfma"))
         legs.append(Leg(f"prefill_quantize_m{m}", lambda m=m, x=x, q8=q8: bq.quantize_act_q8_1(x, q8, m, k),
-                        [x, q8], 1, 2 * m * k + bq.q8_1_act_bytes(m, k), "GB/s", "quantize_q8_1_kernel",
+                        keep, 1, 2 * m * k + bq.q8_1_act_bytes(m, k), "GB/s", "quantize_q8_1_kernel",
                         HBM_PEAK_GBS, "hbm"))
-    m = 512
-    x = torch.from_numpy(np.ascontiguousarray(p["act"][:m]).view(np.int16)).to(dev).view(torch.bfloat16)
-    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-    scratch = torch.empty((n * k,), dtype=torch.bfloat16, device=dev)
+        legs.append(Leg(f"prefill_quantize_mmq_m{m}",
+                        lambda m=m, x=x, q8=q8, y=y: bq.q2_0_prefill_gemm(x, w, y, None, q8, m, n, k, 128, True),
+                        keep, 2, 2.0 * m * n * k, "TOPS", "quantize_q8_1_kernel + q2_0_mmq_kernel",
+                        INT8_PEAK_TOPS, "mfma"))
+        legs.append(Leg(f"fallback_dense_gemm_m{m}", lambda m=m, x=x, y=y: bq.dense_gemm_bf16(x, scratch, y, m, n, k),
+                        [x, scratch, y], 1, 2.0 * m * n * k, "TOPS", "dense_gemm_bf16_kernel", BF16_PEAK_TFLOPS,
+                        "mfma"))
     legs.append(Leg("fallback_dequant", lambda: bq.dequant_q2_0_to_bf16(w, scratch, n, k, 128), [w, scratch],
                     1, w.numel() + 2 * n * k, "GB/s", "dequant_q2_0_kernel", HBM_PEAK_GBS, "hbm"))
-    legs.append(Leg("fallback_dense_gemm_m512", lambda: bq.dense_gemm_bf16(x, scratch, y, m, n, k),
-                    [x, scratch, y], 1, 2.0 * m * n * k, "TOPS", "dense_gemm_bf16_kernel", BF16_PEAK_TFLOPS,
-                    "mfma"))
     return legs
 
 
@@ -276,6 +319,8 @@ def ffn_legs(bq, dev, F):
         legs.append(Leg(f"ffn_prefill_{fmt}_m4096", ffn, keep, 5, 3 * 2.0 * m * H * I, "TOPS",
                         f"{kname} x3 + quantize + silu_mul_quantize", INT8_PEAK_TOPS, "mfma"))
         legs.append(Leg(f"ffn_gate_proj_{fmt}_m4096", lambda wg=wg, gemm=gemm: gemm(q8a, wg, gate, m, I, H),
+                        keep, 1, 2.0 * m * H * I, "TOPS", kname, INT8_PEAK_TOPS, "mfma"))
+        legs.append(Leg(f"ffn_down_proj_{fmt}_m4096", lambda wd=wd, gemm=gemm: gemm(q8h, wd, out, m, H, I),
                         keep, 1, 2.0 * m * H * I, "TOPS", kname, INT8_PEAK_TOPS, "mfma"))
     return legs
 
@@ -311,6 +356,143 @@ def q4k_legs(bq, dev, Q):
     return legs
 
 
+def ceiling_legs(dev, gemv_blocks):
+    """Measured ceilings (ceilings/ceilings.hip): launch floor, cold streaming
+    read of the decode GEMV's bytes with its grid, int8 MFMA and VALU
+    issue rates."""
+    import torch
+    import ceilings
+
+    stream = lambda: ctypes_stream(torch)
+    legs = []
+    calls = 1000
+    for label, blocks, threads in (("1x64", 1, 64), (f"{gemv_blocks}x256", gemv_blocks, 256)):
+        legs.append(Leg(f"ceiling_empty_kernel_{label}",
+                        lambda b=blocks, t=threads: [ceilings.call("ceil_empty", b, t, stream())
+                                                     for _ in range(calls)],
+                        [], calls, calls, "launches/s", "empty_kernel", None, "launch"))
+    bufs = [torch.empty((DECODE_BYTES,), dtype=torch.uint8, device=dev).random_(0, 255)
+            for _ in range(DECODE_COPIES)]
+    sink = torch.zeros((max(gemv_blocks, 4096),), dtype=torch.int32, device=dev)
+    legs.append(Leg("ceiling_stream_read_6713344B",
+                    lambda: [ceilings.call("ceil_stream_read", bufs[i % DECODE_COPIES].data_ptr(), DECODE_BYTES,
+                                           sink.data_ptr(), gemv_blocks, stream()) for i in range(calls)],
+                    bufs + [sink], calls, calls * DECODE_BYTES, "GB/s", "stream_read_kernel (cold, 80 buffers)",
+                    HBM_PEAK_GBS, "hbm"))
+    iters = 4096
+    for blocks in (512, 1024):
+        ops = blocks * 4 * iters * 4 * 2.0 * 32 * 32 * 32
+        legs.append(Leg(f"ceiling_mfma_i8_{blocks}x256",
+                        lambda b=blocks: ceilings.call("ceil_mfma_i8", b, iters, sink.data_ptr(), stream()),
+                        [sink], 1, ops, "TOPS", "v_mfma_i32_32x32x32_i8 loop", INT8_PEAK_TOPS, "mfma"))
+    viters = 8192
+    for blocks in (1024, 2048):
+        instr = blocks * 4 * viters * 8
+        legs.append(Leg(f"ceiling_valu_mad_i24_{blocks}x256",
+                        lambda b=blocks: ceilings.call("ceil_valu_mad", b, viters, sink.data_ptr(), stream()),
+                        [sink], 1, instr, "Ginstr/s", "v_mad_i32_i24 loop", VALU_PEAK_GINSTR, "valu"))
+    return legs
+
+
+def ctypes_stream(torch):
+    return torch.cuda.current_stream().cuda_stream
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def timed_oracle(fn, budget_s, max_calls):
+    """Calls fn until budget_s of CPU time or max_calls; returns (calls, seconds)."""
+    calls, t = 0, 0.0
+    while (t < budget_s and calls < max_calls) or calls == 0:
+        t1 = time.perf_counter()
+        fn()
+        t += time.perf_counter() - t1
+        calls += 1
+    return calls, t
+
+
+def cpu_baselines(ctx, budget):
+    """The oracle on one pinned host core, on bounded samples of each workload:
+    C1 whole, C2 whole calls, C3 the m = 2 verify chain whole, C4 and C5 on 16
+    activation rows with all n (their cost is linear in rows), extrapolated."""
+    import oracle
+    import inputs
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except Exception:
+        pass
+    host = f"one pinned core of {os.cpu_count()}, {cpu_model()}"
+    out = {}
+    if "tiny" in ctx:
+        d = ctx["tiny"]
+        m, n, k = d["m"], d["n"], d["k"]
+
+        def c1():
+            q8, _ = oracle.quantize_act_q8_1(d["act"], m, k)
+            oracle.q2_0_mmq(q8, d["w"], m, n, k)
+            oracle.q2_0_gemv(d["act"][:1], d["w"], 1, n, k)
+
+        calls, t = timed_oracle(c1, 0.05 * budget, 2000)
+        out["tiny_c1"] = {"value": round(2.0 * m * n * k * calls / t / 1e12, 6), "unit": "TOPS", "cores": 1,
+                          "kind": "oracle", "ms_per_call": round(t * 1e3 / calls, 3),
+                          "sample": f"{calls} whole C1 passes (quantize, MMQ m=4 n=256 k=512, GEMV row 0), "
+                                    f"{t:.2f} s on {host}; TOPS counts the MMQ's 2mnk"}
+    if "decode" in ctx:
+        d = ctx["decode"]
+        calls, t = timed_oracle(lambda: oracle.q2_0_gemv(d["act"], d["w"], 1, d["n"], d["k"]), 0.4 * budget, 200)
+        out["decode_c2"] = {"value": round(calls * DECODE_BYTES / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+                            "kind": "oracle",
+                            "sample": f"{calls} decode GEMV calls (n=12288, k=2048) of the oracle, {t:.1f} s on {host}"}
+    if "verify" in ctx:
+        f, m = ctx["verify"], 2
+        H, I = f["hidden"], f["inter"]
+        calls, t = timed_oracle(lambda: oracle.ffn_chain_gemv(np.ascontiguousarray(f["act"][:m]), f["wg"], f["wu"],
+                                                              f["wd"], m, H, I), 0.15 * budget, 20)
+        work = f["wg"].size + f["wu"].size + f["wd"].size + m * (6 * H + 12 * I)
+        out["verify_c3_m2"] = {"value": round(calls * work / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{calls} whole m=2 verify chains (gate, up, silu_mul, down; 71 MB of "
+                                         f"weights), {t:.1f} s on {host}"}
+    if "prefill" in ctx:
+        p, rows = ctx["prefill"], 16
+        n, k = p["n"], p["k"]
+        q8_rows, _ = oracle.quantize_act_q8_1(np.ascontiguousarray(p["act"][:rows]), rows, k)
+        calls, t = timed_oracle(lambda: oracle.q2_0_mmq(q8_rows, p["w"], rows, n, k), 0.1 * budget, 50)
+        out["prefill_c4_m2048"] = {
+            "value": round(2.0 * rows * n * k * calls / t / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "extrapolated_ms_m2048": round(t * 1e3 / calls * 2048 / rows, 1),
+            "sample": f"{calls} oracle MMQ calls on {rows} of the 2048 activation rows (n=12288, k=2048), "
+                      f"{t:.1f} s on {host}; extrapolated from 16 rows (the oracle's cost is linear in rows)"}
+    if "ffn" in ctx:
+        F, rows = ctx["ffn"], 16
+        H, I = F["hidden"], F["inter"]
+        x = np.ascontiguousarray(F["act"][:rows])
+        W = F["q2"]
+
+        def c5():
+            q8, _ = oracle.quantize_act_q8_1(x, rows, H)
+            g = oracle.round_bf16(oracle.q2_0_mmq(q8, W["wg"], rows, I, H))
+            u = oracle.round_bf16(oracle.q2_0_mmq(q8, W["wu"], rows, I, H))
+            q8h, _ = oracle.quantize_act_q8_1(oracle.silu_mul_bf16(g, u), rows, I)
+            oracle.q2_0_mmq(q8h, W["wd"], rows, H, I)
+
+        calls, t = timed_oracle(c5, 0.3 * budget, 5)
+        out["ffn_c5_q2_0_m4096"] = {
+            "value": round(3 * 2.0 * rows * H * I * calls / t / 1e12, 6), "unit": "TOPS", "cores": 1,
+            "kind": "oracle", "extrapolated_ms_m4096": round(t * 1e3 / calls * 4096 / rows, 1),
+            "sample": f"{calls} oracle Q2_0 FFN chains (quantize, gate, up, silu_mul, quantize, down) on {rows} of "
+                      f"the 4096 rows, {t:.1f} s on {host}; extrapolated from 16 rows (linear in rows)"}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -324,27 +506,28 @@ def main():
     dev = torch.device("cuda:0")
     legs_wanted = set(args.legs.split(","))
     legs = []
-    decode_ctx = None
+    ctx = {"tiny": inputs.tiny()}
     if "decode" in legs_wanted:
-        d = inputs.decode_gemv()
-        leg, bpc = decode_leg(bq, dev, d)
-        legs.append(leg)
-        decode_ctx = dict(d=d, bytes_per_call=bpc)
+        ctx["decode"] = inputs.decode_gemv()
+        legs += decode_legs(bq, dev, ctx["decode"])
     if "verify" in legs_wanted:
-        f = inputs.verify_ffn()
-        W = tuple(torch.from_numpy(f[key]).to(dev) for key in ("wg", "wu", "wd"))
+        f = ctx["verify"] = inputs.verify_ffn()
+        W0 = tuple(torch.from_numpy(f[key]).to(dev) for key in ("wg", "wu", "wd"))
+        Wcopies = [W0] + [tuple(t.clone() for t in W0) for _ in range(VERIFY_COPIES - 1)]
         for m in (2, 3, 4, 8):
-            legs.append(verify_leg(bq, dev, W, f["act"], m, f["hidden"], f["inter"]))
+            legs.append(verify_leg(bq, dev, Wcopies, f["act"], m, f["hidden"], f["inter"]))
         for m in (2, 3, 4, 8):
-            legs.append(verify_fused_leg(bq, dev, W, f["act"], m, f["hidden"], f["inter"]))
-    prefill_ctx = None
+            legs.append(verify_fused_leg(bq, dev, Wcopies, f["act"], m, f["hidden"], f["inter"]))
     if "prefill" in legs_wanted:
-        prefill_ctx = inputs.prefill_qkvz()
-        legs += prefill_legs(bq, dev, prefill_ctx)
+        ctx["prefill"] = inputs.prefill_qkvz()
+        legs += prefill_legs(bq, dev, ctx["prefill"])
     if "ffn" in legs_wanted:
-        legs += ffn_legs(bq, dev, inputs.prefill_ffn())
+        ctx["ffn"] = inputs.prefill_ffn()
+        legs += ffn_legs(bq, dev, ctx["ffn"])
     if "q4k" in legs_wanted:
         legs += q4k_legs(bq, dev, inputs.q4k_decode())
+    if "ceilings" in legs_wanted:
+        legs += ceiling_legs(dev, gemv_blocks=12288 // 24)  # the decode GEMV's grid: 24 rows per workgroup
     if "copy" in legs_wanted:
         legs.append(copy_leg(dev))
 
@@ -366,8 +549,25 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     summaries = {leg.name: leg.summary() for leg in legs}
     for s in summaries.values():
-        log(f"{s['name']:28s} {s['ms']:9.4f} ms x{s['reps']:<3d} {s['value']:9.2f} {s['unit']:5s} "
-            f"({100 * s['frac_of_peak']:.1f}% of peak, {s['us_per_launch']:.2f} us/launch)")
+        frac = f"{100 * s['frac_of_peak']:.1f}% of peak, " if "frac_of_peak" in s else ""
+        log(f"{s['name']:34s} {s['ms']:9.4f} ms x{s['reps']:<3d} {s['value']:10.2f} {s['unit']:10s} "
+            f"({frac}{s['us_per_launch']:.2f} us/launch)")
+
+    # ---- measured ceilings ------------------------------------------------------
+    ceil = {}
+    if "ceilings" in legs_wanted:
+        ceil = {
+            "launch_floor_us": {k.split("_")[-1]: summaries[k]["us_per_launch"]
+                                for k in summaries if k.startswith("ceiling_empty_kernel_")},
+            "stream_read_gbs": summaries["ceiling_stream_read_6713344B"]["value"],
+            "stream_read_us_per_launch": summaries["ceiling_stream_read_6713344B"]["us_per_launch"],
+            "mfma_i8_tops": max(s["value"] for k, s in summaries.items() if k.startswith("ceiling_mfma_i8_")),
+            "valu_ginstr_per_s": max(s["value"] for k, s in summaries.items()
+                                     if k.startswith("ceiling_valu_mad_i24_")),
+            "how": "ceilings/ceilings.hip, timed in this run: empty kernels (1000 per graph) with 1x64 lanes and "
+                   "with the decode GEMV's 512x256 grid; a cold read of 6,713,344 B per launch (80 buffers "
+                   "rotated, the GEMV's grid); back-to-back v_mfma_i32_32x32x32_i8 with 4 independent "
+                   "accumulators; back-to-back v_mad_i32_i24 in 8 independent chains (best of two grid sizes)"}
 
     result = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True,
@@ -383,11 +583,16 @@ def main():
                               "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                               "copy-calibrated)",
                               "kernel": s["kernel"], "us_per_launch": s["us_per_launch"],
-                              "bytes_per_launch": decode_ctx["bytes_per_call"]}
+                              "bytes_per_launch": DECODE_BYTES,
+                              "warm_gbs": summaries.get("decode_gemv_m1_warm", {}).get("value")}
+        if ceil:
+            result["roofline"]["ceilings"] = ceil
+            result["roofline"]["frac_of_ceiling"] = round(s["value"] / ceil["stream_read_gbs"], 4)
     if "prefill_mmq_m2048" in summaries:
         s = summaries["prefill_mmq_m2048"]
         result["prefill"] = {"metric": "Q2_0 MMQ prefill int8 TOPS (2mnk / kernel time), m=2048 n=12288 k=2048",
                              "value": s["value"], "unit": "TOPS", "dtype": "i8",
+                             "quantize_plus_mmq_tops": summaries["prefill_quantize_mmq_m2048"]["value"],
                              "roofline": {"bound": "mfma", "achieved": s["value"], "peak": INT8_PEAK_TOPS,
                                           "unit": "TOP/s", "frac": s["frac_of_peak"],
                                           "traffic": measured_traffic(TRAFFIC_MMQ),
@@ -395,44 +600,19 @@ def main():
                                                           "WRITE_SIZE, copy-calibrated)",
                                           "ops_per_launch": 2 * 2048 * 12288 * 2048,
                                           "algorithmic_bytes_per_launch": 61734912}}
+        if ceil:
+            result["prefill"]["roofline"]["frac_of_ceiling"] = round(s["value"] / ceil["mfma_i8_tops"], 4)
     result["legs"] = summaries
 
     # ---- CPU oracle baselines (rank 0, N = 1), on one pinned host core ----------
     if not args.no_cpu_baseline:
-        try:
-            os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
-        except Exception:
-            pass
-    if not args.no_cpu_baseline and "decode_gemv_m1" in summaries:
-        import oracle
-        d = decode_ctx["d"]
-        calls, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds and calls < 200:
-            t1 = time.perf_counter()
-            oracle.q2_0_gemv(d["act"], d["w"], 1, d["n"], d["k"])
-            t_cpu += time.perf_counter() - t1
-            calls += 1
-        cpu_gbs = calls * decode_ctx["bytes_per_call"] / t_cpu / 1e9
-        result["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                                  "sample": f"{calls} decode GEMV calls (n=12288, k=2048) of the oracle, "
-                                            f"{t_cpu:.1f} s on one pinned host core of {os.cpu_count()}"}
-    # ---- CPU oracle baseline of the MMQ: 16 of the 2048 rows, all n -----------
-    if not args.no_cpu_baseline and prefill_ctx is not None and "prefill" in result:
-        import oracle
-        p, rows = prefill_ctx, 16
-        n, k = p["n"], p["k"]
-        q8_rows, _ = oracle.quantize_act_q8_1(np.ascontiguousarray(p["act"][:rows]), rows, k)
-        calls, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds / 4 and calls < 50:
-            t1 = time.perf_counter()
-            oracle.q2_0_mmq(q8_rows, p["w"], rows, n, k)
-            t_cpu += time.perf_counter() - t1
-            calls += 1
-        result["prefill"]["cpu_baseline"] = {
-            "value": round(2.0 * rows * n * k * calls / t_cpu / 1e12, 6), "unit": "TOPS", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{calls} oracle MMQ calls on {rows} of the 2048 activation rows (n=12288, k=2048; the "
-                      f"oracle's cost is linear in rows), {t_cpu:.1f} s on one pinned host core of {os.cpu_count()}"}
+        log("oracle baselines on one host core")
+        cb = cpu_baselines(ctx, args.cpu_seconds)
+        if "decode_c2" in cb:
+            result["cpu_baseline"] = cb["decode_c2"]
+        if "prefill_c4_m2048" in cb and "prefill" in result:
+            result["prefill"]["cpu_baseline"] = cb["prefill_c4_m2048"]
+        result["cpu_baselines"] = cb
     print(json.dumps(result), flush=True)
 
 

@@ -1,0 +1,115 @@
+// Measured ceilings for the benchmark: what this GPU reaches on the launch,
+// streaming-read, int8 matrix-core and vector-ALU paths alone, so that the
+// hot path's figures can be read against them as well as against the
+// published peaks.  Bench-only: built into its own library, never linked
+// into libbqmm.so.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// Nothing: the cost of dispatching a grid and retiring it.
+__global__ void empty_kernel() {}
+
+// Reads `bytes` (a multiple of 16) once with 16-byte loads: workgroup b
+// takes the b-th of gridDim.x equal contiguous ranges, and each lane issues
+// all of its (at most kLoads) loads before using any, so every load of a
+// launch is in flight at once (lanes past the range's end load its last
+// chunk again).  The loaded words are folded together and stored only if the
+// fold hits a value that the inputs here never produce, so the loads cannot
+// be dropped and (in practice) nothing is written.
+constexpr int kLoads = 4;
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restrict__ src, uint64_t chunks,
+                                                          uint32_t *__restrict__ sink) {
+  const uint64_t per = (chunks + gridDim.x - 1) / gridDim.x;
+  const uint64_t begin = (uint64_t)blockIdx.x * per;
+  const uint64_t end = begin + per < chunks ? begin + per : chunks;
+  if (begin >= end) return;
+  uint4 v[kLoads];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const uint64_t i = begin + threadIdx.x + (uint64_t)j * blockDim.x;
+    v[j] = src[i < end ? i : end - 1];
+  }
+  uint32_t x = 0;
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) x ^= v[j].x ^ (v[j].y * 3u) ^ (v[j].z * 5u) ^ (v[j].w * 7u);
+  if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
+}
+
+// Back-to-back v_mfma_i32_32x32x32_i8 with four independent accumulators per
+// wave (no dependent chain, no memory traffic in the loop): the int8 matrix
+// core's issue rate.
+__global__ __launch_bounds__(256) void mfma_i8_kernel(uint32_t iters, int seed, int *__restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const v4i a = {seed + lane, seed ^ lane, seed - lane, seed * 3 + lane};
+  const v4i b = {lane, seed, lane * 5, seed - 7};
+  v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (uint32_t i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, b, c3, 0, 0, 0);
+  }
+  int s = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s ^= c0[r] ^ c1[r] ^ c2[r] ^ c3[r];
+  if (s == 0x7FEDCBA9) sink[blockIdx.x] = s;
+}
+
+// Independent chains of the integer multiply-add the Q2_0 MMQ folds with
+// (v_mad_i32_i24): eight chains per lane, so each instruction's result is
+// not awaited by the next; the vector ALU's issue rate.
+__global__ __launch_bounds__(256) void valu_mad_kernel(uint32_t iters, int seed, int *__restrict__ sink) {
+  const int t = (int)threadIdx.x;
+  int a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = seed + t * (j + 1);
+  const int m0 = (seed & 0x7FF) + 3, m1 = ((seed >> 3) & 0x7FF) + 5;
+  for (uint32_t i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = ((a[j] << 8) >> 8) * (((j & 1) ? m0 : m1)) + a[j];
+  }
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s ^= a[j];
+  if (s == 0x7FEDCBA9) sink[blockIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Each launches one kernel on `stream` and returns the HIP status.
+int ceil_empty(uint32_t blocks, uint32_t threads, void *stream) {
+  hipLaunchKernelGGL(empty_kernel, dim3(blocks), dim3(threads), 0, static_cast<hipStream_t>(stream));
+  return (int)hipGetLastError();
+}
+
+// bytes % 16 == 0 and bytes <= blocks * 256 * kLoads * 16 (every chunk read);
+// sink holds `blocks` uint32.
+int ceil_stream_read(const void *src, uint64_t bytes, void *sink, uint32_t blocks, void *stream) {
+  if (bytes % 16u != 0 || bytes > (uint64_t)blocks * 256u * kLoads * 16u) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4 *>(src), bytes / 16u, static_cast<uint32_t *>(sink));
+  return (int)hipGetLastError();
+}
+
+// Work per launch: blocks * 4 waves * iters * 4 MFMAs * 2*32*32*32 int8 ops.
+int ceil_mfma_i8(uint32_t blocks, uint32_t iters, void *sink, void *stream) {
+  hipLaunchKernelGGL(mfma_i8_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, 12345,
+                     static_cast<int *>(sink));
+  return (int)hipGetLastError();
+}
+
+// Work per launch: blocks * 4 waves * iters * 8 wave-wide multiply-adds.
+int ceil_valu_mad(uint32_t blocks, uint32_t iters, void *sink, void *stream) {
+  hipLaunchKernelGGL(valu_mad_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, 777,
+                     static_cast<int *>(sink));
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

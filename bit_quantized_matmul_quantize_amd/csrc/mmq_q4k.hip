@@ -4,53 +4,91 @@
 //  with A in q8_1 and W in block_q4_K (256 weights in 144 bytes), BF16 store,
 //  any n (a with-check variant for n % 128 != 0).]
 //
-// out[m][n] = sum_j da[m][j] * d[n]*sc_j[n] * D[m][n][j]  -  sum_j dmin[n]*m_j[n] * s[m][j]
-//   D = sum_{t<32} q4 * q (exact int32, one 32-block),  s = the stored q8_1 sum (da * sum q).
+// out[m][n] = sum_sb d[n] * sum_j da[m][j] * sc_j[n] * D[m][n][j]
+//             - sum_j dmin[n]*m_j[n] * s[m][j]
+//   D = sum_{t<32} q4 * q (exact, one 32-block),  s = the stored q8_1 sum (da * sum q).
+//
+// The per-block scale fold is what bounds this kernel (every output needs
+// one VALU operation per 32-block for the activation scale), so the 6-bit
+// sub-scale is moved onto the matrix core: the weight operand is q4 * sc_j
+// and the activation operand the q8_1 code q, both exact small integers in
+// binary16 (q4 * sc_j <= 945, |q| <= 127), so v_mfma_f32_32x32x16_f16
+// returns sc_j * D exactly (every product and partial sum is an integer
+// below 2^24).  Per block and output that leaves one fma with the lane's
+// activation scale, acc += (sc_j * D) * da; per super-block one fma with the
+// weight row's d, out += acc * d.  The min term runs on the matrix core as
+// well, once per super-block: v_mfma_f32_32x32x8_f16 with A = fp16(-dmin *
+// m_j) for the eight sub-blocks and B = their stored sums s, accumulating
+// into the output registers.
 //
 // Tile 128 (n) x 256 (m), 512 lanes = 8 waves of 64 (n) x 64 (m); k is staged
-// 128 at a time (half a super-block: four sub-blocks) through two LDS stages.
-//   * main term: v_mfma_i32_32x32x32_i8 per sub-block (weights as A, so a
-//     lane's 16 accumulators share one activation row and da is a lane
-//     value), then per output: float(D) * da, times d*sc_j of its weight row
-//     (from LDS), added into the output accumulator;
-//   * min term: one v_mfma_f32_32x32x8_f16 per stage and subtile with
-//     A = fp16(-dmin * m_j) for the stage's four sub-blocks and B = their s,
-//     accumulating into the same output registers (no VALU).
-// The MFMA of step i + 1 is issued before the epilogue of step i, and the
-// compute is last in the loop body (see the Q2_0 kernel for why).
+// 64 at a time (one 64-weight chunk of a super-block: sub-block 2t in the low
+// nibbles, 2t + 1 in the high nibbles of the same 32 bytes) through two LDS
+// stages, both operands converted to binary16 once per workgroup while they
+// are written: the q8_1 codes by an exponent-bias trick (bytes xor 0x80 under
+// the exponent of 1024, then one packed subtraction of 1152), the 4-bit codes
+// likewise times sc_j with one packed fma.  The MFMA of step i + 1 is issued
+// before the fold of step i, and the compute is last in the loop body (see
+// the Q2_0 kernel for why).
 #include "bqmm_internal.h"
 
 namespace bqmm {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BN = 128;
 constexpr int BM = 256;
-constexpr int KG = 128;
-constexpr int LDS_STRIDE = KG + 16;
+constexpr int KS = 64;                       // k per stage: one chunk of a super-block
+constexpr int ROW = 2 * KS + 16;             // bytes per staged binary16 row; the pad spreads banks
 constexpr int kThreads = 512;
 // one LDS stage
-constexpr int kActBytes = BM * LDS_STRIDE;          // activation codes
-constexpr int kWBytes = BN * LDS_STRIDE;            // weight codes (one byte each)
-constexpr int kDscOff = kActBytes + kWBytes;        // float [4][BN]: d * sc_j
-constexpr int kNminOff = kDscOff + 4 * BN * 4;      // fp16 [BN][4]: -dmin * m_j
-constexpr int kDaOff = kNminOff + BN * 8;           // float [BM][4]: da
-constexpr int kSOff = kDaOff + BM * 16;             // fp16 [BM][4]: s
-constexpr int kStageBytes = kSOff + BM * 8;
+constexpr int kActBytes = BM * ROW;          // activation codes, binary16
+constexpr int kWBytes = BN * ROW;            // q4 * sc_j, binary16
+constexpr int kDaOff = kActBytes + kWBytes;  // float [BM][2]: da of the stage's two blocks
+constexpr int kStageBytes = kDaOff + BM * 8;
+// per super-block (two of them, alternating): d of each weight row, the min
+// term's operands fp16(-dmin * m_j) [BN][8] and the activation sums s [BM][8]
+constexpr int kSbD = 0;
+constexpr int kSbNmin = kSbD + BN * 4;
+constexpr int kSbS = kSbNmin + BN * 16;
+constexpr int kSbBytes = kSbS + BM * 16;
+constexpr int kLdsBytes = 2 * kStageBytes + 2 * kSbBytes;
+
+__device__ __forceinline__ uint32_t sbyte(const uint32_t S[3], int i) { return (S[i >> 2] >> (8 * (i & 3))) & 0xFFu; }
 
 __device__ __forceinline__ void scale_min(const uint32_t S[3], int j, uint32_t &sc, uint32_t &mn) {
-  auto byte = [&](int i) { return (S[i >> 2] >> (8 * (i & 3))) & 0xFFu; };
   if (j < 4) {
-    sc = byte(j) & 63u;
-    mn = byte(j + 4) & 63u;
+    sc = sbyte(S, j) & 63u;
+    mn = sbyte(S, j + 4) & 63u;
   } else {
-    sc = (byte(j + 4) & 15u) | ((byte(j - 4) >> 6) << 4);
-    mn = (byte(j + 4) >> 4) | ((byte(j) >> 6) << 4);
+    sc = (sbyte(S, j + 4) & 15u) | ((sbyte(S, j - 4) >> 6) << 4);
+    mn = (sbyte(S, j + 4) >> 4) | ((sbyte(S, j) >> 6) << 4);
   }
+}
+
+// Four signed bytes of x as two pairs of binary16, exactly: xor 0x80 turns
+// each byte into q + 128 (0..255); placed under the high byte 0x64 a half is
+// 1024 + q + 128, and one packed subtraction of 1152 leaves q.
+__device__ __forceinline__ void s8x4_to_f16(uint32_t x, uint32_t &lo, uint32_t &hi) {
+  const uint32_t u = x ^ 0x80808080u;
+  const v2h bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u)) + bias);
+  hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, u, 0x07030602u)) + bias);
+}
+
+// Four 4-bit codes (one per byte of x, already masked to 0..15) times sc, as
+// two pairs of binary16: 1024 + q is exact under the exponent of 1024, and
+// the packed fma (1024 + q) * sc - 1024 * sc is rounded once, from the exact
+// q * sc <= 945, which binary16 holds exactly.
+__device__ __forceinline__ void u4x4_to_f16(uint32_t x, v2h sc, v2h nsc1024, uint32_t &lo, uint32_t &hi) {
+  const v2h a = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x, 0x05010400u));
+  const v2h b = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x, 0x07030602u));
+  lo = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(a, sc, nsc1024));
+  hi = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(b, sc, nsc1024));
 }
 
 template <bool kDump>
@@ -59,6 +97,7 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
     int32_t *__restrict__ dots, uint32_t m, uint32_t n, uint32_t k, uint32_t m0, uint32_t mt,
     uint32_t n0, uint32_t nt, uint32_t tile_n0, uint32_t tile_m0, uint32_t ldc) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint8_t *const sb_lds = lds + 2 * kStageBytes;
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u, l32 = lane & 31u, hi = lane >> 5;
@@ -69,80 +108,96 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
   const uint32_t kpad = (k + 255u) / 256u * 256u;
   const uint32_t nblk_pad = kpad / 32u;
   const uint32_t nsb = k / 256u;
-  const uint32_t nstages = k / KG;
+  const uint32_t nstages = k / KS;
   const uint8_t *ds = act_q8 + (uint64_t)m * kpad;
 
-  // global -> register staging; rows past m or n read the last valid row
-  uint32_t a_row[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) a_row[i] = min(m_base + 64u * i + (tid >> 3), m - 1u);
-  const uint32_t a_col = (tid & 7u) * 16u;
+  // Global -> register staging; rows past m or n read the last valid row.
+  //   activation codes: thread -> row tid / 2, bytes 32 * (tid % 2) of the stage;
+  //   weight codes: thread -> row tid / 4, bytes 8 * (tid % 4) of the chunk,
+  //     plus its row's 16-byte header (d, dmin, packed sub-scales/mins);
+  //   activation (d, s): threads 256.. -> row tid - 256, the stage's two blocks.
+  const uint32_t a_row = min(m_base + (tid >> 1), m - 1u), a_half = tid & 1u;
   const uint32_t w_row = min(n_base + (tid >> 2), n - 1u), w_part = tid & 3u;
-  const uint32_t h_row = min(n_base + tid, n - 1u);         // header row for tid < BN
-  const uint32_t s_row = min(m_base + (tid - 256u), m - 1u);  // activation-scale row for tid >= 256
-
-  uint4 ra0, ra1, ra2, ra3, rw, rh = make_uint4(0, 0, 0, 0), rds = make_uint4(0, 0, 0, 0);
+  const uint32_t s_row = min(m_base + (tid - 256u), m - 1u);
+  uint4 ra0, ra1, rh;
+  uint2 rw, rds = make_uint2(0, 0);
 #define BQMM_FETCH(st)                                                                                  \
   do {                                                                                                  \
-    const uint32_t sb_ = (st) >> 1, hs_ = (st) & 1u;                                                    \
-    ra0 = *reinterpret_cast<const uint4 *>(act_q8 + (uint64_t)a_row[0] * kpad + (st) * KG + a_col);      \
-    ra1 = *reinterpret_cast<const uint4 *>(act_q8 + (uint64_t)a_row[1] * kpad + (st) * KG + a_col);      \
-    ra2 = *reinterpret_cast<const uint4 *>(act_q8 + (uint64_t)a_row[2] * kpad + (st) * KG + a_col);      \
-    ra3 = *reinterpret_cast<const uint4 *>(act_q8 + (uint64_t)a_row[3] * kpad + (st) * KG + a_col);      \
-    rw = *reinterpret_cast<const uint4 *>(w + ((uint64_t)w_row * nsb + sb_) * 144u + 16u + 64u * hs_ +  \
-                                          16u * w_part);                                                \
-    if (tid < BN)                                                                                       \
-      rh = *reinterpret_cast<const uint4 *>(w + ((uint64_t)h_row * nsb + sb_) * 144u);                  \
-    else if (tid >= 256u)                                                                               \
-      rds = *reinterpret_cast<const uint4 *>(ds + 4ull * ((uint64_t)s_row * nblk_pad + 4u * (st)));     \
+    const uint32_t sb_ = (st) >> 2, t_ = (st) & 3u;                                                     \
+    const uint8_t *ap_ = act_q8 + (uint64_t)a_row * kpad + (st) * KS + 32u * a_half;                   \
+    ra0 = *reinterpret_cast<const uint4 *>(ap_);                                                        \
+    ra1 = *reinterpret_cast<const uint4 *>(ap_ + 16);                                                   \
+    const uint8_t *bp_ = w + ((uint64_t)w_row * nsb + sb_) * 144u;                                      \
+    rh = *reinterpret_cast<const uint4 *>(bp_);                                                         \
+    rw = *reinterpret_cast<const uint2 *>(bp_ + 16u + 32u * t_ + 8u * w_part);                          \
+    if (tid >= 256u)                                                                                    \
+      rds = *reinterpret_cast<const uint2 *>(ds + 4ull * ((uint64_t)s_row * nblk_pad + 2u * (st)));    \
   } while (0)
 
+  // Write the prefetched stage into LDS stage buffer `buf`; stage st of
+  // super-block st / 4 also writes that super-block's entries of the min
+  // term and the activation sums (and, from its first stage, d).
 #define BQMM_STAGE(buf, st)                                                                             \
   do {                                                                                                  \
     uint8_t *L = lds + (buf) * kStageBytes;                                                             \
-    *reinterpret_cast<uint4 *>(L + (0 * 64 + (tid >> 3)) * LDS_STRIDE + a_col) = ra0;                   \
-    *reinterpret_cast<uint4 *>(L + (1 * 64 + (tid >> 3)) * LDS_STRIDE + a_col) = ra1;                   \
-    *reinterpret_cast<uint4 *>(L + (2 * 64 + (tid >> 3)) * LDS_STRIDE + a_col) = ra2;                   \
-    *reinterpret_cast<uint4 *>(L + (3 * 64 + (tid >> 3)) * LDS_STRIDE + a_col) = ra3;                   \
+    uint8_t *SB = sb_lds + (((st) >> 2) & 1u) * kSbBytes;                                               \
+    const uint32_t t_ = (st) & 3u;                                                                      \
     {                                                                                                   \
-      /* part p: chunk tt = p / 2 (sub-blocks 2tt low nibbles, 2tt+1 high), bytes 16*(p%2) */          \
-      const uint32_t tt = w_part >> 1, i0 = (w_part & 1u) * 16u;                                        \
-      uint8_t *wr = L + kActBytes + (tid >> 2) * LDS_STRIDE + 64u * tt + i0;                            \
-      *reinterpret_cast<uint4 *>(wr) = make_uint4(rw.x & 0x0F0F0F0Fu, rw.y & 0x0F0F0F0Fu,               \
-                                                  rw.z & 0x0F0F0F0Fu, rw.w & 0x0F0F0F0Fu);              \
-      *reinterpret_cast<uint4 *>(wr + 32) = make_uint4((rw.x >> 4) & 0x0F0F0F0Fu, (rw.y >> 4) & 0x0F0F0F0Fu, \
-                                                       (rw.z >> 4) & 0x0F0F0F0Fu, (rw.w >> 4) & 0x0F0F0F0Fu); \
+      uint32_t h[16];                                                                                   \
+      const uint32_t x_[8] = {ra0.x, ra0.y, ra0.z, ra0.w, ra1.x, ra1.y, ra1.z, ra1.w};                  \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i) s8x4_to_f16(x_[i], h[2 * i], h[2 * i + 1]);         \
+      uint8_t *ar = L + (tid >> 1) * ROW + 64u * a_half;                                                \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                     \
+        *reinterpret_cast<uint4 *>(ar + 16 * i) = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]); \
     }                                                                                                   \
-    if (tid < BN) {                                                                                     \
-      const float d_ = f16_bits_to_f32(rh.x & 0xFFFFu), dmin_ = f16_bits_to_f32(rh.x >> 16);           \
+    {                                                                                                   \
       const uint32_t S_[3] = {rh.y, rh.z, rh.w};                                                        \
-      float *dsc = reinterpret_cast<float *>(L + kDscOff);                                              \
-      _Float16 nm[4];                                                                                   \
-      _Pragma("unroll") for (int jl = 0; jl < 4; ++jl) {                                                \
-        uint32_t sc_, mn_;                                                                              \
-        scale_min(S_, 4 * (int)((st) & 1u) + jl, sc_, mn_);                                             \
-        dsc[jl * BN + tid] = d_ * (float)sc_;                                                           \
-        nm[jl] = (_Float16)(-dmin_ * (float)mn_);                                                       \
+      uint32_t sc0_, sc1_, mn0_, mn1_;                                                                  \
+      scale_min(S_, 2 * (int)t_, sc0_, mn0_);                                                           \
+      scale_min(S_, 2 * (int)t_ + 1, sc1_, mn1_);                                                       \
+      if (kDump) sc0_ = sc1_ = 1u;                                                                      \
+      const _Float16 f0_ = (_Float16)(float)sc0_, f1_ = (_Float16)(float)sc1_;                          \
+      const v2h s0_ = {f0_, f0_}, s1_ = {f1_, f1_};                                                     \
+      const v2h n0_ = {(_Float16)(-1024.0f * (float)sc0_), (_Float16)(-1024.0f * (float)sc0_)};         \
+      const v2h n1_ = {(_Float16)(-1024.0f * (float)sc1_), (_Float16)(-1024.0f * (float)sc1_)};         \
+      uint32_t lo_[4], hi_[4];                                                                          \
+      u4x4_to_f16(rw.x & 0x0F0F0F0Fu, s0_, n0_, lo_[0], lo_[1]);                                        \
+      u4x4_to_f16(rw.y & 0x0F0F0F0Fu, s0_, n0_, lo_[2], lo_[3]);                                        \
+      u4x4_to_f16((rw.x >> 4) & 0x0F0F0F0Fu, s1_, n1_, hi_[0], hi_[1]);                                 \
+      u4x4_to_f16((rw.y >> 4) & 0x0F0F0F0Fu, s1_, n1_, hi_[2], hi_[3]);                                 \
+      uint8_t *wr = L + kActBytes + (tid >> 2) * ROW + 16u * w_part;                                    \
+      *reinterpret_cast<uint4 *>(wr) = make_uint4(lo_[0], lo_[1], lo_[2], lo_[3]);                      \
+      *reinterpret_cast<uint4 *>(wr + 64) = make_uint4(hi_[0], hi_[1], hi_[2], hi_[3]);                 \
+      if (!kDump && t_ == 0u) {                                                                         \
+        /* the four lanes of a row each write two of its eight min-term    */                          \
+        /* operands (sub-blocks t_ and t_ + 4, so one unpack form serves); */                          \
+        /* all four write the same d                                        */                          \
+        const float d_ = f16_bits_to_f32(rh.x & 0xFFFFu), dmin_ = f16_bits_to_f32(rh.x >> 16);         \
+        reinterpret_cast<float *>(SB + kSbD)[tid >> 2] = d_;                                            \
+        uint32_t sca_, mna_, scb_, mnb_;                                                                \
+        scale_min(S_, (int)w_part, sca_, mna_);                                                         \
+        scale_min(S_, (int)w_part + 4, scb_, mnb_);                                                     \
+        _Float16 *nm_ = reinterpret_cast<_Float16 *>(SB + kSbNmin + (tid >> 2) * 16);                   \
+        nm_[w_part] = (_Float16)(-dmin_ * (float)mna_);                                                 \
+        nm_[w_part + 4] = (_Float16)(-dmin_ * (float)mnb_);                                             \
       }                                                                                                 \
-      *reinterpret_cast<v4h *>(L + kNminOff + tid * 8) = v4h{nm[0], nm[1], nm[2], nm[3]};               \
-    } else if (tid >= 256u) {                                                                           \
+    }                                                                                                   \
+    if (tid >= 256u) {                                                                                  \
       const uint32_t r_ = tid - 256u;                                                                   \
-      *reinterpret_cast<float4 *>(L + kDaOff + r_ * 16) =                                               \
-          make_float4(f16_bits_to_f32(rds.x & 0xFFFFu), f16_bits_to_f32(rds.y & 0xFFFFu),               \
-                      f16_bits_to_f32(rds.z & 0xFFFFu), f16_bits_to_f32(rds.w & 0xFFFFu));              \
-      *reinterpret_cast<uint2 *>(L + kSOff + r_ * 8) =                                                  \
-          make_uint2((rds.x >> 16) | (rds.y & 0xFFFF0000u), (rds.z >> 16) | (rds.w & 0xFFFF0000u));     \
+      *reinterpret_cast<float2 *>(L + kDaOff + r_ * 8) =                                                \
+          make_float2(f16_bits_to_f32(rds.x & 0xFFFFu), f16_bits_to_f32(rds.y & 0xFFFFu));              \
+      *reinterpret_cast<uint32_t *>(SB + kSbS + r_ * 16 + 4 * t_) = (rds.x >> 16) | (rds.y & 0xFFFF0000u); \
     }                                                                                                   \
   } while (0)
 
-  v16f acc[2][2];
+  v16f acc_out[2][2], acc_sb[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-  const v16i zero16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      for (int r = 0; r < 16; ++r) acc_out[a][b][r] = 0.0f, acc_sb[a][b][r] = 0.0f;
+  const v16f zero16 = {};
 
   BQMM_FETCH(0u);
   BQMM_STAGE(0u, 0u);
@@ -155,77 +210,91 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
     }
     const uint8_t *L = lds + (st & 1u) * kStageBytes;
     const uint8_t *a_lds = L, *w_lds = L + kActBytes;
-    const float *dsc_lds = reinterpret_cast<const float *>(L + kDscOff);
+    const uint32_t t = st & 3u;
 
-    v4i A[2][4], B[2][4];
-    float da[2][4];
+    // 8 steps (b, sn, sm): block b of the stage (sub-block 2t + b), subtiles
+    // sn (weights, A) and sm (activations, B); each step is two MFMAs over the
+    // block's 32 k.  Operands of a block are read when its first step begins.
+    v8h A[2][2], B[2][2];
+    float da[2][2];
+    v16f D[2];
+    auto load_block = [&](int b) {
 #pragma unroll
-    for (int sm = 0; sm < 2; ++sm) {
-      const uint32_t ml = wm * 64 + sm * 32 + l32;
+      for (int sm = 0; sm < 2; ++sm) {
+        const uint32_t ml = wm * 64 + sm * 32 + l32;
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        B[sm][b] = *reinterpret_cast<const v4i *>(a_lds + ml * LDS_STRIDE + 32 * b + 16 * hi);
-      const float4 t = *reinterpret_cast<const float4 *>(L + kDaOff + ml * 16);
-      da[sm][0] = t.x; da[sm][1] = t.y; da[sm][2] = t.z; da[sm][3] = t.w;
-    }
-#pragma unroll
-    for (int sn = 0; sn < 2; ++sn) {
-      const uint32_t nl = wn * 64 + sn * 32 + l32;
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        A[sn][b] = *reinterpret_cast<const v4i *>(w_lds + nl * LDS_STRIDE + 32 * b + 16 * hi);
-    }
-    if constexpr (!kDump) {
-      // min term on the matrix core: K = 8 with the upper four k-slots zero
+        for (int h = 0; h < 2; ++h)
+          B[sm][h] = *reinterpret_cast<const v8h *>(a_lds + ml * ROW + 64 * b + 32 * h + 16 * hi);
+        da[sm][b] = reinterpret_cast<const float *>(L + kDaOff)[ml * 2 + b];
+      }
 #pragma unroll
       for (int sn = 0; sn < 2; ++sn) {
         const uint32_t nl = wn * 64 + sn * 32 + l32;
-        const v4h zh = {0, 0, 0, 0};
-        const v4h an = hi ? zh : *reinterpret_cast<const v4h *>(L + kNminOff + nl * 8);
 #pragma unroll
-        for (int sm = 0; sm < 2; ++sm) {
-          const uint32_t ml = wm * 64 + sm * 32 + l32;
-          const v4h bs = hi ? zh : *reinterpret_cast<const v4h *>(L + kSOff + ml * 8);
-          acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x8f16(an, bs, acc[sn][sm], 0, 0, 0);
-        }
+        for (int h = 0; h < 2; ++h)
+          A[sn][h] = *reinterpret_cast<const v8h *>(w_lds + nl * ROW + 64 * b + 32 * h + 16 * hi);
       }
-    }
-
-    // 16 steps (sn, sm, b), software-pipelined by one
-    v16i D[2];
-    float dsc[16];
+    };
 #pragma unroll
-    for (int i = 0; i <= 16; ++i) {
-      if (i < 16) {
-        const int sn = i >> 3, sm = (i >> 2) & 1, b = i & 3;
-        D[i & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[sn][b], B[sm][b], zero16, 0, 0, 0);
-        // keep the MFMA ahead of the previous step's epilogue (see mmq_q2.hip)
+    for (int i = 0; i <= 8; ++i) {
+      if (i < 8) {
+        const int b = i >> 2, sn = (i >> 1) & 1, sm = i & 1;
+        if ((i & 3) == 0) load_block(b);
+        D[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            A[sn][1], B[sm][1], __builtin_amdgcn_mfma_f32_32x32x16_f16(A[sn][0], B[sm][0], zero16, 0, 0, 0), 0, 0,
+            0);
+        // keep the MFMAs ahead of the previous step's fold (see mmq_q2.hip)
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i > 0) {
         const int p = i - 1;
-        const int sn = p >> 3, sm = (p >> 2) & 1, b = p & 3;
-        const v16i &Dp = D[p & 1];
+        const int b = p >> 2, sn = (p >> 1) & 1, sm = p & 1;
+        const v16f &Dp = D[p & 1];
         if constexpr (kDump) {
           const uint32_t mm = m_base + wm * 64 + sm * 32 + l32;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const uint32_t nn = n_base + wn * 64 + sn * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
             if (mm >= m0 && mm < m0 + mt && nn >= n0 && nn < n0 + nt)
-              dots[((uint64_t)(mm - m0) * nt + (nn - n0)) * (k / 32u) + 4u * st + b] = Dp[r];
+              dots[((uint64_t)(mm - m0) * nt + (nn - n0)) * (k / 32u) + 2u * st + b] = (int32_t)Dp[r];
           }
         } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 t = *reinterpret_cast<const float4 *>(dsc_lds + b * BN + wn * 64 + sn * 32 + 8 * q + 4 * hi);
-            dsc[4 * q + 0] = t.x; dsc[4 * q + 1] = t.y; dsc[4 * q + 2] = t.z; dsc[4 * q + 3] = t.w;
-          }
           const float a = da[sm][b];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[sn][sm][r] = fmaf((float)Dp[r] * a, dsc[r], acc[sn][sm][r]);
+          for (int r = 0; r < 16; ++r) acc_sb[sn][sm][r] = fmaf(Dp[r], a, acc_sb[sn][sm][r]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if constexpr (!kDump) {
+      if (t == 3u) {
+        // end of a super-block: apply each weight row's d, then the min term
+        // on the matrix core (K = 8: the super-block's eight sub-blocks)
+        const uint8_t *SB = sb_lds + ((st >> 2) & 1u) * kSbBytes;
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn) {
+          float dv[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 t4 = *reinterpret_cast<const float4 *>(SB + kSbD + 4 * (wn * 64 + sn * 32 + 8 * q + 4 * hi));
+            dv[4 * q] = t4.x; dv[4 * q + 1] = t4.y; dv[4 * q + 2] = t4.z; dv[4 * q + 3] = t4.w;
+          }
+          const uint32_t nl = wn * 64 + sn * 32 + l32;
+          const v4h an = *reinterpret_cast<const v4h *>(SB + kSbNmin + nl * 16 + 8 * hi);
+#pragma unroll
+          for (int sm = 0; sm < 2; ++sm) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              acc_out[sn][sm][r] = fmaf(acc_sb[sn][sm][r], dv[r], acc_out[sn][sm][r]);
+              acc_sb[sn][sm][r] = 0.0f;
+            }
+            const uint32_t ml = wm * 64 + sm * 32 + l32;
+            const v4h bs = *reinterpret_cast<const v4h *>(SB + kSbS + ml * 16 + 8 * hi);
+            acc_out[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x8f16(an, bs, acc_out[sn][sm], 0, 0, 0);
+          }
+        }
+      }
     }
   }
 #undef BQMM_FETCH
@@ -242,7 +311,7 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t nn = n_base + wn * 64 + sn * 32 + 8 * q + 4 * hi;
-          const v16f &v = acc[sn][sm];
+          const v16f &v = acc_out[sn][sm];
           if (full) {
             *reinterpret_cast<uint2 *>(orow + nn) =
                 make_uint2(pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3]));
@@ -266,21 +335,21 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
 hipError_t launch_q4k_mmq(const void *act_q8, const void *w, void *out, int32_t *dots,
                           uint32_t m0, uint32_t mt, uint32_t n0, uint32_t nt, uint32_t m,
                           uint32_t n, uint32_t k, uint32_t ldc, hipStream_t s) {
-  // Two stages exceed the 64 KB default dynamic-LDS limit; gfx950 allows 160 KB.
-  hipError_t attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(q4k_mmq_kernel<false>), 2 * kStageBytes);
+  // The stages exceed the 64 KB default dynamic-LDS limit; gfx950 allows 160 KB.
+  hipError_t attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(q4k_mmq_kernel<false>), kLdsBytes);
   if (attr_err == hipSuccess)
-    attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(q4k_mmq_kernel<true>), 2 * kStageBytes);
+    attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(q4k_mmq_kernel<true>), kLdsBytes);
   if (attr_err != hipSuccess) return attr_err;
   if (dots == nullptr) {
     const dim3 grid((uint32_t)(((uint64_t)n + BN - 1) / BN), (uint32_t)(((uint64_t)m + BM - 1) / BM));
-    hipLaunchKernelGGL(q4k_mmq_kernel<false>, grid, dim3(kThreads), 2 * kStageBytes, s,
+    hipLaunchKernelGGL(q4k_mmq_kernel<false>, grid, dim3(kThreads), kLdsBytes, s,
                        static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
                        static_cast<uint16_t *>(out), nullptr, m, n, k, 0u, 0u, 0u, 0u, 0u, 0u, ldc);
   } else {
     const uint32_t tn0 = n0 / BN, tn1 = (n0 + nt - 1) / BN;
     const uint32_t tm0 = m0 / BM, tm1 = (m0 + mt - 1) / BM;
     const dim3 grid(tn1 - tn0 + 1, tm1 - tm0 + 1);
-    hipLaunchKernelGGL(q4k_mmq_kernel<true>, grid, dim3(kThreads), 2 * kStageBytes, s,
+    hipLaunchKernelGGL(q4k_mmq_kernel<true>, grid, dim3(kThreads), kLdsBytes, s,
                        static_cast<const uint8_t *>(act_q8), static_cast<const uint8_t *>(w),
                        nullptr, dots, m, n, k, m0, mt, n0, nt, tn0, tm0, n);
   }

@@ -379,6 +379,13 @@ def ceiling_legs(dev, gemv_blocks):
                                            sink.data_ptr(), gemv_blocks, stream()) for i in range(calls)],
                     bufs + [sink], calls, calls * DECODE_BYTES, "GB/s", "stream_read_kernel (cold, 80 buffers)",
                     HBM_PEAK_GBS, "hbm"))
+    out = torch.empty((12288,), dtype=torch.bfloat16, device=dev)
+    legs.append(Leg("ceiling_stream_read_write_6713344B",
+                    lambda: [ceilings.call("ceil_stream_read_write", bufs[i % DECODE_COPIES].data_ptr(),
+                                           DECODE_BYTES - 2 * 12288, out.data_ptr(), 12288, gemv_blocks, stream())
+                             for i in range(calls)],
+                    bufs + [out], calls, calls * DECODE_BYTES, "GB/s",
+                    "stream_read_write_kernel (cold, 80 buffers; 24 KB written)", HBM_PEAK_GBS, "hbm"))
     iters = 4096
     for blocks in (512, 1024):
         ops = blocks * 4 * iters * 4 * 2.0 * 32 * 32 * 32
@@ -561,12 +568,15 @@ def main():
                                 for k in summaries if k.startswith("ceiling_empty_kernel_")},
             "stream_read_gbs": summaries["ceiling_stream_read_6713344B"]["value"],
             "stream_read_us_per_launch": summaries["ceiling_stream_read_6713344B"]["us_per_launch"],
+            "stream_read_write_gbs": summaries["ceiling_stream_read_write_6713344B"]["value"],
+            "stream_read_write_us_per_launch": summaries["ceiling_stream_read_write_6713344B"]["us_per_launch"],
             "mfma_i8_tops": max(s["value"] for k, s in summaries.items() if k.startswith("ceiling_mfma_i8_")),
             "valu_ginstr_per_s": max(s["value"] for k, s in summaries.items()
                                      if k.startswith("ceiling_valu_mad_i24_")),
             "how": "ceilings/ceilings.hip, timed in this run: empty kernels (1000 per graph) with 1x64 lanes and "
                    "with the decode GEMV's 512x256 grid; a cold read of 6,713,344 B per launch (80 buffers "
-                   "rotated, the GEMV's grid); back-to-back v_mfma_i32_32x32x32_i8 with 4 independent "
+                   "rotated, the GEMV's grid), and the same with the GEMV's traffic split as it is (6,688,768 B "
+                   "read, 12,288 bf16 written); back-to-back v_mfma_i32_32x32x32_i8 with 4 independent "
                    "accumulators; back-to-back v_mad_i32_i24 in 8 independent chains (best of two grid sizes)"}
 
     result = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -587,7 +597,8 @@ def main():
                               "warm_gbs": summaries.get("decode_gemv_m1_warm", {}).get("value")}
         if ceil:
             result["roofline"]["ceilings"] = ceil
-            result["roofline"]["frac_of_ceiling"] = round(s["value"] / ceil["stream_read_gbs"], 4)
+            result["roofline"]["frac_of_ceiling"] = round(s["value"] / ceil["stream_read_write_gbs"], 4)
+            result["roofline"]["ceiling_kernel"] = "stream_read_write_kernel"
     if "prefill_mmq_m2048" in summaries:
         s = summaries["prefill_mmq_m2048"]
         result["prefill"] = {"metric": "Q2_0 MMQ prefill int8 TOPS (2mnk / kernel time), m=2048 n=12288 k=2048",

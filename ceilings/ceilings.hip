@@ -40,6 +40,31 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restric
   if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
 }
 
+// The same read, then every workgroup writes its share of `outs` 2-byte
+// values (the decode GEMV's output: one bf16 per weight row), each a fold of
+// the lane's loaded words: the GEMV's whole memory traffic with its grid,
+// and no arithmetic.
+__global__ __launch_bounds__(256) void stream_read_write_kernel(const uint4 *__restrict__ src, uint64_t chunks,
+                                                                uint16_t *__restrict__ dst, uint32_t outs) {
+  const uint64_t per = (chunks + gridDim.x - 1) / gridDim.x;
+  const uint64_t begin = (uint64_t)blockIdx.x * per;
+  const uint64_t end = begin + per < chunks ? begin + per : chunks;
+  uint32_t x = 0;
+  if (begin < end) {
+    uint4 v[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const uint64_t i = begin + threadIdx.x + (uint64_t)j * blockDim.x;
+      v[j] = src[i < end ? i : end - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) x ^= v[j].x ^ (v[j].y * 3u) ^ (v[j].z * 5u) ^ (v[j].w * 7u);
+  }
+  const uint32_t per_out = (outs + gridDim.x - 1) / gridDim.x;
+  const uint32_t o = blockIdx.x * per_out + threadIdx.x;
+  if (threadIdx.x < per_out && o < outs) dst[o] = (uint16_t)(x & 0x7FFFu);
+}
+
 // Back-to-back v_mfma_i32_32x32x32_i8 with four independent accumulators per
 // wave (no dependent chain, no memory traffic in the loop): the int8 matrix
 // core's issue rate.
@@ -95,6 +120,16 @@ int ceil_stream_read(const void *src, uint64_t bytes, void *sink, uint32_t block
   if (bytes % 16u != 0 || bytes > (uint64_t)blocks * 256u * kLoads * 16u) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4 *>(src), bytes / 16u, static_cast<uint32_t *>(sink));
+  return (int)hipGetLastError();
+}
+
+// As ceil_stream_read, then `outs` 2-byte values written to dst (outs <= blocks * 256).
+int ceil_stream_read_write(const void *src, uint64_t bytes, void *dst, uint32_t outs, uint32_t blocks,
+                           void *stream) {
+  if (bytes % 16u != 0 || bytes > (uint64_t)blocks * 256u * kLoads * 16u || outs > blocks * 256u)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_read_write_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4 *>(src), bytes / 16u, static_cast<uint16_t *>(dst), outs);
   return (int)hipGetLastError();
 }
 

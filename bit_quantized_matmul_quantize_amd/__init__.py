@@ -16,7 +16,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbqmm.so")
+# BQMM_SANITIZE=1 selects the host-sanitized build of the same library (see
+# build.py); it is for the CPU test suite only.
+LIB_PATH = os.path.join(_HERE, "libbqmm_san.so" if os.environ.get("BQMM_SANITIZE") == "1" else "libbqmm.so")
 
 BQ_OK, BQ_EINVAL, BQ_EUNSUPPORTED, BQ_EALIGN, BQ_EHIP = 0, -1, -2, -3, -4
 

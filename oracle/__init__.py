@@ -18,16 +18,28 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# BQMM_SANITIZE=1 selects an AddressSanitizer + UndefinedBehaviorSanitizer
+# build (clang, whose runtime the sanitized C ABI library shares); it is for
+# the CPU test suite only (tests/run_sanitized.sh).
+_SANITIZE = os.environ.get("BQMM_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
+_CLANG = os.environ.get("BQMM_CLANG", "/opt/rocm/llvm/bin/clang")
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc (plain -O2, no fast-math)."""
+    """Compile oracle.c into liboracle.so with gcc (plain -O2, no fast-math),
+    or, under BQMM_SANITIZE=1, into liboracle_san.so with clang and the
+    address and undefined-behaviour sanitizers."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-fPIC", "-shared",
-                               _SRC, "-o", tmp, "-lm"])
+        if _SANITIZE:
+            cmd = [_CLANG, "-std=c11", "-O1", "-g", "-Wall", "-Wextra", "-fPIC", "-shared",
+                   "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+                   "-shared-libsan", _SRC, "-o", tmp, "-lm"]
+        else:
+            cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 

@@ -170,7 +170,7 @@ int64_t oracle_quantize_act_q8_1(const uint16_t *act, uint8_t *out, uint32_t m, 
                     float t = roundf(x[i] / d);
                     if (t > 127.0f) t = 127.0f;
                     if (t < -127.0f) t = -127.0f;
-                    q = (int32_t)t;
+                    q = t == t ? (int32_t)t : 0; /* NaN (a flagged block): 0, not undefined */
                 }
                 out[r * kp + b * 32u + (uint64_t)i] = (uint8_t)(int8_t)q;
                 sum += q;
@@ -549,13 +549,16 @@ int64_t oracle_quantize_weight_q4k(const uint16_t *wb, uint8_t *out, uint32_t n,
             for (int j = 0; j < 8; ++j) {
                 sc[j] = 0u;
                 mn[j] = 0u;
+                /* a NaN quotient (only for a block outside the supported
+                 * range, whose bytes are unspecified) gives 0 rather than an
+                 * undefined float-to-unsigned conversion */
                 if (d > 0.0f) {
                     float t = roundf(S[j] / d);
-                    sc[j] = t > 63.0f ? 63u : (uint32_t)t;
+                    sc[j] = !(t > 0.0f) ? 0u : (t > 63.0f ? 63u : (uint32_t)t);
                 }
                 if (dmin > 0.0f) {
                     float t = roundf(M[j] / dmin);
-                    mn[j] = t > 63.0f ? 63u : (uint32_t)t;
+                    mn[j] = !(t > 0.0f) ? 0u : (t > 63.0f ? 63u : (uint32_t)t);
                 }
             }
             /* header: fp16 d, fp16 dmin, then the twelve scale/min bytes */
@@ -579,7 +582,7 @@ int64_t oracle_quantize_weight_q4k(const uint16_t *wb, uint8_t *out, uint32_t n,
                 uint32_t q = 0u;
                 if (step > 0.0f) {
                     float t = roundf((x[e] + off) / step);
-                    q = t < 0.0f ? 0u : (t > 15.0f ? 15u : (uint32_t)t);
+                    q = !(t > 0.0f) ? 0u : (t > 15.0f ? 15u : (uint32_t)t);
                 }
                 int t64 = e / 64, within = e % 64;
                 uint8_t *b = blk + 16 + 32 * t64 + (within % 32);

@@ -21,15 +21,22 @@
 // m_j) for the eight sub-blocks and B = their stored sums s, accumulating
 // into the output registers.
 //
-// Tile 128 (n) x 256 (m), 512 lanes = 8 waves of 64 (n) x 64 (m); k is staged
-// 64 at a time (one 64-weight chunk of a super-block: sub-block 2t in the low
-// nibbles, 2t + 1 in the high nibbles of the same 32 bytes) through two LDS
-// stages, both operands converted to binary16 once per workgroup while they
-// are written: the q8_1 codes by an exponent-bias trick (bytes xor 0x80 under
-// the exponent of 1024, then one packed subtraction of 1152), the 4-bit codes
-// likewise times sc_j with one packed fma.  The MFMA of step i + 1 is issued
-// before the fold of step i, and the compute is last in the loop body (see
-// the Q2_0 kernel for why).
+// Tile 128 (n) x 128 (m), 256 lanes = 4 waves of 64 (n) x 64 (m), two
+// workgroups per CU (76,800 bytes of LDS each); k is staged 64 at a time
+// (one 64-weight chunk of a super-block: sub-block 2t in the low nibbles,
+// 2t + 1 in the high nibbles of the same 32 bytes) through two LDS stages,
+// both operands converted to binary16 once per workgroup while they are
+// written: the q8_1 codes by an exponent-bias trick (bytes xor 0x80 under the
+// exponent of 1024, then one packed subtraction of 1152), the 4-bit codes
+// likewise times sc_j with one packed fma.  Staged rows are 128 bytes with
+// their 16-byte chunks XOR-swizzled by the row's low bits instead of padded,
+// which keeps the operand reads free of bank conflicts and lets two
+// workgroups share a CU.  (A 256 (m) x 128 (n) tile of eight waves, one
+// workgroup per CU, measured 1-9% slower; so did splitting the eight waves
+// into four that stage and four that compute, and 16 x 16 x 32 MFMA
+// subtiles, which run at half the 32 x 32 x 16 rate here.)  The MFMA of step
+// i + 1 is issued before the fold of step i, and the compute is last in the
+// loop body (see the Q2_0 kernel for why).
 #include "bqmm_internal.h"
 
 namespace bqmm {
@@ -41,10 +48,10 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BN = 128;
-constexpr int BM = 256;
+constexpr int BM = 128;
 constexpr int KS = 64;                       // k per stage: one chunk of a super-block
-constexpr int ROW = 2 * KS + 16;             // bytes per staged binary16 row; the pad spreads banks
-constexpr int kThreads = 512;
+constexpr int ROW = 2 * KS;                  // bytes per staged binary16 row (16-byte chunks swizzled)
+constexpr int kThreads = 256;
 // one LDS stage
 constexpr int kActBytes = BM * ROW;          // activation codes, binary16
 constexpr int kWBytes = BN * ROW;            // q4 * sc_j, binary16
@@ -57,6 +64,11 @@ constexpr int kSbNmin = kSbD + BN * 4;
 constexpr int kSbS = kSbNmin + BN * 16;
 constexpr int kSbBytes = kSbS + BM * 16;
 constexpr int kLdsBytes = 2 * kStageBytes + 2 * kSbBytes;
+
+// Byte offset of 16-byte chunk c of staged row r: the chunk index is XOR-ed
+// with the row's low three bits, so eight consecutive rows read or written
+// at one chunk index hit eight different bank groups (no padding needed).
+__device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * ROW + 16u * (c ^ (r & 7u)); }
 
 __device__ __forceinline__ uint32_t sbyte(const uint32_t S[3], int i) { return (S[i >> 2] >> (8 * (i & 3))) & 0xFFu; }
 
@@ -92,7 +104,7 @@ __device__ __forceinline__ void u4x4_to_f16(uint32_t x, v2h sc, v2h nsc1024, uin
 }
 
 template <bool kDump>
-__global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
+__global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
     const uint8_t *__restrict__ act_q8, const uint8_t *__restrict__ w, uint16_t *__restrict__ out,
     int32_t *__restrict__ dots, uint32_t m, uint32_t n, uint32_t k, uint32_t m0, uint32_t mt,
     uint32_t n0, uint32_t nt, uint32_t tile_n0, uint32_t tile_m0, uint32_t ldc) {
@@ -102,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u, l32 = lane & 31u, hi = lane >> 5;
   const uint32_t wave = tid >> 6;
-  const uint32_t wn = wave & 1u, wm = wave >> 1;  // wm in 0..3
+  const uint32_t wn = wave & 1u, wm = wave >> 1;  // wm in 0..1
   const uint32_t n_base = (blockIdx.x + tile_n0) * BN;
   const uint32_t m_base = (blockIdx.y + tile_m0) * BM;
   const uint32_t kpad = (k + 255u) / 256u * 256u;
@@ -113,25 +125,26 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
 
   // Global -> register staging; rows past m or n read the last valid row.
   //   activation codes: thread -> row tid / 2, bytes 32 * (tid % 2) of the stage;
-  //   weight codes: thread -> row tid / 4, bytes 8 * (tid % 4) of the chunk,
-  //     plus its row's 16-byte header (d, dmin, packed sub-scales/mins);
-  //   activation (d, s): threads 256.. -> row tid - 256, the stage's two blocks.
-  const uint32_t a_row = min(m_base + (tid >> 1), m - 1u), a_half = tid & 1u;
-  const uint32_t w_row = min(n_base + (tid >> 2), n - 1u), w_part = tid & 3u;
-  const uint32_t s_row = min(m_base + (tid - 256u), m - 1u);
-  uint4 ra0, ra1, rh;
-  uint2 rw, rds = make_uint2(0, 0);
+  //   weight codes: thread -> row tid / 2, all 32 bytes of the chunk, of which
+  //     it converts the low (tid % 2 = 0) or the high nibbles, plus its row's
+  //     16-byte header (d, dmin, packed sub-scales/mins);
+  //   activation (d, s): thread -> row tid / 2, block tid % 2 of the stage.
+  const uint32_t srow = tid >> 1, sel = tid & 1u;
+  const uint32_t a_row = min(m_base + srow, m - 1u);
+  const uint32_t w_row = min(n_base + srow, n - 1u);
+  uint4 ra0, ra1, rh, rw0, rw1;
+  uint32_t rds;
 #define BQMM_FETCH(st)                                                                                  \
   do {                                                                                                  \
     const uint32_t sb_ = (st) >> 2, t_ = (st) & 3u;                                                     \
-    const uint8_t *ap_ = act_q8 + (uint64_t)a_row * kpad + (st) * KS + 32u * a_half;                   \
+    const uint8_t *ap_ = act_q8 + (uint64_t)a_row * kpad + (st) * KS + 32u * sel;                      \
     ra0 = *reinterpret_cast<const uint4 *>(ap_);                                                        \
     ra1 = *reinterpret_cast<const uint4 *>(ap_ + 16);                                                   \
     const uint8_t *bp_ = w + ((uint64_t)w_row * nsb + sb_) * 144u;                                      \
     rh = *reinterpret_cast<const uint4 *>(bp_);                                                         \
-    rw = *reinterpret_cast<const uint2 *>(bp_ + 16u + 32u * t_ + 8u * w_part);                          \
-    if (tid >= 256u)                                                                                    \
-      rds = *reinterpret_cast<const uint2 *>(ds + 4ull * ((uint64_t)s_row * nblk_pad + 2u * (st)));    \
+    rw0 = *reinterpret_cast<const uint4 *>(bp_ + 16u + 32u * t_);                                       \
+    rw1 = *reinterpret_cast<const uint4 *>(bp_ + 32u + 32u * t_);                                       \
+    rds = *reinterpret_cast<const uint32_t *>(ds + 4ull * ((uint64_t)a_row * nblk_pad + 2u * (st) + sel)); \
   } while (0)
 
   // Write the prefetched stage into LDS stage buffer `buf`; stage st of
@@ -146,48 +159,45 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
       uint32_t h[16];                                                                                   \
       const uint32_t x_[8] = {ra0.x, ra0.y, ra0.z, ra0.w, ra1.x, ra1.y, ra1.z, ra1.w};                  \
       _Pragma("unroll") for (int i = 0; i < 8; ++i) s8x4_to_f16(x_[i], h[2 * i], h[2 * i + 1]);         \
-      uint8_t *ar = L + (tid >> 1) * ROW + 64u * a_half;                                                \
       _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                     \
-        *reinterpret_cast<uint4 *>(ar + 16 * i) = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]); \
+        *reinterpret_cast<uint4 *>(L + swz(srow, 4u * sel + i)) =                                       \
+            make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);                             \
     }                                                                                                   \
     {                                                                                                   \
       const uint32_t S_[3] = {rh.y, rh.z, rh.w};                                                        \
-      uint32_t sc0_, sc1_, mn0_, mn1_;                                                                  \
-      scale_min(S_, 2 * (int)t_, sc0_, mn0_);                                                           \
-      scale_min(S_, 2 * (int)t_ + 1, sc1_, mn1_);                                                       \
-      if (kDump) sc0_ = sc1_ = 1u;                                                                      \
-      const _Float16 f0_ = (_Float16)(float)sc0_, f1_ = (_Float16)(float)sc1_;                          \
-      const v2h s0_ = {f0_, f0_}, s1_ = {f1_, f1_};                                                     \
-      const v2h n0_ = {(_Float16)(-1024.0f * (float)sc0_), (_Float16)(-1024.0f * (float)sc0_)};         \
-      const v2h n1_ = {(_Float16)(-1024.0f * (float)sc1_), (_Float16)(-1024.0f * (float)sc1_)};         \
-      uint32_t lo_[4], hi_[4];                                                                          \
-      u4x4_to_f16(rw.x & 0x0F0F0F0Fu, s0_, n0_, lo_[0], lo_[1]);                                        \
-      u4x4_to_f16(rw.y & 0x0F0F0F0Fu, s0_, n0_, lo_[2], lo_[3]);                                        \
-      u4x4_to_f16((rw.x >> 4) & 0x0F0F0F0Fu, s1_, n1_, hi_[0], hi_[1]);                                 \
-      u4x4_to_f16((rw.y >> 4) & 0x0F0F0F0Fu, s1_, n1_, hi_[2], hi_[3]);                                 \
-      uint8_t *wr = L + kActBytes + (tid >> 2) * ROW + 16u * w_part;                                    \
-      *reinterpret_cast<uint4 *>(wr) = make_uint4(lo_[0], lo_[1], lo_[2], lo_[3]);                      \
-      *reinterpret_cast<uint4 *>(wr + 64) = make_uint4(hi_[0], hi_[1], hi_[2], hi_[3]);                 \
+      uint32_t sc_, mn_;                                                                                \
+      scale_min(S_, 2 * (int)t_ + (int)sel, sc_, mn_);                                                  \
+      if (kDump) sc_ = 1u;                                                                              \
+      const _Float16 f_ = (_Float16)(float)sc_;                                                         \
+      const v2h s_ = {f_, f_};                                                                          \
+      const v2h n_ = {(_Float16)(-1024.0f * (float)sc_), (_Float16)(-1024.0f * (float)sc_)};            \
+      const uint32_t x_[8] = {rw0.x, rw0.y, rw0.z, rw0.w, rw1.x, rw1.y, rw1.z, rw1.w};                  \
+      const uint32_t sh_ = 4u * sel;                                                                    \
+      uint32_t o_[16];                                                                                  \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                     \
+        u4x4_to_f16((x_[i] >> sh_) & 0x0F0F0F0Fu, s_, n_, o_[2 * i], o_[2 * i + 1]);                    \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                     \
+        *reinterpret_cast<uint4 *>(L + kActBytes + swz(srow, 4u * sel + i)) =                           \
+            make_uint4(o_[4 * i], o_[4 * i + 1], o_[4 * i + 2], o_[4 * i + 3]);                         \
       if (!kDump && t_ == 0u) {                                                                         \
-        /* the four lanes of a row each write two of its eight min-term    */                          \
-        /* operands (sub-blocks t_ and t_ + 4, so one unpack form serves); */                          \
-        /* all four write the same d                                        */                          \
+        /* the two lanes of a row each write four of its eight min-term     */                          \
+        /* operands (sub-blocks 2 sel, 2 sel + 1 and those plus 4, so that   */                         \
+        /* each unpack form is known at compile time); both write d         */                          \
         const float d_ = f16_bits_to_f32(rh.x & 0xFFFFu), dmin_ = f16_bits_to_f32(rh.x >> 16);         \
-        reinterpret_cast<float *>(SB + kSbD)[tid >> 2] = d_;                                            \
-        uint32_t sca_, mna_, scb_, mnb_;                                                                \
-        scale_min(S_, (int)w_part, sca_, mna_);                                                         \
-        scale_min(S_, (int)w_part + 4, scb_, mnb_);                                                     \
-        _Float16 *nm_ = reinterpret_cast<_Float16 *>(SB + kSbNmin + (tid >> 2) * 16);                   \
-        nm_[w_part] = (_Float16)(-dmin_ * (float)mna_);                                                 \
-        nm_[w_part + 4] = (_Float16)(-dmin_ * (float)mnb_);                                             \
+        reinterpret_cast<float *>(SB + kSbD)[srow] = d_;                                                \
+        _Float16 *nm_ = reinterpret_cast<_Float16 *>(SB + kSbNmin + srow * 16);                         \
+        _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                                 \
+          const int j_ = 2 * (int)sel + q;                                                              \
+          uint32_t sca_, mna_, scb_, mnb_;                                                              \
+          scale_min(S_, j_, sca_, mna_);                                                                \
+          scale_min(S_, j_ + 4, scb_, mnb_);                                                            \
+          nm_[j_] = (_Float16)(-dmin_ * (float)mna_);                                                   \
+          nm_[j_ + 4] = (_Float16)(-dmin_ * (float)mnb_);                                               \
+        }                                                                                               \
       }                                                                                                 \
     }                                                                                                   \
-    if (tid >= 256u) {                                                                                  \
-      const uint32_t r_ = tid - 256u;                                                                   \
-      *reinterpret_cast<float2 *>(L + kDaOff + r_ * 8) =                                                \
-          make_float2(f16_bits_to_f32(rds.x & 0xFFFFu), f16_bits_to_f32(rds.y & 0xFFFFu));              \
-      *reinterpret_cast<uint32_t *>(SB + kSbS + r_ * 16 + 4 * t_) = (rds.x >> 16) | (rds.y & 0xFFFF0000u); \
-    }                                                                                                   \
+    reinterpret_cast<float *>(L + kDaOff)[2u * srow + sel] = f16_bits_to_f32(rds & 0xFFFFu);           \
+    reinterpret_cast<uint16_t *>(SB + kSbS)[8u * srow + 2u * t_ + sel] = (uint16_t)(rds >> 16);         \
   } while (0)
 
   v16f acc_out[2][2], acc_sb[2][2];
@@ -224,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
         const uint32_t ml = wm * 64 + sm * 32 + l32;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          B[sm][h] = *reinterpret_cast<const v8h *>(a_lds + ml * ROW + 64 * b + 32 * h + 16 * hi);
+          B[sm][h] = *reinterpret_cast<const v8h *>(a_lds + swz(ml, 4 * b + 2 * h + hi));
         da[sm][b] = reinterpret_cast<const float *>(L + kDaOff)[ml * 2 + b];
       }
 #pragma unroll
@@ -232,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 1) void q4k_mmq_kernel(
         const uint32_t nl = wn * 64 + sn * 32 + l32;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          A[sn][h] = *reinterpret_cast<const v8h *>(w_lds + nl * ROW + 64 * b + 32 * h + 16 * hi);
+          A[sn][h] = *reinterpret_cast<const v8h *>(w_lds + swz(nl, 4 * b + 2 * h + hi));
       }
     };
 #pragma unroll

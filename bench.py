@@ -18,7 +18,8 @@ graph and replayed between HIP events:
              (dequant + dense GEMM) at both m;
   ffn      : m=4096 FFN prefill, Q2_0 and Q4_K: quantize, gate and up MMQ
              (sharing the quantized input), silu_mul fused into the down
-             projection's quantization, down MMQ;
+             projection's quantization, down MMQ; each format against the
+             peak of the MFMA it contracts on (int8 for Q2_0, fp16 for Q4_K);
   q4k      : Q4_K decode GEMV (m=1) on the FFN gate [17408, 5120] and down
              [5120, 17408] shapes, each weight rotated through 8 copies
              (401 MB); and the Q4_K weight quantizer on a bf16 [17408, 5120]
@@ -27,8 +28,9 @@ graph and replayed between HIP events:
              a library of its own): an empty kernel (the launch floor, one
              workgroup and the decode GEMV's grid), a cold streaming read of
              the decode GEMV's 6,713,344 bytes per launch with its grid
-             (rotated through 80 buffers), back-to-back int8 MFMAs, and
-             back-to-back 24-bit integer multiply-adds on the vector ALU;
+             (rotated through 80 buffers), back-to-back int8 and fp16 MFMAs
+             (the Q2_0 and the Q4_K MMQ's instructions), and back-to-back
+             24-bit integer multiply-adds on the vector ALU;
   copy     : (not in the default set) a plain 256 MiB device-to-device copy,
              the known-size reference for the HBM byte counters.
 The JSON line reports the decode GEMV (the workload the headline metric is
@@ -55,6 +57,7 @@ METRIC = "Q2_0 MMQ prefill int8 TOPS + GEMV decode HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5033.0      # MI355X dense int8 MFMA, published (no sparsity)
 BF16_PEAK_TFLOPS = 2516.0    # MI355X dense bf16 MFMA, published
+FP16_PEAK_TFLOPS = 2516.0    # MI355X dense fp16 MFMA, published (the Q4_K MMQ contracts in fp16)
 VALU_PEAK_GINSTR = 256 * 4 * 2.4e9 / 4 / 1e9  # wave64 VALU instructions/s: 4 SIMDs/CU, 4 cycles each
 
 DECODE_CALLS = 1000
@@ -304,8 +307,9 @@ def ffn_legs(bq, dev, F):
     up = torch.empty((m, I), dtype=torch.bfloat16, device=dev)
     out = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
     legs = []
-    for fmt, key, gemm, kname in (("q2_0", "q2", bq.q2_0_mmq_gemm, "q2_0_mmq_kernel"),
-                                  ("q4k", "q4k", bq.q4k_mmq_gemm, "q4k_mmq_kernel")):
+    # each format against the peak of the MFMA type its contraction runs on
+    for fmt, key, gemm, kname, peak in (("q2_0", "q2", bq.q2_0_mmq_gemm, "q2_0_mmq_kernel", INT8_PEAK_TOPS),
+                                        ("q4k", "q4k", bq.q4k_mmq_gemm, "q4k_mmq_kernel", FP16_PEAK_TFLOPS)):
         wg, wu, wd = (torch.from_numpy(F[key][name]).to(dev) for name in ("wg", "wu", "wd"))
 
         def ffn(wg=wg, wu=wu, wd=wd, gemm=gemm):
@@ -317,11 +321,11 @@ def ffn_legs(bq, dev, F):
 
         keep = [wg, wu, wd, x, q8a, q8h, gate, up, out]
         legs.append(Leg(f"ffn_prefill_{fmt}_m4096", ffn, keep, 5, 3 * 2.0 * m * H * I, "TOPS",
-                        f"{kname} x3 + quantize + silu_mul_quantize", INT8_PEAK_TOPS, "mfma"))
+                        f"{kname} x3 + quantize + silu_mul_quantize", peak, "mfma"))
         legs.append(Leg(f"ffn_gate_proj_{fmt}_m4096", lambda wg=wg, gemm=gemm: gemm(q8a, wg, gate, m, I, H),
-                        keep, 1, 2.0 * m * H * I, "TOPS", kname, INT8_PEAK_TOPS, "mfma"))
+                        keep, 1, 2.0 * m * H * I, "TOPS", kname, peak, "mfma"))
         legs.append(Leg(f"ffn_down_proj_{fmt}_m4096", lambda wd=wd, gemm=gemm: gemm(q8h, wd, out, m, H, I),
-                        keep, 1, 2.0 * m * H * I, "TOPS", kname, INT8_PEAK_TOPS, "mfma"))
+                        keep, 1, 2.0 * m * H * I, "TOPS", kname, peak, "mfma"))
     return legs
 
 
@@ -392,6 +396,11 @@ def ceiling_legs(dev, gemv_blocks):
         legs.append(Leg(f"ceiling_mfma_i8_{blocks}x256",
                         lambda b=blocks: ceilings.call("ceil_mfma_i8", b, iters, sink.data_ptr(), stream()),
                         [sink], 1, ops, "TOPS", "v_mfma_i32_32x32x32_i8 loop", INT8_PEAK_TOPS, "mfma"))
+    for blocks in (512, 1024):
+        ops = blocks * 4 * iters * 4 * 2.0 * 32 * 32 * 16
+        legs.append(Leg(f"ceiling_mfma_f16_{blocks}x256",
+                        lambda b=blocks: ceilings.call("ceil_mfma_f16", b, iters, sink.data_ptr(), stream()),
+                        [sink], 1, ops, "TOPS", "v_mfma_f32_32x32x16_f16 loop", FP16_PEAK_TFLOPS, "mfma"))
     viters = 8192
     for blocks in (1024, 2048):
         instr = blocks * 4 * viters * 8
@@ -571,13 +580,22 @@ def main():
             "stream_read_write_gbs": summaries["ceiling_stream_read_write_6713344B"]["value"],
             "stream_read_write_us_per_launch": summaries["ceiling_stream_read_write_6713344B"]["us_per_launch"],
             "mfma_i8_tops": max(s["value"] for k, s in summaries.items() if k.startswith("ceiling_mfma_i8_")),
+            "mfma_f16_tflops": max(s["value"] for k, s in summaries.items() if k.startswith("ceiling_mfma_f16_")),
             "valu_ginstr_per_s": max(s["value"] for k, s in summaries.items()
                                      if k.startswith("ceiling_valu_mad_i24_")),
             "how": "ceilings/ceilings.hip, timed in this run: empty kernels (1000 per graph) with 1x64 lanes and "
                    "with the decode GEMV's 512x256 grid; a cold read of 6,713,344 B per launch (80 buffers "
                    "rotated, the GEMV's grid), and the same with the GEMV's traffic split as it is (6,688,768 B "
-                   "read, 12,288 bf16 written); back-to-back v_mfma_i32_32x32x32_i8 with 4 independent "
-                   "accumulators; back-to-back v_mad_i32_i24 in 8 independent chains (best of two grid sizes)"}
+                   "read, 12,288 bf16 written); back-to-back v_mfma_i32_32x32x32_i8 and, apart, "
+                   "v_mfma_f32_32x32x16_f16 with 4 independent accumulators; back-to-back v_mad_i32_i24 in 8 independent chains (best of two grid sizes)"}
+
+        # each MMQ leg against the measured rate of the MFMA it runs on
+        for s in summaries.values():
+            k = s.get("kernel", "")
+            c = (ceil["mfma_f16_tflops"] if k.startswith("q4k_mmq") else
+                 ceil["mfma_i8_tops"] if k.startswith(("q2_0_mmq", "quantize_q8_1_kernel + q2_0_mmq")) else None)
+            if c:
+                s["frac_of_ceiling"] = round(s["value"] / c, 4)
 
     result = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True,

@@ -32,7 +32,8 @@ def lib():
         P, U32, U64 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64
         for name, args in (("ceil_empty", [U32, U32, P]), ("ceil_stream_read", [P, U64, P, U32, P]),
                            ("ceil_stream_read_write", [P, U64, P, U32, U32, P]),
-                           ("ceil_mfma_i8", [U32, U32, P, P]), ("ceil_valu_mad", [U32, U32, P, P])):
+                           ("ceil_mfma_i8", [U32, U32, P, P]), ("ceil_mfma_f16", [U32, U32, P, P]),
+                           ("ceil_valu_mad", [U32, U32, P, P])):
             f = getattr(l, name)
             f.restype = ctypes.c_int
             f.argtypes = args

@@ -10,6 +10,8 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 // Nothing: the cost of dispatching a grid and retiring it.
 __global__ void empty_kernel() {}
@@ -85,6 +87,29 @@ __global__ __launch_bounds__(256) void mfma_i8_kernel(uint32_t iters, int seed, 
   if (s == 0x7FEDCBA9) sink[blockIdx.x] = s;
 }
 
+// The same for v_mfma_f32_32x32x16_f16, the instruction the Q4_K MMQ runs on:
+// the fp16 matrix core's issue rate.
+__global__ __launch_bounds__(256) void mfma_f16_kernel(uint32_t iters, int seed, int *__restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  v8h a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (_Float16)(float)((seed + lane + j) & 7);
+    b[j] = (_Float16)(float)((lane * 3 + j) & 7);
+  }
+  v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (uint32_t i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, b, c3, 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  if (s == -1.0f) sink[blockIdx.x] = (int)s;
+}
+
 // Independent chains of the integer multiply-add the Q2_0 MMQ folds with
 // (v_mad_i32_i24): eight chains per lane, so each instruction's result is
 // not awaited by the next; the vector ALU's issue rate.
@@ -136,6 +161,13 @@ int ceil_stream_read_write(const void *src, uint64_t bytes, void *dst, uint32_t 
 // Work per launch: blocks * 4 waves * iters * 4 MFMAs * 2*32*32*32 int8 ops.
 int ceil_mfma_i8(uint32_t blocks, uint32_t iters, void *sink, void *stream) {
   hipLaunchKernelGGL(mfma_i8_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, 12345,
+                     static_cast<int *>(sink));
+  return (int)hipGetLastError();
+}
+
+// Work per launch: blocks * 4 waves * iters * 4 MFMAs * 2*32*32*16 fp16 flops.
+int ceil_mfma_f16(uint32_t blocks, uint32_t iters, void *sink, void *stream) {
+  hipLaunchKernelGGL(mfma_f16_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, 12345,
                      static_cast<int *>(sink));
   return (int)hipGetLastError();
 }

@@ -29,8 +29,10 @@ graph and replayed between HIP events:
              workgroup and the decode GEMV's grid), a cold streaming read of
              the decode GEMV's 6,713,344 bytes per launch with its grid
              (rotated through 80 buffers), back-to-back int8 and fp16 MFMAs
-             (the Q2_0 and the Q4_K MMQ's instructions), and back-to-back
-             24-bit integer multiply-adds on the vector ALU;
+             (the Q2_0 and the Q4_K MMQ's instructions), back-to-back 24-bit
+             integer multiply-adds on the vector ALU, the MFMA loops with the
+             MMQs' numbers of VALU instructions per MFMA interleaved, and LDS
+             read and write bandwidth;
   copy     : (not in the default set) a plain 256 MiB device-to-device copy,
              the known-size reference for the HBM byte counters.
 The JSON line reports the decode GEMV (the workload the headline metric is
@@ -362,8 +364,8 @@ def q4k_legs(bq, dev, Q):
 
 def ceiling_legs(dev, gemv_blocks):
     """Measured ceilings (ceilings/ceilings.hip): launch floor, cold streaming
-    read of the decode GEMV's bytes with its grid, int8 MFMA and VALU
-    issue rates."""
+    read of the decode GEMV's bytes with its grid, int8 and fp16 MFMA and
+    VALU issue rates, MFMA rates at the MMQs' VALU mixes, LDS bandwidth."""
     import torch
     import ceilings
 
@@ -407,6 +409,24 @@ def ceiling_legs(dev, gemv_blocks):
         legs.append(Leg(f"ceiling_valu_mad_i24_{blocks}x256",
                         lambda b=blocks: ceilings.call("ceil_valu_mad", b, viters, sink.data_ptr(), stream()),
                         [sink], 1, instr, "Ginstr/s", "v_mad_i32_i24 loop", VALU_PEAK_GINSTR, "valu"))
+    # the MMQs' instruction mixes: four MFMAs and 4v multiply-adds per iteration
+    # (v = 24: the Q2_0 fold's VALU per int8 MFMA; 33: that kernel's whole mix;
+    # 18: the Q4_K kernel's per fp16 MFMA), two waves per SIMD as in the kernels
+    miters = 1024
+    for f16, per4, label in ((0, 96, "i8_24valu"), (0, 132, "i8_33valu"), (1, 72, "f16_18valu")):
+        ops = 512 * 4 * miters * 4 * 2.0 * 32 * 32 * (16 if f16 else 32)
+        legs.append(Leg(f"ceiling_mix_{label}_512x256",
+                        lambda f=f16, v=per4: ceilings.call("ceil_mix", 512, miters, f, v, sink.data_ptr(), stream()),
+                        [sink], 1, ops, "TOPS",
+                        f"{'v_mfma_f32_32x32x16_f16' if f16 else 'v_mfma_i32_32x32x32_i8'} + {per4 // 4} "
+                        f"v_mad_i32_i24 per MFMA", FP16_PEAK_TFLOPS if f16 else INT8_PEAK_TOPS, "mfma"))
+    # LDS bandwidth, 16-byte accesses by every lane, two workgroups per CU
+    liters = 2048
+    for write in (0, 1):
+        nbytes = 512 * 256 * liters * 16 * 16
+        legs.append(Leg(f"ceiling_lds_{'write' if write else 'read'}_b128",
+                        lambda w=write: ceilings.call("ceil_lds", 512, liters, w, sink.data_ptr(), stream()),
+                        [sink], 1, nbytes, "GB/s", f"ds_{'write' if write else 'read'}_b128 loop", None, "lds"))
     return legs
 
 
@@ -583,11 +603,19 @@ def main():
             "mfma_f16_tflops": max(s["value"] for k, s in summaries.items() if k.startswith("ceiling_mfma_f16_")),
             "valu_ginstr_per_s": max(s["value"] for k, s in summaries.items()
                                      if k.startswith("ceiling_valu_mad_i24_")),
+            "mfma_i8_with_24_valu_tops": summaries["ceiling_mix_i8_24valu_512x256"]["value"],
+            "mfma_i8_with_33_valu_tops": summaries["ceiling_mix_i8_33valu_512x256"]["value"],
+            "mfma_f16_with_18_valu_tflops": summaries["ceiling_mix_f16_18valu_512x256"]["value"],
+            "lds_read_gbs": summaries["ceiling_lds_read_b128"]["value"],
+            "lds_write_gbs": summaries["ceiling_lds_write_b128"]["value"],
             "how": "ceilings/ceilings.hip, timed in this run: empty kernels (1000 per graph) with 1x64 lanes and "
                    "with the decode GEMV's 512x256 grid; a cold read of 6,713,344 B per launch (80 buffers "
                    "rotated, the GEMV's grid), and the same with the GEMV's traffic split as it is (6,688,768 B "
                    "read, 12,288 bf16 written); back-to-back v_mfma_i32_32x32x32_i8 and, apart, "
-                   "v_mfma_f32_32x32x16_f16 with 4 independent accumulators; back-to-back v_mad_i32_i24 in 8 independent chains (best of two grid sizes)"}
+                   "v_mfma_f32_32x32x16_f16 with 4 independent accumulators; back-to-back v_mad_i32_i24 in 8 "
+                   "independent chains (best of two grid sizes); the MFMA loops with 24 or 33 (int8) and 18 (fp16) independent v_mad_i32_i24 per MFMA in "
+                   "the same waves (the MMQs' instruction mixes); ds_read_b128 and ds_write_b128 by every "
+                   "lane, bank-conflict free"}
 
         # each MMQ leg against the measured rate of the MFMA it runs on
         for s in summaries.values():
@@ -596,6 +624,10 @@ def main():
                  ceil["mfma_i8_tops"] if k.startswith(("q2_0_mmq", "quantize_q8_1_kernel + q2_0_mmq")) else None)
             if c:
                 s["frac_of_ceiling"] = round(s["value"] / c, 4)
+            cm = (ceil["mfma_f16_with_18_valu_tflops"] if k.startswith("q4k_mmq") else
+                  ceil["mfma_i8_with_33_valu_tops"] if k.startswith("q2_0_mmq") else None)
+            if cm:
+                s["frac_of_mix_ceiling"] = round(s["value"] / cm, 4)
 
     result = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True,
@@ -631,6 +663,8 @@ def main():
                                           "algorithmic_bytes_per_launch": 61734912}}
         if ceil:
             result["prefill"]["roofline"]["frac_of_ceiling"] = round(s["value"] / ceil["mfma_i8_tops"], 4)
+            result["prefill"]["roofline"]["frac_of_mix_ceiling"] = round(
+                s["value"] / ceil["mfma_i8_with_33_valu_tops"], 4)
     result["legs"] = summaries
 
     # ---- CPU oracle baselines (rank 0, N = 1), on one pinned host core ----------

@@ -33,7 +33,9 @@ def lib():
         for name, args in (("ceil_empty", [U32, U32, P]), ("ceil_stream_read", [P, U64, P, U32, P]),
                            ("ceil_stream_read_write", [P, U64, P, U32, U32, P]),
                            ("ceil_mfma_i8", [U32, U32, P, P]), ("ceil_mfma_f16", [U32, U32, P, P]),
-                           ("ceil_valu_mad", [U32, U32, P, P])):
+                           ("ceil_valu_mad", [U32, U32, P, P]),
+                           ("ceil_mix", [U32, U32, ctypes.c_int, U32, P, P]),
+                           ("ceil_lds", [U32, U32, ctypes.c_int, P, P])):
             f = getattr(l, name)
             f.restype = ctypes.c_int
             f.argtypes = args

@@ -129,6 +129,80 @@ __global__ __launch_bounds__(256) void valu_mad_kernel(uint32_t iters, int seed,
   if (s == 0x7FEDCBA9) sink[blockIdx.x] = s;
 }
 
+// MFMAs and vector-ALU work in one instruction stream: per iteration four
+// independent MFMAs (int8 32x32x32, or fp16 32x32x16 when kF16) and kV
+// 24-bit multiply-adds in eight independent chains, so neither unit waits on
+// the other's results: what the chip sustains at a given mix of VALU
+// instructions per MFMA (the MMQ kernels' fold and staging work per MFMA).
+template <bool kF16, int kV>
+__global__ __launch_bounds__(256) void mix_kernel(uint32_t iters, int seed, int *__restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const v4i a = {seed + lane, seed ^ lane, seed - lane, seed * 3 + lane};
+  const v4i b = {lane, seed, lane * 5, seed - 7};
+  v8h ah, bh;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ah[j] = (_Float16)(float)((seed + lane + j) & 7);
+    bh[j] = (_Float16)(float)((lane * 3 + j) & 7);
+  }
+  v16i c[4] = {};
+  v16f f[4] = {};
+  int x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = seed + lane * (j + 1);
+  const int m0 = (seed & 0x7FF) + 3;
+  for (uint32_t i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (kF16)
+        f[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, f[q], 0, 0, 0);
+      else
+        c[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c[q], 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < kV / 4; ++v) x[v & 7] = ((x[v & 7] << 8) >> 8) * m0 + x[v & 7];
+    }
+  }
+  int s = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s ^= c[q][r] ^ (int)f[q][r];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s ^= x[j];
+  if (s == 0x7FEDCBA9) sink[blockIdx.x] = s;
+}
+
+// LDS bandwidth: each lane reads (or writes) 16 consecutive bytes per access,
+// a wave 1 KiB without bank conflicts, 16 accesses per iteration over a
+// 64 KiB buffer (two workgroups per CU).
+template <bool kWrite>
+__global__ __launch_bounds__(256) void lds_kernel(uint32_t iters, int *__restrict__ sink) {
+  __shared__ uint4 buf[4096];
+  const uint32_t t = threadIdx.x;
+  for (uint32_t i = t; i < 4096u; i += 256u) buf[i] = make_uint4(i, i * 3u, i * 7u, i * 11u);
+  __syncthreads();
+  uint32_t acc = 0, acc2 = 0;
+  for (uint32_t it = 0; it < iters; ++it) {
+    const uint32_t sh = (it & 7u) * 256u;
+    const uint4 d = make_uint4(it, t, acc, 7u);
+#pragma unroll
+    for (uint32_t i = 0; i < 16u; ++i) {
+      const uint32_t idx = (t + 256u * i + sh) & 4095u;
+      if (kWrite) {
+        buf[idx] = d;
+      } else {
+        // two three-input adds per access keep the vector ALU off the path
+        const uint4 v = buf[idx];
+        acc = acc + v.x + v.y;
+        acc2 = acc2 + v.z + v.w;
+      }
+    }
+  }
+  __syncthreads();
+  acc ^= acc2 ^ buf[t].x;
+  if (acc == 0x7FEDCBA9u) sink[blockIdx.x] = (int)acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,6 +243,33 @@ int ceil_mfma_i8(uint32_t blocks, uint32_t iters, void *sink, void *stream) {
 int ceil_mfma_f16(uint32_t blocks, uint32_t iters, void *sink, void *stream) {
   hipLaunchKernelGGL(mfma_f16_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, 12345,
                      static_cast<int *>(sink));
+  return (int)hipGetLastError();
+}
+
+// Work per launch: blocks * 4 waves * iters * 4 MFMAs (int8 32x32x32, or
+// fp16 32x32x16 when f16 != 0) plus valu_per_4 wave-wide multiply-adds per 4
+// MFMAs; valu_per_4 is one of 96, 132 (int8) or 72 (fp16).
+int ceil_mix(uint32_t blocks, uint32_t iters, int f16, uint32_t valu_per_4, void *sink, void *stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int *k = static_cast<int *>(sink);
+  if (!f16 && valu_per_4 == 96u)
+    hipLaunchKernelGGL((mix_kernel<false, 96>), dim3(blocks), dim3(256), 0, s, iters, 12345, k);
+  else if (!f16 && valu_per_4 == 132u)
+    hipLaunchKernelGGL((mix_kernel<false, 132>), dim3(blocks), dim3(256), 0, s, iters, 12345, k);
+  else if (f16 && valu_per_4 == 72u)
+    hipLaunchKernelGGL((mix_kernel<true, 72>), dim3(blocks), dim3(256), 0, s, iters, 12345, k);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+// Bytes per launch: blocks * 256 lanes * iters * 16 accesses * 16 bytes.
+int ceil_lds(uint32_t blocks, uint32_t iters, int write, void *sink, void *stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (write)
+    hipLaunchKernelGGL(lds_kernel<true>, dim3(blocks), dim3(256), 0, s, iters, static_cast<int *>(sink));
+  else
+    hipLaunchKernelGGL(lds_kernel<false>, dim3(blocks), dim3(256), 0, s, iters, static_cast<int *>(sink));
   return (int)hipGetLastError();
 }
 

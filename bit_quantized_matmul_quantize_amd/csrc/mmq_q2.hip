@@ -36,7 +36,9 @@
 // blocks whose exponent lies in [E_p - 6, E_p] and 0 to every other block,
 // and carries the factor 2^-7p in the staged weight scales, so the passes add
 // up to the whole product and no block's scale is rounded by more than the
-// above or dropped (at most five passes cover the binary16 range).  The
+// above or dropped (at most five passes cover the binary16 range).  A
+// subnormal scale takes exponent 0 here: the bands that hold 0 have E_p <= 6,
+// where its multiplier is an exact integer.  The
 // prologue finds the number of passes; a tile of rows within the span takes
 // one.
 #include "bqmm_internal.h"
@@ -67,16 +69,22 @@ __device__ __forceinline__ uint32_t unpack_signed(uint32_t word, int j) {
   return __builtin_amdgcn_perm(0u, 0x0100FFFEu, sel);
 }
 
-// Exponent field of a binary16 scale (low 16 bits of h), at least 1: a
-// subnormal's significand is scaled like field 1's.
+// Exponent field of a binary16 scale (low 16 bits of h), at least 1: the
+// field of a row's largest scale sets its top band (a subnormal top scale is
+// scaled like field 1's).
 __device__ __forceinline__ uint32_t exp_field(uint32_t h) { return max((h >> 10) & 31u, 1u); }
 
+// The band position of a block scale: its exponent field, 0 for a subnormal,
+// whose value d = f * 2^-24 gives the integer f * 2^(6 - ep) in every band
+// that holds field 0 (ep <= 6), so subnormal scales are never rounded.
+__device__ __forceinline__ uint32_t band_field(uint32_t h) { return (h >> 10) & 31u; }
+
 // Integer multiplier of block scale h in the pass whose top exponent is ep:
-// da * 2^(30 - ep) when the block's exponent lies in [ep - 6, ep], else 0
-// (a zero scale gives 0 either way).
+// da * 2^(30 - ep) when the block's band position lies in [ep - 6, ep],
+// else 0 (a zero scale gives 0 either way).
 __device__ __forceinline__ int band_mu(uint32_t h, int ep) {
   const float v = ldexpf(f16_bits_to_f32(h & 0xFFFFu), 30 - ep);
-  return (uint32_t)(ep - (int)exp_field(h)) <= 6u ? (int)rintf(v) : 0;
+  return (uint32_t)(ep - (int)band_field(h)) <= 6u ? (int)rintf(v) : 0;
 }
 
 // TN x TM subtiles of 32 x 32 per wave, WN waves along n (4 / WN along m).
@@ -125,8 +133,8 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
   const uint32_t s_row = (tid < BN) ? min(n_base + tid, n - 1u) : min(m_base + (s_stager ? tid - BN : 0u), m - 1u);
 
   // Row exponent: exponent field E (exp_field) of the largest block scale of
-  // the row, and the smallest field among its nonzero block scales, which
-  // give the row's band passes (E - min) / 7 + 1; the tile takes the most of
+  // the row, and the smallest band position among its nonzero block scales
+  // (0 for a subnormal), which give the row's band passes (E - min) / 7 + 1; the tile takes the most of
   // its rows.  Two lanes per row read its (d, s) pairs as 16-byte chunks of four
   // blocks (k % 128 == 0, so the row holds whole chunks), eight loads in
   // flight per batch: one memory round trip per batch instead of one per
@@ -139,8 +147,8 @@ __global__ __launch_bounds__(kThreads, kDump ? 1 : 2) void q2_0_mmq_kernel(
         reinterpret_cast<const uint4 *>(ds + 4ull * (uint64_t)min(m_base + r, m - 1u) * nblk_pad);
     const uint32_t nq = k / 128u;
     uint32_t mx = 0, mn = 31u;
-    // exponent field of a nonzero scale; 31, above every field, for a zero one
-    auto nz_field = [](uint32_t h) { return (h & 0x7FFFu) == 0u ? 31u : exp_field(h); };
+    // band position of a nonzero scale; 31, above every field, for a zero one
+    auto nz_field = [](uint32_t h) { return (h & 0x7FFFu) == 0u ? 31u : band_field(h); };
     for (uint32_t c0 = part; c0 < nq; c0 += 16u) {
       uint4 v[8];
 #pragma unroll

@@ -263,3 +263,55 @@ def test_fold_wide_span_rows_do_not_change_other_tiles(gpu):
     q8b, q8bd = _q8_dev(gpu, plain, m, k)
     wd = dev_u8(w, gpu)
     assert np.array_equal(_mmq(gpu, q8ad, wd, m, n, k)[128:], _mmq(gpu, q8bd, wd, m, n, k)[128:])
+
+
+def _subnormal_scale_case(m, n, k, seed):
+    """Rows whose one dominant block sets the row's largest q8_1 scale to
+    binary16 exponent field 6, 7 or 8 (a single value of 0.375, 0.75 or 1.5)
+    while every other block holds values whose scale is subnormal, d = j·2^-24
+    for j in 1..9 (block maximum 127·j·2^-24); every weight row has code 2
+    under the dominant block, so those rows' products come from the
+    subnormal-scale blocks alone.  Other rows are ordinary N(0,1) activations
+    with outlier channels."""
+    g = inputs.rng(seed)
+    x = g.standard_normal((m, k)).astype(np.float32)
+    x[:, g.choice(k, max(1, k // 100), replace=False)] *= 20.0
+    rows = []
+    for i, top in enumerate((0.375, 0.75, 1.5) * 2):
+        r = 3 * i
+        row = np.zeros(k, dtype=np.float32)
+        for b in range(1, k // 32):
+            amax = np.float32(127.0 * int(g.integers(1, 10)) * 2.0 ** -24)
+            vals = (g.uniform(-1.0, 1.0, 32) * amax).astype(np.float32)
+            vals[int(g.integers(0, 32))] = amax if g.random() < 0.5 else -amax
+            row[32 * b:32 * b + 32] = vals
+        row[7] = top
+        x[r] = row
+        rows.append(r)
+    act = inputs.f32_to_bf16_bits(x)
+    w = inputs.q2_0_weight(g, n, k)
+    codes = w[: n * k // 4].reshape(n, k // 4)
+    b = codes[:, 0:32]  # field 0 of group 0 is block 0
+    b &= np.uint8(0xFC)
+    b |= np.uint8(0x02)
+    return act, w, np.array(rows)
+
+
+@pytest.mark.parametrize("m,n,k,seed", [(130, 384, 1024, 21),     # 96 x 128 tiles
+                                        (1030, 5500, 512, 22)])   # 128 x 128 tiles
+def test_fold_subnormal_block_scales(gpu, m, n, k, seed):
+    # subnormal q8_1 scales are applied exactly next to a row maximum of any
+    # exponent (field 7 puts them at the bottom of the top band's reach)
+    act, w, sub = _subnormal_scale_case(m, n, k, seed)
+    q8, q8d = _q8_dev(gpu, act, m, k)
+    _, ds = _planes(q8, m, k)
+    fields = (ds[:, :, 0] >> 10) & 31
+    for r in sub:  # the scales asked for are really there
+        assert fields[r, 0] in (6, 7, 8) and np.all(fields[r, 1:k // 32] == 0)
+        assert np.all(ds[r, 1:k // 32, 0] > 0)
+    assert 7 in {int(fields[r, 0]) for r in sub}
+    y = _mmq(gpu, q8d, dev_u8(w, gpu), m, n, k)
+    rows = np.unique(np.concatenate([sub, [1, 2, 127, 128, m - 1]]))
+    R = oracle.q2_0_mmq(_rows_sel(q8, m, k, rows), w, len(rows), n, k)
+    assert np.all(np.linalg.norm(R[np.isin(rows, sub)], axis=1) > 0)
+    assert row_error(y[rows], R) <= ROW_TOL

@@ -17,12 +17,14 @@
 // below 2^24).  Per block and output that leaves one fma with the lane's
 // activation scale, acc += (sc_j * D) * da; per super-block one fma with the
 // weight row's d, out += acc * d.  The min term runs on the matrix core as
-// well, once per super-block: v_mfma_f32_32x32x8_f16 with A = fp16(-dmin *
-// m_j) for the eight sub-blocks and B = their stored sums s, accumulating
-// into the output registers.
+// well, once per super-block: v_mfma_f32_32x32x8_f16 with A = m_j (exact
+// small integers) for the eight sub-blocks and B = their stored sums s gives
+// sum_j m_j * s_j (each product exact in fp32), and one fma per output
+// applies -dmin.  (Folding dmin into A would round dmin * m_j to binary16 and
+// overflow it for dmin above 1040, inside the format's range.)
 //
 // Tile 128 (n) x 128 (m), 256 lanes = 4 waves of 64 (n) x 64 (m), two
-// workgroups per CU (76,800 bytes of LDS each); k is staged 64 at a time
+// workgroups per CU (77,824 bytes of LDS each); k is staged 64 at a time
 // (one 64-weight chunk of a super-block: sub-block 2t in the low nibbles,
 // 2t + 1 in the high nibbles of the same 32 bytes) through two LDS stages,
 // both operands converted to binary16 once per workgroup while they are
@@ -58,10 +60,12 @@ constexpr int kWBytes = BN * ROW;            // q4 * sc_j, binary16
 constexpr int kDaOff = kActBytes + kWBytes;  // float [BM][2]: da of the stage's two blocks
 constexpr int kStageBytes = kDaOff + BM * 8;
 // per super-block (two of them, alternating): d of each weight row, the min
-// term's operands fp16(-dmin * m_j) [BN][8] and the activation sums s [BM][8]
+// term's weight operands m_j [BN][8] (binary16) and -dmin of each weight
+// row, and the activation sums s [BM][8]
 constexpr int kSbD = 0;
-constexpr int kSbNmin = kSbD + BN * 4;
-constexpr int kSbS = kSbNmin + BN * 16;
+constexpr int kSbNdmin = kSbD + BN * 4;
+constexpr int kSbMin = kSbNdmin + BN * 4;
+constexpr int kSbS = kSbMin + BN * 16;
 constexpr int kSbBytes = kSbS + BM * 16;
 constexpr int kLdsBytes = 2 * kStageBytes + 2 * kSbBytes;
 
@@ -185,14 +189,15 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
         /* each unpack form is known at compile time); both write d         */                          \
         const float d_ = f16_bits_to_f32(rh.x & 0xFFFFu), dmin_ = f16_bits_to_f32(rh.x >> 16);         \
         reinterpret_cast<float *>(SB + kSbD)[srow] = d_;                                                \
-        _Float16 *nm_ = reinterpret_cast<_Float16 *>(SB + kSbNmin + srow * 16);                         \
+        reinterpret_cast<float *>(SB + kSbNdmin)[srow] = -dmin_;                                        \
+        _Float16 *nm_ = reinterpret_cast<_Float16 *>(SB + kSbMin + srow * 16);                          \
         _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                                 \
           const int j_ = 2 * (int)sel + q;                                                              \
           uint32_t sca_, mna_, scb_, mnb_;                                                              \
           scale_min(S_, j_, sca_, mna_);                                                                \
           scale_min(S_, j_ + 4, scb_, mnb_);                                                            \
-          nm_[j_] = (_Float16)(-dmin_ * (float)mna_);                                                   \
-          nm_[j_ + 4] = (_Float16)(-dmin_ * (float)mnb_);                                               \
+          nm_[j_] = (_Float16)(float)mna_;                                                              \
+          nm_[j_ + 4] = (_Float16)(float)mnb_;                                                          \
         }                                                                                               \
       }                                                                                                 \
     }                                                                                                   \
@@ -279,29 +284,33 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
 
     if constexpr (!kDump) {
       if (t == 3u) {
-        // end of a super-block: apply each weight row's d, then the min term
-        // on the matrix core (K = 8: the super-block's eight sub-blocks)
+        // end of a super-block: apply each weight row's d, then the min term:
+        // sum_j m_j * s_j on the matrix core (K = 8: the super-block's eight
+        // sub-blocks) times -dmin
         const uint8_t *SB = sb_lds + ((st >> 2) & 1u) * kSbBytes;
 #pragma unroll
         for (int sn = 0; sn < 2; ++sn) {
-          float dv[16];
+          float dv[16], nv[16];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 t4 = *reinterpret_cast<const float4 *>(SB + kSbD + 4 * (wn * 64 + sn * 32 + 8 * q + 4 * hi));
+            const uint32_t o = 4 * (wn * 64 + sn * 32 + 8 * q + 4 * hi);
+            const float4 t4 = *reinterpret_cast<const float4 *>(SB + kSbD + o);
+            const float4 u4 = *reinterpret_cast<const float4 *>(SB + kSbNdmin + o);
             dv[4 * q] = t4.x; dv[4 * q + 1] = t4.y; dv[4 * q + 2] = t4.z; dv[4 * q + 3] = t4.w;
+            nv[4 * q] = u4.x; nv[4 * q + 1] = u4.y; nv[4 * q + 2] = u4.z; nv[4 * q + 3] = u4.w;
           }
           const uint32_t nl = wn * 64 + sn * 32 + l32;
-          const v4h an = *reinterpret_cast<const v4h *>(SB + kSbNmin + nl * 16 + 8 * hi);
+          const v4h an = *reinterpret_cast<const v4h *>(SB + kSbMin + nl * 16 + 8 * hi);
 #pragma unroll
           for (int sm = 0; sm < 2; ++sm) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              acc_out[sn][sm][r] = fmaf(acc_sb[sn][sm][r], dv[r], acc_out[sn][sm][r]);
-              acc_sb[sn][sm][r] = 0.0f;
-            }
             const uint32_t ml = wm * 64 + sm * 32 + l32;
             const v4h bs = *reinterpret_cast<const v4h *>(SB + kSbS + ml * 16 + 8 * hi);
-            acc_out[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x8f16(an, bs, acc_out[sn][sm], 0, 0, 0);
+            D[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(an, bs, zero16, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              acc_out[sn][sm][r] = fmaf(D[0][r], nv[r], fmaf(acc_sb[sn][sm][r], dv[r], acc_out[sn][sm][r]));
+              acc_sb[sn][sm][r] = 0.0f;
+            }
           }
         }
       }

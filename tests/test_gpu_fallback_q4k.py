@@ -132,6 +132,29 @@ def test_q4k_small(gpu, m, n, k, seed):
     assert np.array_equal(dots.cpu().numpy().reshape(m, n, k // 32), oracle.q4k_blockdots(q8, w, m, n, k))
 
 
+@pytest.mark.parametrize("m,n,k,seed", [(130, 300, 512, 55), (4, 256, 768, 56)])
+def test_q4k_large_scales(gpu, m, n, k, seed):
+    # super-block scales far above the workloads': dmin up to 6e4, so that
+    # dmin * m_j (m_j up to 63) lies outside the binary16 range; the min term
+    # must come from exact products in fp32 and stay finite and within bound
+    g = inputs.rng(seed)
+    w = inputs.q4k_weight(g, n, k).reshape(-1, 144).copy()
+    nsb = w.shape[0]
+    d = g.uniform(500.0, 5000.0, nsb).astype(np.float16)
+    dmin = g.uniform(1100.0, 60000.0, nsb).astype(np.float16)
+    w[:, 0:2] = d.view(np.uint8).reshape(nsb, 2)
+    w[:, 2:4] = dmin.view(np.uint8).reshape(nsb, 2)
+    w = w.reshape(-1)
+    act = inputs.activations(g, m, k, outliers=True)
+    q8, _ = oracle.quantize_act_q8_1(act, m, k)
+    out = empty_bf16((m, n), gpu)
+    bq.q4k_mmq_gemm(dev_u8(q8, gpu), dev_u8(w, gpu), out, m, n, k)
+    y = host_f64(out)
+    R = oracle.q4k_mmq(q8, w, m, n, k)
+    assert np.all(np.isfinite(y))
+    assert row_error(y, R) <= ROW_TOL
+
+
 def test_q4k_ffn_prefill_sampled(gpu):
     # m = 4096 FFN gate projection [17408, 5120] in Q4_K: sampled rows, and
     # the down projection [5120, 17408] on its own input

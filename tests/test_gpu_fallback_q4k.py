@@ -155,21 +155,37 @@ def test_q4k_large_scales(gpu, m, n, k, seed):
     assert row_error(y, R) <= ROW_TOL
 
 
+def _q4k_rows(w, n, k, r0, rt):
+    """Q4_K bytes of weight rows [r0, r0+rt) (whole rows of super-blocks)."""
+    return w.reshape(n, k // 256 * 144)[r0:r0 + rt].reshape(-1)
+
+
 def test_q4k_ffn_prefill_sampled(gpu):
-    # m = 4096 FFN gate projection [17408, 5120] in Q4_K: sampled rows, and
-    # the down projection [5120, 17408] on its own input
+    # m = 4096 FFN gate projection [17408, 5120] in Q4_K and the down
+    # projection [5120, 17408] on its own input: 16 sampled rows (first, last,
+    # both sides of the middle, random) and the block dots of two 32 x 32
+    # windows (first tile corner, last rows/columns)
     d = inputs.prefill_ffn(formats=("q4k",))
     H, I = d["hidden"], d["inter"]
     m = 4096
-    rows = np.array([0, 1, 1000, 2047, 2048, 4095])
+    rows = np.unique(np.concatenate([[0, 1, 2047, 2048, 4095], inputs.rng(96).choice(m, 11, replace=False)]))
     for w, n, k, act in [(d["q4k"]["wg"], I, H, d["act"]),
                          (d["q4k"]["wd"], H, I, inputs.activations(inputs.rng(54), m, I))]:
+        print(f"case n={n} k={k} m={m}", flush=True)
         q8, _ = oracle.quantize_act_q8_1(act, m, k)
+        q8d, wd = dev_u8(q8, gpu), dev_u8(w, gpu)
         out = empty_bf16((m, n), gpu)
-        bq.q4k_mmq_gemm(dev_u8(q8, gpu), dev_u8(w, gpu), out, m, n, k)
+        bq.q4k_mmq_gemm(q8d, wd, out, m, n, k)
         y = host_f64(out)
         R = oracle.q4k_mmq(_q8_rows(q8, m, k, rows), w, len(rows), n, k)
         assert row_error(y[rows], R) <= ROW_TOL
+        for (m0, n0) in [(0, 0), (m - 32, n - 32)]:
+            dots = torch.full((32 * 32 * (k // 32),), -7, dtype=torch.int32, device=gpu)
+            bq.q4k_mmq_blockdots(q8d, wd, dots, m0, 32, n0, 32, m, n, k)
+            torch.cuda.synchronize()
+            Dref = oracle.q4k_blockdots(_q8_rows(q8, m, k, np.arange(m0, m0 + 32)), _q4k_rows(w, n, k, n0, 32),
+                                        32, 32, k)
+            assert np.array_equal(dots.cpu().numpy().reshape(32, 32, k // 32), Dref)
 
 
 def test_q4k_strided_output(gpu):

@@ -151,17 +151,24 @@ def test_batch_invariance(gpu):
 
 
 def test_ffn_prefill_q2_sampled(gpu):
-    # m = 4096 FFN prefill in Q2_0: gate [17408, 5120] and down [5120, 17408]
+    # m = 4096 FFN prefill in Q2_0: gate [17408, 5120] and down [5120, 17408],
+    # 16 sampled rows (first, last, both sides of the middle, random) and the
+    # block dots of two 32 x 32 windows (first tile corner, last rows/columns)
     d = inputs.prefill_ffn(formats=("q2_0",))
     H, I, m = d["hidden"], d["inter"], 4096
-    rows = np.array([0, 1, 1000, 2047, 2048, 4095])
+    rows = np.unique(np.concatenate([[0, 1, 2047, 2048, 4095], inputs.rng(97).choice(m, 11, replace=False)]))
     for w, n, k, act in [(d["q2"]["wg"], I, H, d["act"]),
                          (d["q2"]["wd"], H, I, inputs.activations(inputs.rng(55), m, I))]:
         print(f"case n={n} k={k} m={m}", flush=True)
         q8, q8d = _q8_dev(gpu, act, m, k)
-        y = _mmq(gpu, q8d, dev_u8(w, gpu), m, n, k)
+        wd = dev_u8(w, gpu)
+        y = _mmq(gpu, q8d, wd, m, n, k)
         R = oracle.q2_0_mmq(_rows_sel(q8, m, k, rows), w, len(rows), n, k)
         assert row_error(y[rows], R) <= ROW_TOL
+        for (m0, n0) in [(0, 0), (m - 32, n - 32)]:
+            D = _dots(gpu, q8d, wd, m0, 32, n0, 32, m, n, k)
+            Dref = oracle.q2_0_blockdots(_rows_q8(q8, m, k, m0, 32), _w_rows(w, n, k, n0, 32), 32, 32, k)
+            assert np.array_equal(D, Dref)
 
 
 @pytest.mark.parametrize("m,n,k,ldc,off,seed", [(300, 136, 512, 1024, 256, 60),    # ragged tiles

@@ -457,7 +457,8 @@ def timed_oracle(fn, budget_s, max_calls):
 
 def cpu_baselines(ctx, budget):
     """The oracle on one pinned host core, on bounded samples of each workload:
-    C1 whole, C2 whole calls, C3 the m = 2 verify chain whole, C4 and C5 on 16
+    the tiny case whole, the decode GEMV in whole calls, the m = 2 verify chain
+    whole, the m = 2048 prefill MMQ and the m = 4096 FFN chain on 16
     activation rows with all n (their cost is linear in rows), extrapolated."""
     import oracle
     import inputs
@@ -477,14 +478,14 @@ def cpu_baselines(ctx, budget):
             oracle.q2_0_gemv(d["act"][:1], d["w"], 1, n, k)
 
         calls, t = timed_oracle(c1, 0.05 * budget, 2000)
-        out["tiny_c1"] = {"value": round(2.0 * m * n * k * calls / t / 1e12, 6), "unit": "TOPS", "cores": 1,
+        out["tiny_m4_n256_k512"] = {"value": round(2.0 * m * n * k * calls / t / 1e12, 6), "unit": "TOPS", "cores": 1,
                           "kind": "oracle", "ms_per_call": round(t * 1e3 / calls, 3),
-                          "sample": f"{calls} whole C1 passes (quantize, MMQ m=4 n=256 k=512, GEMV row 0), "
+                          "sample": f"{calls} whole tiny passes (quantize, MMQ m=4 n=256 k=512, GEMV row 0), "
                                     f"{t:.2f} s on {host}; TOPS counts the MMQ's 2mnk"}
     if "decode" in ctx:
         d = ctx["decode"]
         calls, t = timed_oracle(lambda: oracle.q2_0_gemv(d["act"], d["w"], 1, d["n"], d["k"]), 0.4 * budget, 200)
-        out["decode_c2"] = {"value": round(calls * DECODE_BYTES / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+        out["decode_gemv_n12288_k2048"] = {"value": round(calls * DECODE_BYTES / t / 1e9, 4), "unit": "GB/s", "cores": 1,
                             "kind": "oracle",
                             "sample": f"{calls} decode GEMV calls (n=12288, k=2048) of the oracle, {t:.1f} s on {host}"}
     if "verify" in ctx:
@@ -493,7 +494,7 @@ def cpu_baselines(ctx, budget):
         calls, t = timed_oracle(lambda: oracle.ffn_chain_gemv(np.ascontiguousarray(f["act"][:m]), f["wg"], f["wu"],
                                                               f["wd"], m, H, I), 0.15 * budget, 20)
         work = f["wg"].size + f["wu"].size + f["wd"].size + m * (6 * H + 12 * I)
-        out["verify_c3_m2"] = {"value": round(calls * work / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+        out["verify_ffn_m2"] = {"value": round(calls * work / t / 1e9, 4), "unit": "GB/s", "cores": 1,
                                "kind": "oracle",
                                "sample": f"{calls} whole m=2 verify chains (gate, up, silu_mul, down; 71 MB of "
                                          f"weights), {t:.1f} s on {host}"}
@@ -502,7 +503,7 @@ def cpu_baselines(ctx, budget):
         n, k = p["n"], p["k"]
         q8_rows, _ = oracle.quantize_act_q8_1(np.ascontiguousarray(p["act"][:rows]), rows, k)
         calls, t = timed_oracle(lambda: oracle.q2_0_mmq(q8_rows, p["w"], rows, n, k), 0.1 * budget, 50)
-        out["prefill_c4_m2048"] = {
+        out["prefill_qkvz_mmq_m2048"] = {
             "value": round(2.0 * rows * n * k * calls / t / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
             "extrapolated_ms_m2048": round(t * 1e3 / calls * 2048 / rows, 1),
             "sample": f"{calls} oracle MMQ calls on {rows} of the 2048 activation rows (n=12288, k=2048), "
@@ -521,7 +522,7 @@ def cpu_baselines(ctx, budget):
             oracle.q2_0_mmq(q8h, W["wd"], rows, H, I)
 
         calls, t = timed_oracle(c5, 0.3 * budget, 5)
-        out["ffn_c5_q2_0_m4096"] = {
+        out["ffn_prefill_q2_0_m4096"] = {
             "value": round(3 * 2.0 * rows * H * I * calls / t / 1e12, 6), "unit": "TOPS", "cores": 1,
             "kind": "oracle", "extrapolated_ms_m4096": round(t * 1e3 / calls * 4096 / rows, 1),
             "sample": f"{calls} oracle Q2_0 FFN chains (quantize, gate, up, silu_mul, quantize, down) on {rows} of "
@@ -671,10 +672,10 @@ def main():
     if not args.no_cpu_baseline:
         log("oracle baselines on one host core")
         cb = cpu_baselines(ctx, args.cpu_seconds)
-        if "decode_c2" in cb:
-            result["cpu_baseline"] = cb["decode_c2"]
-        if "prefill_c4_m2048" in cb and "prefill" in result:
-            result["prefill"]["cpu_baseline"] = cb["prefill_c4_m2048"]
+        if "decode_gemv_n12288_k2048" in cb:
+            result["cpu_baseline"] = cb["decode_gemv_n12288_k2048"]
+        if "prefill_qkvz_mmq_m2048" in cb and "prefill" in result:
+            result["prefill"]["cpu_baseline"] = cb["prefill_qkvz_mmq_m2048"]
         result["cpu_baselines"] = cb
     print(json.dumps(result), flush=True)
 

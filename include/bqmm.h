@@ -121,8 +121,12 @@ int silu_mul_quantize_q8_1(const void *gate_bf16, const void *up_bf16, void *out
 
 /* Q2_0 MMQ: out[m][n] (bf16, row-major, row stride n) =
  *   sum_k deq(act_q8)[m][k] * deq(w_q2)[n][k],
- * on int8 matrix cores with exact int32 block dot products; scales applied
- * in fp32.  [page layers/qwen3_ssm/init_q2.rs, fn qkvz_q2_prefill_gemm:
+ * on int8 matrix cores with exact int32 block dot products; the scales are
+ * applied after them: each q8_1 block scale as an exact integer multiplier
+ * within a band of binary16 exponents (rounded by at most 2^-10 relative at
+ * a band's lowest exponent; a tile whose rows span more takes one pass per
+ * band), each weight group scale with an fp32 fma.
+ * [page layers/qwen3_ssm/init_q2.rs, fn qkvz_q2_prefill_gemm:
  *  out[m, n] = input[m, k] @ W^T via quantize_act_q8_1 then q2_0_mmq_gemm,
  *  group 128 only.]
  * act_q8: q8_1 of [m][k]; w_q2: Q2_0 [n][k] with group 128.  k % 128 == 0,
@@ -221,7 +225,10 @@ int q2_0_prefill_gemm_noalloc(const void *act_bf16, const void *w_q2, void *out_
                               uint32_t m, uint32_t n, uint32_t k, uint32_t group, int use_mmq,
                               void *stream);
 
-/* Q4_K MMQ: out[m][n] (bf16) = sum_k deq(act_q8)[m][k] * deq_q4k(w)[n][k].
+/* Q4_K MMQ: out[m][n] (bf16) = sum_k deq(act_q8)[m][k] * deq_q4k(w)[n][k],
+ * on fp16 matrix cores with exact operands (q4 * sc_j and the q8_1 codes;
+ * m_j and the stored q8_1 sums for the min term), the activation scale, d
+ * and dmin applied in fp32.
  * [page layers/ops/q4k_mmq.rs, fn q4k_mmq_gemm: C[m, n] = A[m, k] x W[n, k],
  *  A in q8_1, W in block_q4_K, BF16 store; any n.]  k % 256 == 0. */
 int q4k_mmq_gemm(const void *act_q8, const void *w_q4k, void *out_bf16,

@@ -60,9 +60,6 @@ __device__ __forceinline__ v4f mfma(v4u a, v4u b, v4f c) {
 #ifndef BQMM_GEMVX_WIDE_N
 #define BQMM_GEMVX_WIDE_N 8192
 #endif
-#ifndef BQMM_GEMVX_P
-#define BQMM_GEMVX_P 2
-#endif
 constexpr int kStageBatch = 8;  // scale-staging loads per lane per round
 
 template <int M, int T, int W, int P, int NW, int MINW>
@@ -233,10 +230,9 @@ inline size_t lds_bytes(int W, int T, int NW, uint32_t k) {
   return sc_bytes > red_bytes ? sc_bytes : red_bytes;
 }
 
-template <int M, int W, int T, int NW, int MINW>
+template <int M, int W, int T, int NW, int MINW, int P>
 hipError_t launch_w(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
                     hipStream_t s) {
-  constexpr int P = BQMM_GEMVX_P;
   const size_t lds = lds_bytes(W, T, NW, k);
   if (lds > 65536) return hipErrorInvalidValue;  // the dispatcher checks q2_0_gemv_mfma_fits first
   const uint32_t blocks = (n + 16 * T - 1) / (16 * T);
@@ -269,6 +265,20 @@ hipError_t launch_w(const void *act, const void *w, const void *w2, void *out, u
 #ifndef BQMM_GEMVX_MINW_FUSED
 #define BQMM_GEMVX_MINW_FUSED 2
 #endif
+// Groups of loads in flight per wave (P): one for the fused and the narrow
+// kernels, two for the wide one.  Measured at m = 4, 6, 8 on the FFN shapes
+// (cold, same-box A/B, identical outputs): one group instead of two made the
+// fused gate/up 2-5% faster and the narrow down 1-1.5% faster, and the wide
+// single-weight kernel 0.5-1% slower.
+#ifndef BQMM_GEMVX_P_WIDE
+#define BQMM_GEMVX_P_WIDE 2
+#endif
+#ifndef BQMM_GEMVX_P_NARROW
+#define BQMM_GEMVX_P_NARROW 1
+#endif
+#ifndef BQMM_GEMVX_P_FUSED
+#define BQMM_GEMVX_P_FUSED 1
+#endif
 // The launch shape launch_m picks for (n, k): waves W and tiles per wave T.
 inline void launch_shape(uint32_t n, uint32_t k, int NW, int &W, int &T) {
   if ((k >> 7) >= 8) {
@@ -286,14 +296,17 @@ hipError_t launch_m(const void *act, const void *w, const void *w2, void *out, u
   const uint32_t G = k >> 7;
   if (G >= 8) {
     if constexpr (NW == 2) {
-      return launch_w<M, 8, BQMM_GEMVX_T_FUSED, NW, BQMM_GEMVX_MINW_FUSED>(act, w, w2, out, n, k, s);
+      return launch_w<M, 8, BQMM_GEMVX_T_FUSED, NW, BQMM_GEMVX_MINW_FUSED, BQMM_GEMVX_P_FUSED>(act, w, w2, out, n,
+                                                                                              k, s);
     } else {
       if (n >= BQMM_GEMVX_WIDE_N)
-        return launch_w<M, 8, BQMM_GEMVX_T_WIDE, NW, BQMM_GEMVX_MINW_WIDE>(act, w, w2, out, n, k, s);
-      return launch_w<M, 8, BQMM_GEMVX_T_NARROW, NW, BQMM_GEMVX_MINW_NARROW>(act, w, w2, out, n, k, s);
+        return launch_w<M, 8, BQMM_GEMVX_T_WIDE, NW, BQMM_GEMVX_MINW_WIDE, BQMM_GEMVX_P_WIDE>(act, w, w2, out, n, k,
+                                                                                           s);
+      return launch_w<M, 8, BQMM_GEMVX_T_NARROW, NW, BQMM_GEMVX_MINW_NARROW, BQMM_GEMVX_P_NARROW>(act, w, w2, out,
+                                                                                                n, k, s);
     }
   }
-  return launch_w<M, 1, 2, NW, 1>(act, w, w2, out, n, k, s);
+  return launch_w<M, 1, 2, NW, 1, 2>(act, w, w2, out, n, k, s);
 }
 
 

@@ -15,18 +15,21 @@ namespace {
 __global__ __launch_bounds__(256) void dequant_q2_0_kernel(const uint8_t *__restrict__ w,
                                                            uint16_t *__restrict__ out, uint32_t n,
                                                            uint32_t k, uint32_t group) {
-  const uint64_t words_per_row = k / 16u;
-  const uint64_t total = (uint64_t)n * words_per_row;
-  const uint32_t words_per_group = group / 16u;
+  // One lane per 8 code bytes (two words, always inside one group since
+  // group % 32 == 0): field j of those bytes is 8 consecutive k, written as
+  // one 16-byte store.
+  const uint64_t pairs_per_row = k / 32u;
+  const uint64_t total = (uint64_t)n * pairs_per_row;
+  const uint32_t pairs_per_group = group / 32u;
   const uint16_t *scales = reinterpret_cast<const uint16_t *>(w + (uint64_t)n * k / 4u);
   const uint32_t groups_per_row = k / group;
-  for (uint64_t wi = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; wi < total;
-       wi += (uint64_t)gridDim.x * blockDim.x) {
-    const uint64_t r = wi / words_per_row;
-    const uint32_t wr = (uint32_t)(wi - r * words_per_row);
-    const uint32_t g = wr / words_per_group;
-    const uint32_t t0 = (wr - g * words_per_group) * 4u;
-    const uint32_t word = reinterpret_cast<const uint32_t *>(w)[wi];
+  for (uint64_t pi = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; pi < total;
+       pi += (uint64_t)gridDim.x * blockDim.x) {
+    const uint64_t r = pi / pairs_per_row;
+    const uint32_t pr = (uint32_t)(pi - r * pairs_per_row);
+    const uint32_t g = pr / pairs_per_group;
+    const uint32_t t0 = (pr - g * pairs_per_group) * 8u;
+    const uint2 words = reinterpret_cast<const uint2 *>(w)[pi];
     const float d = f16_bits_to_f32(scales[r * groups_per_row + g]);
     const uint64_t lut = (uint64_t)f32_to_bf16_rne(-2.0f * d) |
                          ((uint64_t)f32_to_bf16_rne(-d) << 16) |
@@ -35,14 +38,14 @@ __global__ __launch_bounds__(256) void dequant_q2_0_kernel(const uint8_t *__rest
     uint16_t *dst = out + r * k + (uint64_t)g * group + t0;
 #pragma unroll
     for (uint32_t j = 0; j < 4; ++j) {
-      uint32_t v[4];
+      uint32_t v[8];
 #pragma unroll
-      for (uint32_t i = 0; i < 4; ++i) {
-        const uint32_t c = (word >> (8u * i + 2u * j)) & 3u;
+      for (uint32_t i = 0; i < 8; ++i) {
+        const uint32_t c = (((i < 4) ? words.x : words.y) >> (8u * (i & 3u) + 2u * j)) & 3u;
         v[i] = (uint32_t)(lut >> (16u * c)) & 0xFFFFu;
       }
-      *reinterpret_cast<uint2 *>(dst + j * (group / 4u)) =
-          make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+      *reinterpret_cast<uint4 *>(dst + j * (group / 4u)) =
+          make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
     }
   }
 }
@@ -90,8 +93,8 @@ uint32_t grid_for(uint64_t items, uint32_t per_block) {
 
 hipError_t launch_dequant_q2_0(const void *w, void *out, uint32_t n, uint32_t k, uint32_t group,
                                hipStream_t s) {
-  const uint64_t words = (uint64_t)n * (k / 16u);
-  hipLaunchKernelGGL(dequant_q2_0_kernel, dim3(grid_for(words, 256)), dim3(256), 0, s,
+  const uint64_t pairs = (uint64_t)n * (k / 32u);
+  hipLaunchKernelGGL(dequant_q2_0_kernel, dim3(grid_for(pairs, 256)), dim3(256), 0, s,
                      static_cast<const uint8_t *>(w), static_cast<uint16_t *>(out), n, k, group);
   return hipGetLastError();
 }

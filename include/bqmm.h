@@ -264,7 +264,10 @@ int quantize_weight_q4k(const void *w_bf16, void *out_q4k, uint32_t n, uint32_t 
                         void *stream);
 
 /* out[i] = bf16_rne(silu(gate[i]) * up[i]) for i < count, silu(g) =
- * g/(1+exp(-g)) in fp32.  out == gate is allowed (in place).
+ * g/(1+exp(-g)) in fp32 with the hardware exp2 and reciprocal: within one bf16
+ * step of the exact value for gate >= -87; below about -87.3 the result is +-0
+ * (the exact value is under 1e-35 * |up| there).  out == gate is allowed (in
+ * place).
  * [page layers/dense_ffn_decode_batch.rs, fn forward_km_q2: silu_mul over
  *  m * intermediate elements with the output over the gate buffer.] */
 int silu_mul_bf16(const void *gate, const void *up, void *out, uint64_t count, void *stream);

@@ -140,6 +140,27 @@ def test_silu_mul(gpu):
         assert np.array_equal(host_bits(gd), got)
 
 
+def test_silu_mul_wide_gate_range(gpu):
+    """Gate values from -87 to 100: exp(-g) reaches 6e37 at the low end and
+    underflows at the high end; one bf16 step still holds there. Below about
+    -87.3 the device result may be +-0: it stays under 1e-35 * |up|."""
+    g = inputs.rng(29)
+    count = 65536
+    gate = np.array([oracle.f64_to_bf16(x) for x in np.linspace(-87.0, 100.0, count)],
+                    dtype=np.uint16)
+    up = inputs.activations(g, 1, count)[0]
+    ref = oracle.silu_mul_bf16(gate, up)
+    out = empty_bf16((count,), gpu)
+    bq.silu_mul_bf16(dev_bf16(gate, gpu), dev_bf16(up, gpu), out)
+    assert bf16_ulp_distance(host_bits(out), ref).max() <= 1
+    low = np.array([oracle.f64_to_bf16(x) for x in (-88.0, -90.0, -200.0)], dtype=np.uint16)
+    up3 = inputs.activations(g, 1, 3)[0]
+    out3 = empty_bf16((3,), gpu)
+    bq.silu_mul_bf16(dev_bf16(low, gpu), dev_bf16(up3, gpu), out3)
+    got3 = inputs.bf16_bits_to_f32(host_bits(out3)).astype(np.float64)
+    assert np.all(np.abs(got3) <= 1e-35 * np.abs(inputs.bf16_bits_to_f32(up3)))
+
+
 @pytest.fixture(scope="module")
 def ffn():
     return inputs.verify_ffn()

@@ -8,37 +8,47 @@
 //             - sum_j dmin[n]*m_j[n] * s[m][j]
 //   D = sum_{t<32} q4 * q (exact, one 32-block),  s = the stored q8_1 sum (da * sum q).
 //
-// The per-block scale fold is what bounds this kernel (every output needs
-// one VALU operation per 32-block for the activation scale), so the 6-bit
-// sub-scale is moved onto the matrix core: the weight operand is q4 * sc_j
-// and the activation operand the q8_1 code q, both exact small integers in
-// binary16 (q4 * sc_j <= 945, |q| <= 127), so v_mfma_f32_32x32x16_f16
-// returns sc_j * D exactly (every product and partial sum is an integer
-// below 2^24).  Per block and output that leaves one fma with the lane's
-// activation scale, acc += (sc_j * D) * da; per super-block one fma with the
-// weight row's d, out += acc * d.  The min term runs on the matrix core as
-// well, once per super-block: v_mfma_f32_32x32x8_f16 with A = m_j (exact
-// small integers) for the eight sub-blocks and B = their stored sums s gives
-// sum_j m_j * s_j (each product exact in fp32), and one fma per output
-// applies -dmin.  (Folding dmin into A would round dmin * m_j to binary16 and
-// overflow it for dmin above 1040, inside the format's range.)
+// The weight's 6-bit sub-scale is moved onto the matrix core: the weight
+// operand is q4 * sc_j, an exact small integer in binary16 (<= 945).  The
+// activation scale is moved into the other operand: it is
+// q * da * 2^-e rounded once to binary16, where 2^e is a power of two per
+// activation row and super-block chosen from the largest da of the
+// super-block's eight blocks (the exponent field f of that da, at least 1,
+// gives e = f - 22, so that |q * da * 2^-e| < 2^15 and da * 2^-e is exact
+// for blocks within 2^21 of the largest).  v_mfma_f32_32x32x16_f16 then
+// accumulates a whole super-block in place (fp32), and per super-block and
+// output one multiply by 2^e, one fma with the weight row's d and one with
+// the min term remain, instead of one fma per output per 32-block for the
+// activation scale.  The min term runs on the matrix core too, once per
+// super-block: v_mfma_f32_32x32x8_f16 with A = m_j (exact small integers) for
+// the eight sub-blocks and B = their stored sums s gives sum_j m_j * s_j
+// (each product exact in fp32), and one fma per output applies -dmin.
+// (Folding dmin into A would round dmin * m_j to binary16 and overflow it for
+// dmin above 1040, inside the format's range.)  Rounding the activation
+// operand costs a relative 2^-11 per value, below the 2^-8 that q8_1 codes
+// carry; in exchange the kernel issues 13.5 instead of 19 VALU instructions
+// per MFMA (measured with the SQ counters), which made it 4-5% faster: on this
+// kernel the staging (global loads, conversion, LDS writes), the barriers
+// and the flush each take a share of the time, and a copy without any MFMA
+// still ran 87% as long.
 //
 // Tile 128 (n) x 128 (m), 256 lanes = 4 waves of 64 (n) x 64 (m), two
-// workgroups per CU (77,824 bytes of LDS each); k is staged 64 at a time
+// workgroups per CU (76,800 bytes of LDS each); k is staged 64 at a time
 // (one 64-weight chunk of a super-block: sub-block 2t in the low nibbles,
 // 2t + 1 in the high nibbles of the same 32 bytes) through two LDS stages,
 // both operands converted to binary16 once per workgroup while they are
 // written: the q8_1 codes by an exponent-bias trick (bytes xor 0x80 under the
-// exponent of 1024, then one packed subtraction of 1152), the 4-bit codes
-// likewise times sc_j with one packed fma.  Staged rows are 128 bytes with
-// their 16-byte chunks XOR-swizzled by the row's low bits instead of padded,
-// which keeps the operand reads free of bank conflicts and lets two
-// workgroups share a CU.  (A 256 (m) x 128 (n) tile of eight waves, one
-// workgroup per CU, measured 1-9% slower; so did splitting the eight waves
-// into four that stage and four that compute, and 16 x 16 x 32 MFMA
-// subtiles, which run at half the 32 x 32 x 16 rate here.)  The MFMA of step
-// i + 1 is issued before the fold of step i, and the compute is last in the
-// loop body (see the Q2_0 kernel for why).
+// exponent of 1024, then one packed subtraction of 1152) and one packed
+// multiply by da * 2^-e, the 4-bit codes likewise times sc_j with one packed
+// fma.  Staged rows are 128 bytes with their 16-byte chunks XOR-swizzled by
+// the row's low bits instead of padded, which lets two workgroups share a CU.
+// (A 256 (m) x 128 (n) tile of eight waves, one workgroup per CU, measured
+// 1-9% slower; so did splitting the eight waves into four that stage and four
+// that compute, and 16 x 16 x 32 MFMA subtiles, which run at half the
+// 32 x 32 x 16 rate here.  Unrolling the loop by a super-block, with and
+// without a forced MFMA/VALU interleave of 4 to 9 VALU instructions per MFMA,
+// and a swizzle by the row's bits 1-3 measured within 3% of this loop.)  The
+// compute is last in the loop body (see the Q2_0 kernel for why).
 #include "bqmm_internal.h"
 
 namespace bqmm {
@@ -55,18 +65,18 @@ constexpr int KS = 64;                       // k per stage: one chunk of a supe
 constexpr int ROW = 2 * KS;                  // bytes per staged binary16 row (16-byte chunks swizzled)
 constexpr int kThreads = 256;
 // one LDS stage
-constexpr int kActBytes = BM * ROW;          // activation codes, binary16
+constexpr int kActBytes = BM * ROW;          // q * da * 2^-e, binary16
 constexpr int kWBytes = BN * ROW;            // q4 * sc_j, binary16
-constexpr int kDaOff = kActBytes + kWBytes;  // float [BM][2]: da of the stage's two blocks
-constexpr int kStageBytes = kDaOff + BM * 8;
+constexpr int kStageBytes = kActBytes + kWBytes;
 // per super-block (two of them, alternating): d of each weight row, the min
 // term's weight operands m_j [BN][8] (binary16) and -dmin of each weight
-// row, and the activation sums s [BM][8]
+// row, the activation sums s [BM][8] and each activation row's 2^e
 constexpr int kSbD = 0;
 constexpr int kSbNdmin = kSbD + BN * 4;
 constexpr int kSbMin = kSbNdmin + BN * 4;
 constexpr int kSbS = kSbMin + BN * 16;
-constexpr int kSbBytes = kSbS + BM * 16;
+constexpr int kSbE = kSbS + BM * 16;
+constexpr int kSbBytes = kSbE + BM * 4;
 constexpr int kLdsBytes = 2 * kStageBytes + 2 * kSbBytes;
 
 // Byte offset of 16-byte chunk c of staged row r: the chunk index is XOR-ed
@@ -136,8 +146,9 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
   const uint32_t srow = tid >> 1, sel = tid & 1u;
   const uint32_t a_row = min(m_base + srow, m - 1u);
   const uint32_t w_row = min(n_base + srow, n - 1u);
-  uint4 ra0, ra1, rh, rw0, rw1;
+  uint4 ra0, ra1, rh, rw0, rw1, rdd;
   uint32_t rds;
+  uint32_t ef = 1;  // exponent field of the largest da in the current super-block (at least 1)
 #define BQMM_FETCH(st)                                                                                  \
   do {                                                                                                  \
     const uint32_t sb_ = (st) >> 2, t_ = (st) & 3u;                                                     \
@@ -149,6 +160,8 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
     rw0 = *reinterpret_cast<const uint4 *>(bp_ + 16u + 32u * t_);                                       \
     rw1 = *reinterpret_cast<const uint4 *>(bp_ + 32u + 32u * t_);                                       \
     rds = *reinterpret_cast<const uint32_t *>(ds + 4ull * ((uint64_t)a_row * nblk_pad + 2u * (st) + sel)); \
+    if (!kDump && t_ == 0u)                                                                             \
+      rdd = *reinterpret_cast<const uint4 *>(ds + 4ull * ((uint64_t)a_row * nblk_pad + 8u * sb_ + 4u * sel)); \
   } while (0)
 
   // Write the prefetched stage into LDS stage buffer `buf`; stage st of
@@ -163,6 +176,20 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
       uint32_t h[16];                                                                                   \
       const uint32_t x_[8] = {ra0.x, ra0.y, ra0.z, ra0.w, ra1.x, ra1.y, ra1.z, ra1.w};                  \
       _Pragma("unroll") for (int i = 0; i < 8; ++i) s8x4_to_f16(x_[i], h[2 * i], h[2 * i + 1]);         \
+      if (!kDump) {                                                                                     \
+        if (t_ == 0u) {                                                                                 \
+          /* largest |da| of the row's eight blocks: four here, four in the */                          \
+          /* partner lane (tid ^ 1, same quad); e = ef - 22                  */                         \
+          uint32_t mx_ = max(max(rdd.x & 0x7FFFu, rdd.y & 0x7FFFu), max(rdd.z & 0x7FFFu, rdd.w & 0x7FFFu)); \
+          mx_ = max(mx_, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx_, 0xB1, 0xF, 0xF, false));     \
+          ef = max(mx_ >> 10, 1u);                                                                      \
+          reinterpret_cast<float *>(SB + kSbE)[srow] = __builtin_amdgcn_ldexpf(1.0f, (int)ef - 22);     \
+        }                                                                                               \
+        const _Float16 a_ = (_Float16)__builtin_amdgcn_ldexpf(f16_bits_to_f32(rds & 0xFFFFu), 22 - (int)ef); \
+        const v2h av_ = {a_, a_};                                                                       \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i)                                                  \
+          h[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, h[i]) * av_);                     \
+      }                                                                                                 \
       _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                     \
         *reinterpret_cast<uint4 *>(L + swz(srow, 4u * sel + i)) =                                       \
             make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);                             \
@@ -201,17 +228,16 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
         }                                                                                               \
       }                                                                                                 \
     }                                                                                                   \
-    reinterpret_cast<float *>(L + kDaOff)[2u * srow + sel] = f16_bits_to_f32(rds & 0xFFFFu);           \
     reinterpret_cast<uint16_t *>(SB + kSbS)[8u * srow + 2u * t_ + sel] = (uint16_t)(rds >> 16);         \
   } while (0)
 
-  v16f acc_out[2][2], acc_sb[2][2];
+  v16f acc_out[2][2], acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc_out[a][b][r] = 0.0f, acc_sb[a][b][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) acc_out[a][b][r] = 0.0f, acc[a][b][r] = 0.0f;
   const v16f zero16 = {};
 
   BQMM_FETCH(0u);
@@ -227,66 +253,50 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
     const uint8_t *a_lds = L, *w_lds = L + kActBytes;
     const uint32_t t = st & 3u;
 
-    // 8 steps (b, sn, sm): block b of the stage (sub-block 2t + b), subtiles
-    // sn (weights, A) and sm (activations, B); each step is two MFMAs over the
-    // block's 32 k.  Operands of a block are read when its first step begins.
-    v8h A[2][2], B[2][2];
-    float da[2][2];
-    v16f D[2];
-    auto load_block = [&](int b) {
+    // Two blocks (sub-blocks 2t, 2t + 1), each two k-halves of 16 over the
+    // four subtiles (sn: weights, A; sm: activations, B), accumulating the
+    // super-block in place.
 #pragma unroll
-      for (int sm = 0; sm < 2; ++sm) {
-        const uint32_t ml = wm * 64 + sm * 32 + l32;
+    for (int b = 0; b < 2; ++b) {
+      v8h A[2][2], B[2][2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          B[sm][h] = *reinterpret_cast<const v8h *>(a_lds + swz(ml, 4 * b + 2 * h + hi));
-        da[sm][b] = reinterpret_cast<const float *>(L + kDaOff)[ml * 2 + b];
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int sm = 0; sm < 2; ++sm)
+          B[sm][h] = *reinterpret_cast<const v8h *>(a_lds + swz(wm * 64 + sm * 32 + l32, 4 * b + 2 * h + hi));
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn)
+          A[sn][h] = *reinterpret_cast<const v8h *>(w_lds + swz(wn * 64 + sn * 32 + l32, 4 * b + 2 * h + hi));
       }
 #pragma unroll
-      for (int sn = 0; sn < 2; ++sn) {
-        const uint32_t nl = wn * 64 + sn * 32 + l32;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          A[sn][h] = *reinterpret_cast<const v8h *>(w_lds + swz(nl, 4 * b + 2 * h + hi));
-      }
-    };
+        for (int sn = 0; sn < 2; ++sn)
 #pragma unroll
-    for (int i = 0; i <= 8; ++i) {
-      if (i < 8) {
-        const int b = i >> 2, sn = (i >> 1) & 1, sm = i & 1;
-        if ((i & 3) == 0) load_block(b);
-        D[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            A[sn][1], B[sm][1], __builtin_amdgcn_mfma_f32_32x32x16_f16(A[sn][0], B[sm][0], zero16, 0, 0, 0), 0, 0,
-            0);
-        // keep the MFMAs ahead of the previous step's fold (see mmq_q2.hip)
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (i > 0) {
-        const int p = i - 1;
-        const int b = p >> 2, sn = (p >> 1) & 1, sm = p & 1;
-        const v16f &Dp = D[p & 1];
-        if constexpr (kDump) {
-          const uint32_t mm = m_base + wm * 64 + sm * 32 + l32;
+          for (int sm = 0; sm < 2; ++sm)
+            acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[sn][h], B[sm][h], acc[sn][sm], 0, 0, 0);
+      if constexpr (kDump) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint32_t nn = n_base + wn * 64 + sn * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (mm >= m0 && mm < m0 + mt && nn >= n0 && nn < n0 + nt)
-              dots[((uint64_t)(mm - m0) * nt + (nn - n0)) * (k / 32u) + 2u * st + b] = (int32_t)Dp[r];
+        for (int sn = 0; sn < 2; ++sn)
+#pragma unroll
+          for (int sm = 0; sm < 2; ++sm) {
+            const uint32_t mm = m_base + wm * 64 + sm * 32 + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const uint32_t nn = n_base + wn * 64 + sn * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+              if (mm >= m0 && mm < m0 + mt && nn >= n0 && nn < n0 + nt)
+                dots[((uint64_t)(mm - m0) * nt + (nn - n0)) * (k / 32u) + 2u * st + b] = (int32_t)acc[sn][sm][r];
+              acc[sn][sm][r] = 0.0f;
+            }
           }
-        } else {
-          const float a = da[sm][b];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_sb[sn][sm][r] = fmaf(Dp[r], a, acc_sb[sn][sm][r]);
-        }
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
 
     if constexpr (!kDump) {
       if (t == 3u) {
-        // end of a super-block: apply each weight row's d, then the min term:
-        // sum_j m_j * s_j on the matrix core (K = 8: the super-block's eight
-        // sub-blocks) times -dmin
+        // end of a super-block: undo the activation row's 2^-e, apply each
+        // weight row's d, then the min term: sum_j m_j * s_j on the matrix
+        // core (K = 8: the super-block's eight sub-blocks) times -dmin
         const uint8_t *SB = sb_lds + ((st >> 2) & 1u) * kSbBytes;
 #pragma unroll
         for (int sn = 0; sn < 2; ++sn) {
@@ -305,11 +315,12 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
           for (int sm = 0; sm < 2; ++sm) {
             const uint32_t ml = wm * 64 + sm * 32 + l32;
             const v4h bs = *reinterpret_cast<const v4h *>(SB + kSbS + ml * 16 + 8 * hi);
-            D[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(an, bs, zero16, 0, 0, 0);
+            const float e2 = reinterpret_cast<const float *>(SB + kSbE)[ml];
+            const v16f Dm = __builtin_amdgcn_mfma_f32_32x32x8f16(an, bs, zero16, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              acc_out[sn][sm][r] = fmaf(D[0][r], nv[r], fmaf(acc_sb[sn][sm][r], dv[r], acc_out[sn][sm][r]));
-              acc_sb[sn][sm][r] = 0.0f;
+              acc_out[sn][sm][r] = fmaf(Dm[r], nv[r], fmaf(acc[sn][sm][r] * e2, dv[r], acc_out[sn][sm][r]));
+              acc[sn][sm][r] = 0.0f;
             }
           }
         }

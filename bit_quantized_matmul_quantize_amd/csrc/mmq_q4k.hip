@@ -14,8 +14,10 @@
 // q * da * 2^-e rounded once to binary16, where 2^e is a power of two per
 // activation row and super-block chosen from the largest da of the
 // super-block's eight blocks (the exponent field f of that da, at least 1,
-// gives e = f - 22, so that |q * da * 2^-e| < 2^15 and da * 2^-e is exact
-// for blocks within 2^21 of the largest).  v_mfma_f32_32x32x16_f16 then
+// gives e = f - 23, so that |q * da * 2^-e| < 127 * 2^9 < 65504 and
+// da * 2^-e is exact for blocks within 2^22 of the largest; a block further
+// below loses one bit of its scale per binade and, beyond about 2^33, all of
+// it).  v_mfma_f32_32x32x16_f16 then
 // accumulates a whole super-block in place (fp32), and per super-block and
 // output one multiply by 2^e, one fma with the weight row's d and one with
 // the min term remain, instead of one fma per output per 32-block for the
@@ -179,13 +181,13 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
       if (!kDump) {                                                                                     \
         if (t_ == 0u) {                                                                                 \
           /* largest |da| of the row's eight blocks: four here, four in the */                          \
-          /* partner lane (tid ^ 1, same quad); e = ef - 22                  */                         \
+          /* partner lane (tid ^ 1, same quad); e = ef - 23                  */                         \
           uint32_t mx_ = max(max(rdd.x & 0x7FFFu, rdd.y & 0x7FFFu), max(rdd.z & 0x7FFFu, rdd.w & 0x7FFFu)); \
           mx_ = max(mx_, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx_, 0xB1, 0xF, 0xF, false));     \
           ef = max(mx_ >> 10, 1u);                                                                      \
-          reinterpret_cast<float *>(SB + kSbE)[srow] = __builtin_amdgcn_ldexpf(1.0f, (int)ef - 22);     \
+          reinterpret_cast<float *>(SB + kSbE)[srow] = __builtin_amdgcn_ldexpf(1.0f, (int)ef - 23);     \
         }                                                                                               \
-        const _Float16 a_ = (_Float16)__builtin_amdgcn_ldexpf(f16_bits_to_f32(rds & 0xFFFFu), 22 - (int)ef); \
+        const _Float16 a_ = (_Float16)__builtin_amdgcn_ldexpf(f16_bits_to_f32(rds & 0xFFFFu), 23 - (int)ef); \
         const v2h av_ = {a_, a_};                                                                       \
         _Pragma("unroll") for (int i = 0; i < 16; ++i)                                                  \
           h[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, h[i]) * av_);                     \

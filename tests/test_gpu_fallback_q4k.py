@@ -8,6 +8,7 @@ import torch
 
 import inputs
 import oracle
+import q4k_pack
 import bit_quantized_matmul_quantize_amd as bq
 from parity_helpers import (FROB_TOL, ROW_TOL, dev_bf16, dev_u8, empty_bf16, frob_error, host_bits,
                             host_f64, rows_ok, row_error)
@@ -206,3 +207,57 @@ def test_q4k_strided_output(gpu):
     mask = torch.ones_like(big, dtype=torch.bool)
     mask[:, off:off + n] = False
     assert bool((big[mask] == -3.0).all())
+
+
+def _zero_subblocks(w, n, k, subs):
+    """Q4_K bytes with sub-blocks `subs` of every super-block zeroed (codes 0 and m_j = 0),
+    so their dequantized weights are exactly 0; the rest unchanged."""
+    b = w.reshape(n * (k // 256), 144).copy()
+    for j in subs:
+        t, hi_nib = j // 2, j % 2
+        code = b[:, 16 + 32 * t:48 + 32 * t]
+        code &= np.uint8(0x0F if hi_nib else 0xF0)
+        if j < 4:
+            b[:, 8 + j] &= np.uint8(0xC0)               # m_j: low six bits of S[j+4]
+        else:
+            b[:, 8 + j] &= np.uint8(0x0F)               # low four bits of m_j: high nibble of S[j+4]
+            b[:, 4 + j] &= np.uint8(0x3F)               # high two bits of m_j: top of S[j]
+    return b.reshape(-1)
+
+
+@pytest.mark.parametrize("m,n,k,seed", [(130, 1000, 512, 57), (260, 2100, 768, 58)])
+def test_q4k_wide_activation_scale_spans(gpu, m, n, k, seed):
+    # Rows whose q8_1 block scales span 2^6..2^24 inside each super-block: one
+    # block per super-block holds a single value of 2000 and the others sit
+    # about 2^s below; the weights under that block are exactly zero, so the
+    # outputs come from the small blocks alone (the case in which the matrix
+    # core's binary16 activation operand could lose them).
+    g = inputs.rng(seed)
+    w = _zero_subblocks(inputs.q4k_weight(g, n, k), n, k, (0, 5))
+    deq = q4k_pack.dequant(w, n, k).reshape(n, k // 256, 256)
+    assert np.all(deq[:, :, 0:32] == 0) and np.all(deq[:, :, 160:192] == 0)
+    x = g.standard_normal((m, k)).astype(np.float32)
+    wide = []
+    r = 0
+    for s in (6, 12, 20, 24):
+        for dom in (0, 5):
+            row = g.standard_normal(k).astype(np.float32) * np.float32(2000.0 * 2.0 ** -s / 2.5)
+            for sb in range(k // 256):
+                blk = row[256 * sb + 32 * dom:256 * sb + 32 * dom + 32]
+                blk[:] = 0.0
+                blk[7] = 2000.0
+            x[r] = row
+            wide.append(r)
+            r += 3
+    act = inputs.f32_to_bf16_bits(x)
+    q8, _ = oracle.quantize_act_q8_1(act, m, k)
+    kp = (k + 255) // 256 * 256
+    d = q8[m * kp:].copy().view(np.uint16).reshape(m, kp // 32, 2)[:, :, 0].copy().view(np.float16).astype(np.float64)
+    assert max(d[i][d[i] > 0].max() / d[i][d[i] > 0].min() for i in wide) >= 2.0 ** 22
+    out = empty_bf16((m, n), gpu)
+    bq.q4k_mmq_gemm(dev_u8(q8, gpu), dev_u8(w, gpu), out, m, n, k)
+    y = host_f64(out)
+    rows = np.unique(np.concatenate([wide, [1, 2, m - 1], inputs.rng(seed).choice(m, 6, replace=False)]))
+    R = oracle.q4k_mmq(_q8_rows(q8, m, k, rows), w, len(rows), n, k)
+    assert np.all(np.linalg.norm(R, axis=1) > 0)
+    assert row_error(y[rows], R) <= ROW_TOL

@@ -411,9 +411,9 @@ def ceiling_legs(dev, gemv_blocks):
                         [sink], 1, instr, "Ginstr/s", "v_mad_i32_i24 loop", VALU_PEAK_GINSTR, "valu"))
     # the MMQs' instruction mixes: four MFMAs and 4v multiply-adds per iteration
     # (v = 24: the Q2_0 fold's VALU per int8 MFMA; 33: that kernel's whole mix;
-    # 18: the Q4_K kernel's per fp16 MFMA), two waves per SIMD as in the kernels
+    # 14: the Q4_K kernel's per fp16 MFMA), two waves per SIMD as in the kernels
     miters = 1024
-    for f16, per4, label in ((0, 96, "i8_24valu"), (0, 132, "i8_33valu"), (1, 72, "f16_18valu")):
+    for f16, per4, label in ((0, 96, "i8_24valu"), (0, 132, "i8_33valu"), (1, 56, "f16_14valu")):
         ops = 512 * 4 * miters * 4 * 2.0 * 32 * 32 * (16 if f16 else 32)
         legs.append(Leg(f"ceiling_mix_{label}_512x256",
                         lambda f=f16, v=per4: ceilings.call("ceil_mix", 512, miters, f, v, sink.data_ptr(), stream()),
@@ -606,7 +606,7 @@ def main():
                                      if k.startswith("ceiling_valu_mad_i24_")),
             "mfma_i8_with_24_valu_tops": summaries["ceiling_mix_i8_24valu_512x256"]["value"],
             "mfma_i8_with_33_valu_tops": summaries["ceiling_mix_i8_33valu_512x256"]["value"],
-            "mfma_f16_with_18_valu_tflops": summaries["ceiling_mix_f16_18valu_512x256"]["value"],
+            "mfma_f16_with_14_valu_tflops": summaries["ceiling_mix_f16_14valu_512x256"]["value"],
             "lds_read_gbs": summaries["ceiling_lds_read_b128"]["value"],
             "lds_write_gbs": summaries["ceiling_lds_write_b128"]["value"],
             "how": "ceilings/ceilings.hip, timed in this run: empty kernels (1000 per graph) with 1x64 lanes and "
@@ -614,7 +614,7 @@ def main():
                    "rotated, the GEMV's grid), and the same with the GEMV's traffic split as it is (6,688,768 B "
                    "read, 12,288 bf16 written); back-to-back v_mfma_i32_32x32x32_i8 and, apart, "
                    "v_mfma_f32_32x32x16_f16 with 4 independent accumulators; back-to-back v_mad_i32_i24 in 8 "
-                   "independent chains (best of two grid sizes); the MFMA loops with 24 or 33 (int8) and 18 (fp16) independent v_mad_i32_i24 per MFMA in "
+                   "independent chains (best of two grid sizes); the MFMA loops with 24 or 33 (int8) and 14 (fp16) independent v_mad_i32_i24 per MFMA in "
                    "the same waves (the MMQs' instruction mixes); ds_read_b128 and ds_write_b128 by every "
                    "lane, bank-conflict free"}
 
@@ -625,7 +625,7 @@ def main():
                  ceil["mfma_i8_tops"] if k.startswith(("q2_0_mmq", "quantize_q8_1_kernel + q2_0_mmq")) else None)
             if c:
                 s["frac_of_ceiling"] = round(s["value"] / c, 4)
-            cm = (ceil["mfma_f16_with_18_valu_tflops"] if k.startswith("q4k_mmq") else
+            cm = (ceil["mfma_f16_with_14_valu_tflops"] if k.startswith("q4k_mmq") else
                   ceil["mfma_i8_with_33_valu_tops"] if k.startswith("q2_0_mmq") else None)
             if cm:
                 s["frac_of_mix_ceiling"] = round(s["value"] / cm, 4)

@@ -248,7 +248,7 @@ int ceil_mfma_f16(uint32_t blocks, uint32_t iters, void *sink, void *stream) {
 
 // Work per launch: blocks * 4 waves * iters * 4 MFMAs (int8 32x32x32, or
 // fp16 32x32x16 when f16 != 0) plus valu_per_4 wave-wide multiply-adds per 4
-// MFMAs; valu_per_4 is one of 96, 132 (int8) or 72 (fp16).
+// MFMAs; valu_per_4 is one of 96, 132 (int8) or 56 (fp16).
 int ceil_mix(uint32_t blocks, uint32_t iters, int f16, uint32_t valu_per_4, void *sink, void *stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   int *k = static_cast<int *>(sink);
@@ -256,8 +256,8 @@ int ceil_mix(uint32_t blocks, uint32_t iters, int f16, uint32_t valu_per_4, void
     hipLaunchKernelGGL((mix_kernel<false, 96>), dim3(blocks), dim3(256), 0, s, iters, 12345, k);
   else if (!f16 && valu_per_4 == 132u)
     hipLaunchKernelGGL((mix_kernel<false, 132>), dim3(blocks), dim3(256), 0, s, iters, 12345, k);
-  else if (f16 && valu_per_4 == 72u)
-    hipLaunchKernelGGL((mix_kernel<true, 72>), dim3(blocks), dim3(256), 0, s, iters, 12345, k);
+  else if (f16 && valu_per_4 == 56u)
+    hipLaunchKernelGGL((mix_kernel<true, 56>), dim3(blocks), dim3(256), 0, s, iters, 12345, k);
   else
     return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();

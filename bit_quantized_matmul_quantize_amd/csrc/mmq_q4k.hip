@@ -12,30 +12,29 @@
 // operand is q4 * sc_j, an exact small integer in binary16 (<= 945).  The
 // activation scale is moved into the other operand: it is
 // q * da * 2^-e rounded once to binary16, where 2^e is a power of two per
-// activation row and super-block chosen from the largest da of the
-// super-block's eight blocks (the exponent field f of that da, at least 1,
-// gives e = f - 23, so that |q * da * 2^-e| < 127 * 2^9 < 65504 and
-// da * 2^-e is exact for blocks within 2^22 of the largest; a block further
-// below loses one bit of its scale per binade and, beyond about 2^33, all of
-// it).  v_mfma_f32_32x32x16_f16 then
-// accumulates a whole super-block in place (fp32), and per super-block and
-// output one multiply by 2^e, one fma with the weight row's d and one with
-// the min term remain, instead of one fma per output per 32-block for the
-// activation scale.  The min term runs on the matrix core too, once per
-// super-block: v_mfma_f32_32x32x8_f16 with A = m_j (exact small integers) for
-// the eight sub-blocks and B = their stored sums s gives sum_j m_j * s_j
-// (each product exact in fp32), and one fma per output applies -dmin.
-// (Folding dmin into A would round dmin * m_j to binary16 and overflow it for
-// dmin above 1040, inside the format's range.)  Rounding the activation
-// operand costs a relative 2^-11 per value, below the 2^-8 that q8_1 codes
-// carry; in exchange the kernel issues 13.5 instead of 19 VALU instructions
-// per MFMA (measured with the SQ counters), which made it 4-5% faster: on this
-// kernel the staging (global loads, conversion, LDS writes), the barriers
-// and the flush each take a share of the time, and a copy without any MFMA
-// still ran 87% as long.
+// activation row, chosen by a prologue from the row's largest da (the
+// exponent field f of that da, at least 1, gives e = f - 23, so that
+// |q * da * 2^-e| < 127 * 2^9 < 65504 and da * 2^-e is exact for blocks
+// within 2^22 of the largest; a block further below loses one bit of its
+// scale per binade and, beyond about 2^33, all of it).
+// v_mfma_f32_32x32x16_f16 then accumulates a whole super-block in place
+// (fp32, its first MFMA starting from zero), and per super-block and output
+// two fmas remain: one with the weight row's d and one with the min term.
+// The min term runs on the matrix core too, once per super-block:
+// v_mfma_f32_32x32x8_f16 with A = m_j (exact small integers) for the eight
+// sub-blocks and B = their stored sums s times 2^-(e + 6) (exact, and below
+// 2^15) gives sum_j m_j * s_j * 2^-(e + 6), and one fma per output applies
+// -64 dmin.  (Folding dmin into A would round dmin * m_j to binary16 and
+// overflow it for dmin above 1040, inside the format's range.)  2^e is
+// applied once, when the outputs are stored.  Rounding the activation operand
+// costs a relative 2^-11 per value, below the 2^-8 that q8_1 codes carry; in
+// exchange the kernel issues 11.7 instead of 19.1 VALU instructions per
+// MFMA (SQ counters), which made it about 9% faster: on this kernel the staging (global
+// loads, conversion, LDS writes), the barriers and the flush each take a
+// share of the time, and a copy without any MFMA still ran 87% as long.
 //
 // Tile 128 (n) x 128 (m), 256 lanes = 4 waves of 64 (n) x 64 (m), two
-// workgroups per CU (76,800 bytes of LDS each); k is staged 64 at a time
+// workgroups per CU (76,288 bytes of LDS each); k is staged 64 at a time
 // (one 64-weight chunk of a super-block: sub-block 2t in the low nibbles,
 // 2t + 1 in the high nibbles of the same 32 bytes) through two LDS stages,
 // both operands converted to binary16 once per workgroup while they are
@@ -72,13 +71,12 @@ constexpr int kWBytes = BN * ROW;            // q4 * sc_j, binary16
 constexpr int kStageBytes = kActBytes + kWBytes;
 // per super-block (two of them, alternating): d of each weight row, the min
 // term's weight operands m_j [BN][8] (binary16) and -dmin of each weight
-// row, the activation sums s [BM][8] and each activation row's 2^e
+// row (times 64), and the activation sums s * 2^-(e + 6) [BM][8]
 constexpr int kSbD = 0;
 constexpr int kSbNdmin = kSbD + BN * 4;
 constexpr int kSbMin = kSbNdmin + BN * 4;
 constexpr int kSbS = kSbMin + BN * 16;
-constexpr int kSbE = kSbS + BM * 16;
-constexpr int kSbBytes = kSbE + BM * 4;
+constexpr int kSbBytes = kSbS + BM * 16;
 constexpr int kLdsBytes = 2 * kStageBytes + 2 * kSbBytes;
 
 // Byte offset of 16-byte chunk c of staged row r: the chunk index is XOR-ed
@@ -125,6 +123,8 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
     int32_t *__restrict__ dots, uint32_t m, uint32_t n, uint32_t k, uint32_t m0, uint32_t mt,
     uint32_t n0, uint32_t nt, uint32_t tile_n0, uint32_t tile_m0, uint32_t ldc) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  // exponent field ef of each tile row's largest activation block scale
+  __shared__ int q4k_rowexp[BM];
   uint8_t *const sb_lds = lds + 2 * kStageBytes;
 
   const uint32_t tid = threadIdx.x;
@@ -148,9 +148,31 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
   const uint32_t srow = tid >> 1, sel = tid & 1u;
   const uint32_t a_row = min(m_base + srow, m - 1u);
   const uint32_t w_row = min(n_base + srow, n - 1u);
-  uint4 ra0, ra1, rh, rw0, rw1, rdd;
+  uint4 ra0, ra1, rh, rw0, rw1;
   uint32_t rds;
-  uint32_t ef = 1;  // exponent field of the largest da in the current super-block (at least 1)
+
+  // Row exponent: the binary16 exponent field ef (at least 1) of the largest
+  // q8_1 block scale of this thread's activation row; e = ef - 23.  The two
+  // lanes of a row (tid ^ 1, same quad) scan alternate 16-byte chunks of four
+  // (d, s) pairs, eight loads in flight per batch; chunk indices past the end
+  // are clamped to the last chunk, which leaves the maximum unchanged.
+  uint32_t ef = 1;
+  if constexpr (!kDump) {
+    const uint4 *chunks = reinterpret_cast<const uint4 *>(ds + 4ull * (uint64_t)a_row * nblk_pad);
+    const uint32_t nq = k / 128u;
+    uint32_t mx = 0;
+    for (uint32_t c0 = sel; c0 < nq; c0 += 16u) {
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = chunks[min(c0 + 2u * j, nq - 1u)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        mx = max(mx, max(max(v[j].x & 0x7FFFu, v[j].y & 0x7FFFu), max(v[j].z & 0x7FFFu, v[j].w & 0x7FFFu)));
+    }
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xF, 0xF, false));
+    ef = max(mx >> 10, 1u);
+    if (sel == 0u) q4k_rowexp[srow] = (int)ef;
+  }
 #define BQMM_FETCH(st)                                                                                  \
   do {                                                                                                  \
     const uint32_t sb_ = (st) >> 2, t_ = (st) & 3u;                                                     \
@@ -162,8 +184,6 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
     rw0 = *reinterpret_cast<const uint4 *>(bp_ + 16u + 32u * t_);                                       \
     rw1 = *reinterpret_cast<const uint4 *>(bp_ + 32u + 32u * t_);                                       \
     rds = *reinterpret_cast<const uint32_t *>(ds + 4ull * ((uint64_t)a_row * nblk_pad + 2u * (st) + sel)); \
-    if (!kDump && t_ == 0u)                                                                             \
-      rdd = *reinterpret_cast<const uint4 *>(ds + 4ull * ((uint64_t)a_row * nblk_pad + 8u * sb_ + 4u * sel)); \
   } while (0)
 
   // Write the prefetched stage into LDS stage buffer `buf`; stage st of
@@ -179,14 +199,6 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
       const uint32_t x_[8] = {ra0.x, ra0.y, ra0.z, ra0.w, ra1.x, ra1.y, ra1.z, ra1.w};                  \
       _Pragma("unroll") for (int i = 0; i < 8; ++i) s8x4_to_f16(x_[i], h[2 * i], h[2 * i + 1]);         \
       if (!kDump) {                                                                                     \
-        if (t_ == 0u) {                                                                                 \
-          /* largest |da| of the row's eight blocks: four here, four in the */                          \
-          /* partner lane (tid ^ 1, same quad); e = ef - 23                  */                         \
-          uint32_t mx_ = max(max(rdd.x & 0x7FFFu, rdd.y & 0x7FFFu), max(rdd.z & 0x7FFFu, rdd.w & 0x7FFFu)); \
-          mx_ = max(mx_, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx_, 0xB1, 0xF, 0xF, false));     \
-          ef = max(mx_ >> 10, 1u);                                                                      \
-          reinterpret_cast<float *>(SB + kSbE)[srow] = __builtin_amdgcn_ldexpf(1.0f, (int)ef - 23);     \
-        }                                                                                               \
         const _Float16 a_ = (_Float16)__builtin_amdgcn_ldexpf(f16_bits_to_f32(rds & 0xFFFFu), 23 - (int)ef); \
         const v2h av_ = {a_, a_};                                                                       \
         _Pragma("unroll") for (int i = 0; i < 16; ++i)                                                  \
@@ -218,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
         /* each unpack form is known at compile time); both write d         */                          \
         const float d_ = f16_bits_to_f32(rh.x & 0xFFFFu), dmin_ = f16_bits_to_f32(rh.x >> 16);         \
         reinterpret_cast<float *>(SB + kSbD)[srow] = d_;                                                \
-        reinterpret_cast<float *>(SB + kSbNdmin)[srow] = -dmin_;                                        \
+        reinterpret_cast<float *>(SB + kSbNdmin)[srow] = -64.0f * dmin_;                                \
         _Float16 *nm_ = reinterpret_cast<_Float16 *>(SB + kSbMin + srow * 16);                          \
         _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                                 \
           const int j_ = 2 * (int)sel + q;                                                              \
@@ -230,7 +242,8 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
         }                                                                                               \
       }                                                                                                 \
     }                                                                                                   \
-    reinterpret_cast<uint16_t *>(SB + kSbS)[8u * srow + 2u * t_ + sel] = (uint16_t)(rds >> 16);         \
+    reinterpret_cast<_Float16 *>(SB + kSbS)[8u * srow + 2u * t_ + sel] =                                \
+        (_Float16)__builtin_amdgcn_ldexpf(f16_bits_to_f32(rds >> 16), 17 - (int)ef);                    \
   } while (0)
 
   v16f acc_out[2][2], acc[2][2];
@@ -270,13 +283,25 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
         for (int sn = 0; sn < 2; ++sn)
           A[sn][h] = *reinterpret_cast<const v8h *>(w_lds + swz(wn * 64 + sn * 32 + l32, 4 * b + 2 * h + hi));
       }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
+      // a super-block's first MFMA starts from zero (no clearing of acc)
+      if (!kDump && b == 0 && t == 0u) {
 #pragma unroll
         for (int sn = 0; sn < 2; ++sn)
 #pragma unroll
           for (int sm = 0; sm < 2; ++sm)
-            acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[sn][h], B[sm][h], acc[sn][sm], 0, 0, 0);
+            acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[sn][0], B[sm][0], zero16, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn)
+#pragma unroll
+          for (int sm = 0; sm < 2; ++sm)
+            acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[sn][0], B[sm][0], acc[sn][sm], 0, 0, 0);
+      }
+#pragma unroll
+      for (int sn = 0; sn < 2; ++sn)
+#pragma unroll
+        for (int sm = 0; sm < 2; ++sm)
+          acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[sn][1], B[sm][1], acc[sn][sm], 0, 0, 0);
       if constexpr (kDump) {
 #pragma unroll
         for (int sn = 0; sn < 2; ++sn)
@@ -296,9 +321,9 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
 
     if constexpr (!kDump) {
       if (t == 3u) {
-        // end of a super-block: undo the activation row's 2^-e, apply each
-        // weight row's d, then the min term: sum_j m_j * s_j on the matrix
-        // core (K = 8: the super-block's eight sub-blocks) times -dmin
+        // end of a super-block: apply each weight row's d, then the min
+        // term: sum_j m_j * s_j * 2^-(e + 6) on the matrix core (K = 8: the
+        // super-block's eight sub-blocks) times -64 dmin
         const uint8_t *SB = sb_lds + ((st >> 2) & 1u) * kSbBytes;
 #pragma unroll
         for (int sn = 0; sn < 2; ++sn) {
@@ -317,13 +342,10 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
           for (int sm = 0; sm < 2; ++sm) {
             const uint32_t ml = wm * 64 + sm * 32 + l32;
             const v4h bs = *reinterpret_cast<const v4h *>(SB + kSbS + ml * 16 + 8 * hi);
-            const float e2 = reinterpret_cast<const float *>(SB + kSbE)[ml];
             const v16f Dm = __builtin_amdgcn_mfma_f32_32x32x8f16(an, bs, zero16, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              acc_out[sn][sm][r] = fmaf(Dm[r], nv[r], fmaf(acc[sn][sm][r] * e2, dv[r], acc_out[sn][sm][r]));
-              acc[sn][sm][r] = 0.0f;
-            }
+            for (int r = 0; r < 16; ++r)
+              acc_out[sn][sm][r] = fmaf(Dm[r], nv[r], fmaf(acc[sn][sm][r], dv[r], acc_out[sn][sm][r]));
           }
         }
       }
@@ -336,14 +358,19 @@ __global__ __launch_bounds__(kThreads, 2) void q4k_mmq_kernel(
     const bool full = (m_base + BM <= m) && (n_base + BN <= n) && (ldc % 4u) == 0u;
 #pragma unroll
     for (int sm = 0; sm < 2; ++sm) {
-      const uint32_t mm = m_base + wm * 64 + sm * 32 + l32;
+      const uint32_t mloc = wm * 64 + sm * 32 + l32;
+      const uint32_t mm = m_base + mloc;
       uint16_t *orow = out + (uint64_t)min(mm, m - 1u) * ldc;
+      // undo the activation operand's 2^-e (exact: a power of two)
+      const float e2 = __builtin_amdgcn_ldexpf(1.0f, q4k_rowexp[mloc] - 23);
 #pragma unroll
       for (int sn = 0; sn < 2; ++sn)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t nn = n_base + wn * 64 + sn * 32 + 8 * q + 4 * hi;
-          const v16f &v = acc_out[sn][sm];
+          v16f v = acc_out[sn][sm];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * q + e] *= e2;
           if (full) {
             *reinterpret_cast<uint2 *>(orow + nn) =
                 make_uint2(pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3]));

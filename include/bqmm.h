@@ -228,11 +228,11 @@ int q2_0_prefill_gemm_noalloc(const void *act_bf16, const void *w_q2, void *out_
 /* Q4_K MMQ: out[m][n] (bf16) = sum_k deq(act_q8)[m][k] * deq_q4k(w)[n][k],
  * on fp16 matrix cores: the weight operand q4 * sc_j is exact, the
  * activation operand is q * da * 2^-e rounded once to binary16 (relative
- * error at most 2^-11; e per activation row and super-block, from its largest
- * da; a block more than 2^22 below that largest loses one bit of its scale
- * per binade, and beyond about 2^33 contributes nothing), the min term from
- * the exact m_j and the stored q8_1 sums, with
- * 2^e, d and dmin applied in fp32 once per super-block.
+ * error at most 2^-11; e per activation row, from its largest da; a block
+ * more than 2^22 below that largest loses one bit of its scale per binade,
+ * and beyond about 2^33 contributes nothing), the min term from the exact
+ * m_j and the stored q8_1 sums times 2^-(e + 6), d and dmin applied in fp32
+ * once per super-block and 2^e once per output.
  * [page layers/ops/q4k_mmq.rs, fn q4k_mmq_gemm: C[m, n] = A[m, k] x W[n, k],
  *  A in q8_1, W in block_q4_K, BF16 store; any n.]  k % 256 == 0. */
 int q4k_mmq_gemm(const void *act_q8, const void *w_q4k, void *out_bf16,

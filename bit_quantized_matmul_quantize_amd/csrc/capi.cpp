@@ -260,8 +260,7 @@ int q4k_gemv_vec(const void *act_bf16, const void *w_q4k, void *out_bf16, uint32
   REQUIRE(act_bf16 && w_q4k && out_bf16, BQ_EINVAL, "q4k_gemv_vec: null pointer");
   REQUIRE(n >= 1 && k >= 1, BQ_EINVAL, "q4k_gemv_vec: n=%u k=%u must be >= 1", n, k);
   REQUIRE(k % 256u == 0, BQ_EINVAL, "q4k_gemv_vec: k=%u must be a multiple of 256", k);
-  REQUIRE(k <= 65536u, BQ_EUNSUPPORTED, "q4k_gemv_vec: k=%u > 65536", k);
-  REQUIRE(n <= kMaxRows, BQ_EINVAL, "q4k_gemv_vec: n=%u too large", n);
+  REQUIRE(k <= kMaxK && n <= kMaxRows, BQ_EINVAL, "q4k_gemv_vec: n=%u k=%u too large", n, k);
   REQUIRE(aligned16(act_bf16) && aligned16(w_q4k) && aligned16(out_bf16), BQ_EALIGN,
           "q4k_gemv_vec: buffers must be 16-byte aligned");
   REQUIRE_DISJOINT("q4k_gemv_vec", out_bf16, bf16_bytes(1, n), act_bf16, bf16_bytes(1, k), "the activations");

@@ -25,7 +25,9 @@
 //
 // Work split: the whole activation vector is prepared once per workgroup in
 // LDS (36 dwords per unit: 16 pairs per sub-block, the two B, padding that
-// keeps 16 consecutive units on distinct bank quads).  A group of G lanes
+// keeps 16 consecutive units on distinct bank quads); beyond k = 65536
+// (1024 units, 147 KB) it is prepared and consumed 1024 units at a time, with
+// a barrier between chunks, in a second instantiation of the kernel.  A group of G lanes
 // serves R rows; lane li takes units li, li + G, ...; since G is a multiple
 // of 4, the lane's chunk t = li % 4 is fixed and so are its scale-field
 // positions.  Per row and unit a lane loads the 16-byte header and the two
@@ -38,14 +40,16 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnitDw = 36;                 // LDS dwords per unit
-constexpr uint32_t kMaxK = 65536;           // 1024 units: 147 KB of LDS
+constexpr uint32_t kChunkUnits = 1024;      // units staged in LDS at a time: 147 KB, k = 65536
 constexpr uint32_t kMagic128 = 0x43004300u;  // bf16 128.0 in both halves
 
 struct UnitLoads {
   uint4 h, c0, c1;  // header, code bytes 0..15 and 16..31 of the unit
 };
 
-template <int G, int R>
+// kChunked: k > 65536, the activation vector staged one chunk of 1024 units
+// at a time (otherwise in one piece, as a single chunk).
+template <int G, int R, bool kChunked>
 __global__ __launch_bounds__(kThreads) void q4k_gemv1_kernel(const uint16_t *__restrict__ act,
                                                              const uint8_t *__restrict__ w,
                                                              uint16_t *__restrict__ out, uint32_t n,
@@ -55,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void q4k_gemv1_kernel(const uint16_t *__r
   const uint32_t tid = threadIdx.x;
   const uint32_t li = tid % G, grp = tid / G;
   const uint32_t nsb = k >> 8, U = nsb * 4u;
-  const uint32_t iters = (U + G - 1) / G, Upad = iters * G;
+  uint32_t ub = 0;  // first unit of the chunk staged in LDS
   const uint32_t row_base = blockIdx.x * (kThreads / G * R) + grp * R;
 
   // Weight loads, unconditional from clamped addresses: a row past n reads
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void q4k_gemv1_kernel(const uint16_t *__r
   for (int r = 0; r < R; ++r)
     wrow[r] = w + (uint64_t)min(row_base + r, n - 1u) * nsb * 144u + 16u + 32u * t;
   auto load_unit = [&](uint32_t it, UnitLoads (&L)[R]) {
-    const uint32_t sb = min(li + G * it, U - 1u) >> 2;
+    const uint32_t sb = min(ub + li + G * it, U - 1u) >> 2;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint8_t *p = wrow[r] + sb * 144u;
@@ -82,12 +86,11 @@ __global__ __launch_bounds__(kThreads) void q4k_gemv1_kernel(const uint16_t *__r
   // and B.  The first item's activation loads go out before the first weight
   // loads: vector-memory counters retire in order, so the prep then waits for
   // the (L2-resident) activations only.
-  const uint32_t items = 2u * Upad;
   auto prep = [&](uint32_t item, const uint4 (&v)[4]) {
     const uint32_t u = item >> 1, hs = item & 1u;
     uint32_t D[16] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w,
                       v[2].x, v[2].y, v[2].z, v[2].w, v[3].x, v[3].y, v[3].z, v[3].w};
-    if (u >= U) {
+    if (ub + u >= U) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) D[i] = 0u;
     }
@@ -105,28 +108,13 @@ __global__ __launch_bounds__(kThreads) void q4k_gemv1_kernel(const uint16_t *__r
   };
   auto act_src = [&](uint32_t item) {
     // unit u = (super-block u / 4, chunk u % 4): values 64u .. 64u + 63
-    return act + 64u * min(item >> 1, U - 1u) + 32u * (item & 1u);
+    return act + 64u * min(ub + (item >> 1), U - 1u) + 32u * (item & 1u);
   };
   auto load_act = [&](uint32_t item, uint4 (&v)[4]) {
     const uint4 *src = reinterpret_cast<const uint4 *>(act_src(item));
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = src[q];
   };
-  {
-    const uint32_t first = min(tid, items - 1u);
-    uint4 v[4];
-    load_act(first, v);
-    load_unit(0, cur);
-    // lanes past the last item redo it: same values to the same LDS words
-    prep(first, v);
-  }
-  for (uint32_t item = tid + kThreads; item < items; item += kThreads) {
-    uint4 v[4];
-    load_act(item, v);
-    prep(item, v);
-  }
-  __syncthreads();
-
   // Lane-fixed positions of the two sub-blocks' 6-bit fields (j = 2t, 2t+1).
   // t < 2:  sc_j = S[j] & 63, m_j = S[j+4] & 63            (header words y, z)
   // t >= 2: sc_j = (S[j+4] & 15) | (S[j-4] >> 6) << 4,
@@ -180,27 +168,52 @@ __global__ __launch_bounds__(kThreads) void q4k_gemv1_kernel(const uint16_t *__r
     }
   };
 
-  // Two register sets alternate (unrolled by two, so nothing is copied); the
-  // last one or two units are peeled so that every prefetch is unconditional.
-  // The scheduling barriers keep each prefetch above the wait for the unit
-  // being computed (left alone, the scheduler sinks the loads below it and
-  // only one unit per lane is ever in flight).
-  uint32_t it = 0;
-  for (; it + 2 < iters; it += 2) {
-    load_unit(it + 1, nxt);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(it, cur);
-    load_unit(it + 2, cur);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(it + 1, nxt);
-  }
-  if (it + 1 < iters) {
-    load_unit(it + 1, nxt);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(it, cur);
-    compute(it + 1, nxt);
-  } else {
-    compute(it, cur);
+  // The activation vector is staged chunk by chunk (one chunk for k <= 65536).
+  for (;;) {
+    const uint32_t Uc = kChunked ? min(U - ub, kChunkUnits) : U;
+    const uint32_t iters = (Uc + G - 1) / G, Upad = iters * G;
+    const uint32_t items = 2u * Upad;
+    if (kChunked && ub > 0) __syncthreads();  // every lane is done with the previous chunk's LDS
+    {
+      const uint32_t first = min(tid, items - 1u);
+      uint4 v[4];
+      load_act(first, v);
+      load_unit(0, cur);
+      // lanes past the last item redo it: same values to the same LDS words
+      prep(first, v);
+    }
+    for (uint32_t item = tid + kThreads; item < items; item += kThreads) {
+      uint4 v[4];
+      load_act(item, v);
+      prep(item, v);
+    }
+    __syncthreads();
+
+    // Two register sets alternate (unrolled by two, so nothing is copied); the
+    // last one or two units are peeled so that every prefetch is unconditional.
+    // The scheduling barriers keep each prefetch above the wait for the unit
+    // being computed (left alone, the scheduler sinks the loads below it and
+    // only one unit per lane is ever in flight).
+    uint32_t it = 0;
+    for (; it + 2 < iters; it += 2) {
+      load_unit(it + 1, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(it, cur);
+      load_unit(it + 2, cur);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(it + 1, nxt);
+    }
+    if (it + 1 < iters) {
+      load_unit(it + 1, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(it, cur);
+      compute(it + 1, nxt);
+    } else {
+      compute(it, cur);
+    }
+    if (!kChunked) break;
+    ub += kChunkUnits;
+    if (ub >= U) break;
   }
 
   static_assert(G == 16 || G == 32, "row sums over 16 or 32 lanes");
@@ -215,18 +228,18 @@ __global__ __launch_bounds__(kThreads) void q4k_gemv1_kernel(const uint16_t *__r
   }
 }
 
-template <int G, int R>
+template <int G, int R, bool kChunked>
 hipError_t launch_g(const void *act, const void *w, void *out, uint32_t n, uint32_t k, hipStream_t s) {
-  const uint32_t U = (k >> 8) * 4u, Upad = (U + G - 1) / G * G;
-  const size_t lds = (size_t)Upad * kUnitDw * 4u;
+  const uint32_t U = (k >> 8) * 4u, Uc = U < kChunkUnits ? U : kChunkUnits;
+  const size_t lds = (size_t)((Uc + G - 1) / G * G) * kUnitDw * 4u;
   if (lds > 65536) {
-    const hipError_t attr_err = ensure_dynamic_lds(reinterpret_cast<const void *>(q4k_gemv1_kernel<G, R>),
-                                                   (int)((size_t)(kMaxK / 64u) * kUnitDw * 4u));
+    const hipError_t attr_err = ensure_dynamic_lds(
+        reinterpret_cast<const void *>(q4k_gemv1_kernel<G, R, kChunked>), (int)((size_t)kChunkUnits * kUnitDw * 4u));
     if (attr_err != hipSuccess) return attr_err;
   }
   constexpr uint32_t rows_per_block = kThreads / G * R;
   const uint32_t blocks = (n + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((q4k_gemv1_kernel<G, R>), dim3(blocks), dim3(kThreads), lds, s,
+  hipLaunchKernelGGL((q4k_gemv1_kernel<G, R, kChunked>), dim3(blocks), dim3(kThreads), lds, s,
                      static_cast<const uint16_t *>(act), static_cast<const uint8_t *>(w),
                      static_cast<uint16_t *>(out), n, k);
   return hipGetLastError();
@@ -236,13 +249,13 @@ hipError_t launch_g(const void *act, const void *w, void *out, uint32_t n, uint3
 
 hipError_t launch_q4k_gemv(const void *act, const void *w, void *out, uint32_t n, uint32_t k,
                            hipStream_t s) {
-  if (k > kMaxK) return hipErrorInvalidValue;
   // Half-wave groups, one row per lane: measured on the FFN shapes against
   // 16-lane groups and two rows per lane (gate [17408, 5120] 11.3 us vs
   // 11.6 / 13.3 us; down [5120, 17408] 12.9 us vs 13.8 / 14.0 us): more
   // workgroups of fewer rows balance better over the compute units, and the
   // per-instruction footprint of one row per lane is more compact.
-  return launch_g<32, 1>(act, w, out, n, k, s);
+  if (k > 256u * kChunkUnits / 4u) return launch_g<32, 1, true>(act, w, out, n, k, s);
+  return launch_g<32, 1, false>(act, w, out, n, k, s);
 }
 
 }  // namespace bqmm

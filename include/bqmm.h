@@ -245,8 +245,8 @@ int q4k_mmq_gemm(const void *act_q8, const void *w_q4k, void *out_bf16,
  *  the bf16-input decode form follows the Q2_0 decode GEMV, page
  *  layers/qwen3_ssm/init.rs, q2_0_gemv_vec.]
  * act_bf16: [k]; w_q4k: [n][k/256] blocks of 144 bytes; out_bf16: [n].
- * k % 256 == 0 and k <= 65536 (the activation vector is staged in LDS;
- * larger k returns BQ_EUNSUPPORTED); n >= 1. */
+ * k % 256 == 0 (the activation vector is staged in LDS 65536 values at a
+ * time); n >= 1. */
 int q4k_gemv_vec(const void *act_bf16, const void *w_q4k, void *out_bf16,
                  uint32_t n, uint32_t k, void *stream);
 

@@ -107,7 +107,7 @@ def _err(bq):
     (lambda l: l.q4k_gemv_vec(A, B, C, 0, 512, None), -1, "n=0"),
     (lambda l: l.q4k_gemv_vec(None, B, C, 4, 512, None), -1, "null"),
     (lambda l: l.q4k_gemv_vec(A, MIS, C, 4, 512, None), -3, "aligned"),
-    (lambda l: l.q4k_gemv_vec(A, B, C, 4, 65536 + 256, None), -2, "> 65536"),
+    (lambda l: l.q4k_gemv_vec(A, B, C, 4, (1 << 30) + 256, None), -1, "too large"),
     (lambda l: l.quantize_weight_q4k(A, B, 4, 300, None), -1, "multiple of 256"),
     (lambda l: l.quantize_weight_q4k(A, None, 4, 512, None), -1, "null"),
     (lambda l: l.quantize_weight_q4k(A, MIS, 4, 512, None), -3, "aligned"),

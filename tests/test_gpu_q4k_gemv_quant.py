@@ -38,7 +38,10 @@ def test_gemv_workload_shapes(gpu, n, k, seed):
 
 
 @pytest.mark.parametrize("n,k,seed", [(7, 512, 111), (33, 768, 112), (1, 256, 113), (3, 256, 114),
-                                      (64, 65536, 115), (17, 1280, 116)])
+                                      (64, 65536, 115), (17, 1280, 116),
+                                      # past one LDS chunk of 65536 values: a second, ragged
+                                      # chunk, and three full chunks
+                                      (9, 65536 + 1280, 119), (5, 3 * 65536, 120)])
 def test_gemv_edge_shapes(gpu, n, k, seed):
     g = inputs.rng(seed)
     w = inputs.q4k_weight(g, n, k)
@@ -75,10 +78,6 @@ def test_gemv_rejects(gpu):
     out = empty_bf16((4,), gpu)
     with pytest.raises(bq.BqmmError):
         bq.q4k_gemv_vec(a, w, out, 4, 500)
-    big = torch.zeros(65536 + 256, dtype=torch.bfloat16, device=gpu)
-    wb = torch.zeros(oracle.q4k_bytes(1, 65536 + 256), dtype=torch.uint8, device=gpu)
-    with pytest.raises(bq.BqmmError):
-        bq.q4k_gemv_vec(big, wb, out, 1, 65536 + 256)
 
 
 # --- weight quantizer ------------------------------------------------------

@@ -458,8 +458,9 @@ def timed_oracle(fn, budget_s, max_calls):
 def cpu_baselines(ctx, budget):
     """The oracle on one pinned host core, on bounded samples of each workload:
     the tiny case whole, the decode GEMV in whole calls, the m = 2 verify chain
-    whole, the m = 2048 prefill MMQ and the m = 4096 FFN chain on 16
-    activation rows with all n (their cost is linear in rows), extrapolated."""
+    whole, the m = 2048 prefill MMQ and the m = 4096 FFN chains (Q2_0 and
+    Q4_K) on 16 activation rows with all n (their cost is linear in rows),
+    extrapolated."""
     import oracle
     import inputs
     try:
@@ -521,12 +522,28 @@ def cpu_baselines(ctx, budget):
             q8h, _ = oracle.quantize_act_q8_1(oracle.silu_mul_bf16(g, u), rows, I)
             oracle.q2_0_mmq(q8h, W["wd"], rows, H, I)
 
-        calls, t = timed_oracle(c5, 0.3 * budget, 5)
+        calls, t = timed_oracle(c5, 0.15 * budget, 5)
         out["ffn_prefill_q2_0_m4096"] = {
             "value": round(3 * 2.0 * rows * H * I * calls / t / 1e12, 6), "unit": "TOPS", "cores": 1,
             "kind": "oracle", "extrapolated_ms_m4096": round(t * 1e3 / calls * 4096 / rows, 1),
             "sample": f"{calls} oracle Q2_0 FFN chains (quantize, gate, up, silu_mul, quantize, down) on {rows} of "
                       f"the 4096 rows, {t:.1f} s on {host}; extrapolated from 16 rows (linear in rows)"}
+        if "q4k" in F:
+            W4 = F["q4k"]
+
+            def c5k():
+                q8, _ = oracle.quantize_act_q8_1(x, rows, H)
+                g = oracle.round_bf16(oracle.q4k_mmq(q8, W4["wg"], rows, I, H))
+                u = oracle.round_bf16(oracle.q4k_mmq(q8, W4["wu"], rows, I, H))
+                q8h, _ = oracle.quantize_act_q8_1(oracle.silu_mul_bf16(g, u), rows, I)
+                oracle.q4k_mmq(q8h, W4["wd"], rows, H, I)
+
+            calls, t = timed_oracle(c5k, 0.15 * budget, 5)
+            out["ffn_prefill_q4k_m4096"] = {
+                "value": round(3 * 2.0 * rows * H * I * calls / t / 1e12, 6), "unit": "TOPS", "cores": 1,
+                "kind": "oracle", "extrapolated_ms_m4096": round(t * 1e3 / calls * 4096 / rows, 1),
+                "sample": f"{calls} oracle Q4_K FFN chains (quantize, gate, up, silu_mul, quantize, down) on {rows} "
+                          f"of the 4096 rows, {t:.1f} s on {host}; extrapolated from 16 rows (linear in rows)"}
     return out
 
 

@@ -38,10 +38,23 @@
 // two 8-wave workgroups share a CU and all 363 fit at once (20.4 us, was 25.4
 // with T = 2 at 134 VGPRs, one workgroup per CU and 544 of them); narrow
 // (n = 5120) T = 2, 160 workgroups (24.7 us, was 31.2 with T = 1); fused
-// gate/up T = 3 of each weight (36.7 us, was 46.1 with T = 1).  There is no
-// barrier in the main loop.  A wave's weight scales are staged once in LDS
+// gate/up T = 3 of each weight (36.7 us, was 46.1 with T = 1).
+// Balanced rows: where that grid has more workgroups than the chip has
+// compute units, some units run two workgroups and others one, and the units
+// with two set the time.  The launch then gives every unit one workgroup of
+// rb = ceil(n / CUs) rows (68 for n = 17408 on 256 units) in T = ceil(rb / 16)
+// tiles, the last one starting at row rb - 16 so that it overlaps its
+// neighbour inside the workgroup (no row is loaded by two workgroups; the
+// overlapped rows are stored once).  Same-box A/B, m = 4 / 6 / 8, identical
+// outputs: gate 17.0 / 17.7 / 19.2 -> 14.7 / 15.2 / 15.9 us, fused gate/up
+// 29.8 / 30.9 / 32.5 -> 27.1 / 27.8 / 28.6 us.  The narrow down projection
+// (160 workgroups, one per unit) gains nothing from it: split into 256
+// workgroups of 20 rows it measured 2% slower.  There is no barrier in the
+// main loop.  A wave's weight scales are staged once in LDS
 // ([group][row], so one 8-byte read gives the four rows of a lane's
 // outputs).  Loads run P groups ahead, unconditionally from clamped addresses.
+#include <atomic>
+
 #include "gemv_common.h"
 
 namespace bqmm {
@@ -67,7 +80,7 @@ __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint
                                                                 const uint8_t *__restrict__ w,
                                                                 const uint8_t *__restrict__ w2,
                                                                 uint16_t *__restrict__ out,
-                                                                uint32_t n, uint32_t k) {
+                                                                uint32_t n, uint32_t k, uint32_t rb) {
   static_assert(M >= 1 && M <= 16, "one MFMA column per activation row");
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   static_assert(NW == 1 || NW == 2, "one weight, or gate and up");
@@ -78,14 +91,15 @@ __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint
   const uint32_t G = k >> 7;
   const uint32_t gmax = (G + W - 1) / W;  // groups of the widest wave
   const uint32_t gb = wave * G / W, ng = (wave + 1) * G / W - gb;  // >= 1 since G >= W
-  const uint32_t row0 = blockIdx.x * kRows;
+  // rb rows per workgroup (16 <= rb <= 16 T); tile t starts at row min(16 t, rb - 16)
+  const uint32_t row0 = blockIdx.x * rb;
 
   // weight bytes 8 lg .. +7 of each 128-group of this lane's rows (rows past n
   // read row n - 1 and are not stored); slots T .. 2T-1 are the up rows
   const uint8_t *wp[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    const uint32_t row = min(row0 + 16u * (t % T) + lr, n - 1u);
+    const uint32_t row = min(row0 + min(16u * (t % T), rb - 16u) + lr, n - 1u);
     wp[t] = (t < T ? w : w2) + (uint64_t)row * (k >> 2) + 8u * lg;
   }
   const uint16_t *ap = act + (uint64_t)min(lr, (uint32_t)M - 1u) * k + 8u * lg;
@@ -119,7 +133,7 @@ __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint
       const uint32_t wv = i >= per_w ? 1u : 0u, rem = i - wv * per_w;
       const uint32_t gi = rem / kRows, r = rem - gi * kRows;
       const uint16_t *scales = reinterpret_cast<const uint16_t *>((wv == 0 ? w : w2) + (uint64_t)n * k / 4u);
-      v[b] = scales[(uint64_t)min(row0 + r, n - 1u) * G + gb + gi];
+      v[b] = scales[(uint64_t)min(row0 + min(r & ~15u, rb - 16u) + (r & 15u), n - 1u) * G + gb + gi];
       dst[b] = (wv * gmax + gi) * kRows + r;
     }
 #pragma unroll
@@ -216,7 +230,9 @@ __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint
       for (int v = 0; v < W; ++v) su += red[v * TT * 256 + T * 256 + src];
       h = f32_to_bf16_rne(silu_mul_f32(bf16_to_f32(h), bf16_to_f32(f32_to_bf16_rne(su))));
     }
-    if (row0 + r < n) out[(uint64_t)col * n + row0 + r] = (uint16_t)h;
+    // a row of the last tile that the tile before it covers is stored by that tile
+    const uint32_t lr0 = min(16u * t, rb - 16u) + rr;
+    if (lr0 >= 16u * t && lr0 < rb && row0 + lr0 < n) out[(uint64_t)col * n + row0 + lr0] = (uint16_t)h;
   }
 }
 
@@ -238,8 +254,43 @@ hipError_t launch_w(const void *act, const void *w, const void *w2, void *out, u
   const uint32_t blocks = (n + 16 * T - 1) / (16 * T);
   hipLaunchKernelGGL((q2_0_gemv_mfma_kernel<M, T, W, P, NW, MINW>), dim3(blocks), dim3(64 * W), lds, s,
                      static_cast<const uint16_t *>(act), static_cast<const uint8_t *>(w),
-                     static_cast<const uint8_t *>(w2), static_cast<uint16_t *>(out), n, k);
+                     static_cast<const uint8_t *>(w2), static_cast<uint16_t *>(out), n, k, 16u * T);
   return hipGetLastError();
+}
+
+// The balanced launch: one workgroup of rb rows per compute unit.  Its dynamic
+// LDS is raised to at least kBalancedMinLds, more than half a unit's 160 KB,
+// so that no unit takes two of them.
+constexpr size_t kBalancedMinLds = 81 * 1024;
+constexpr size_t kMaxLds = 160 * 1024;
+template <int M, int T, int NW, int P>
+hipError_t launch_balanced(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
+                           uint32_t rb, hipStream_t s) {
+  constexpr int W = 8;
+  size_t lds = lds_bytes(W, T, NW, k);
+  if (lds > kMaxLds) return hipErrorInvalidValue;  // checked by balanced_rows first
+  if (lds < kBalancedMinLds) lds = kBalancedMinLds;
+  const hipError_t e =
+      ensure_dynamic_lds(reinterpret_cast<const void *>(q2_0_gemv_mfma_kernel<M, T, W, P, NW, 1>), (int)lds);
+  if (e != hipSuccess) return e;
+  const uint32_t blocks = (n + rb - 1) / rb;
+  hipLaunchKernelGGL((q2_0_gemv_mfma_kernel<M, T, W, P, NW, 1>), dim3(blocks), dim3(64 * W), lds, s,
+                     static_cast<const uint16_t *>(act), static_cast<const uint8_t *>(w),
+                     static_cast<const uint8_t *>(w2), static_cast<uint16_t *>(out), n, k, rb);
+  return hipGetLastError();
+}
+
+// Compute units of the current device (queried once per device).
+inline uint32_t cu_count() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 0) v = 0;
+    cus[dev].store(v, std::memory_order_relaxed);
+  }
+  return (uint32_t)v;
 }
 
 // Eight waves split k when it has at least eight groups (W <= G is required).
@@ -290,11 +341,36 @@ inline void launch_shape(uint32_t n, uint32_t k, int NW, int &W, int &T) {
   }
 }
 
+// Rows per workgroup of the balanced launch for (n, k), or 0 where the plain
+// grid (T tiles per workgroup) fits the compute units in one workgroup each,
+// or the balanced tile count is outside 4..6 (4..5 for two weights: six tiles
+// of each spill registers), or its LDS does not fit.
+inline uint32_t balanced_rows(uint32_t n, uint32_t k, int NW, int T) {
+  const uint32_t ncu = cu_count();
+  if (ncu == 0 || (n + 16u * T - 1) / (16u * T) <= ncu) return 0;
+  const uint32_t rb = (n + ncu - 1) / ncu, tb = (rb + 15) / 16;
+  if (tb < 4 || tb > (NW == 2 ? 5u : 6u) || lds_bytes(8, (int)tb, NW, k) > kMaxLds) return 0;
+  return rb;
+}
+
 template <int M, int NW>
 hipError_t launch_m(const void *act, const void *w, const void *w2, void *out, uint32_t n, uint32_t k,
                     hipStream_t s) {
   const uint32_t G = k >> 7;
   if (G >= 8) {
+    const int Tp = NW == 2 ? BQMM_GEMVX_T_FUSED : (n >= BQMM_GEMVX_WIDE_N ? BQMM_GEMVX_T_WIDE : BQMM_GEMVX_T_NARROW);
+    const uint32_t rb = balanced_rows(n, k, NW, Tp);
+    if (rb != 0) {
+      // prefetch depth as in the plain launch: two groups for one weight, one for two
+      constexpr int P = NW == 2 ? 1 : 2;
+      switch ((rb + 15) / 16) {
+        case 4: return launch_balanced<M, 4, NW, P>(act, w, w2, out, n, k, rb, s);
+        case 5: return launch_balanced<M, 5, NW, P>(act, w, w2, out, n, k, rb, s);
+        default:
+          if constexpr (NW == 1) return launch_balanced<M, 6, NW, P>(act, w, w2, out, n, k, rb, s);
+          else return hipErrorInvalidValue;  // balanced_rows allows at most five tiles here
+      }
+    }
     if constexpr (NW == 2) {
       return launch_w<M, 8, BQMM_GEMVX_T_FUSED, NW, BQMM_GEMVX_MINW_FUSED, BQMM_GEMVX_P_FUSED>(act, w, w2, out, n,
                                                                                               k, s);

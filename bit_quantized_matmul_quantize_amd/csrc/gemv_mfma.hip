@@ -9,18 +9,35 @@
 // ALU that work grows with m (two per v_dot2), so this kernel moves the
 // products to v_mfma_f32_16x16x32_bf16 and keeps the VALU for the
 // m-independent part: turning codes into bf16 (about 0.75 ops per code).
-// Its weight loads cover 32 bytes of each of 16 rows per instruction, which
-// streams at about half the rate of row-contiguous loads, so the dispatcher
-// uses it only where the per-code ALU work of the vector kernel is larger.
+// The dispatcher uses it only where the per-code ALU work of the vector
+// kernel is larger.
 //
 // Operands of one MFMA (field j of a 128-group, i.e. the 32 k of block j):
-//   A = 16 weight rows x 32 k; lane l holds row l % 16 and the 8 consecutive
-//       k = 8 (l / 16) .. +7, i.e. bytes 8 (l / 16) .. +7 of the row's group,
-//       code field j, as bf16 2^e_j + c (mantissa OR, exact; e = 7, 5, 3, 2);
+//   A = 16 weight rows x 32 k; lane l holds row l % 16 and, with lg = l / 16,
+//       the 8 consecutive k = bo .. bo + 7 of field j, bo = 16 (lg & 1) +
+//       8 (lg >> 1), i.e. bytes bo .. bo + 7 of the row's group (the four
+//       lane groups cover the 32 bytes in a permuted order), code field j,
+//       as bf16 2^e_j + c (mantissa OR, exact; e = 7, 5, 3, 2);
 //   B = the same 32 k x 16 columns; column j' < m is activation row j',
 //       loaded as 8 consecutive bf16 straight from memory (columns >= m
 //       repeat row m - 1 and their outputs are dropped);
 //   D = 16 x 16 fp32; lane l holds column l % 16, rows 4 (l / 16) .. +3.
+// Weight loads take two groups (64 bytes of a row) at once, four consecutive
+// lanes on one row's 64 bytes (lane l: row l / 4, 16-byte chunk l % 4), so an
+// instruction covers 16 rows x 64 contiguous bytes.  A wave hands each tile's
+// load to the MFMA layout through 1 KB of LDS (one 16-byte store and one load
+// per lane, conflict-free) and then one v_permlane32_swap per dword splits
+// the pair into the two groups' A words.  Against the earlier loads of one
+// group per instruction, 8 bytes per lane on 16 rows x 32 bytes (same-box
+// A/B at m = 4 / 6 / 8, identical results between the two new versions):
+// the pair loads alone took the down projection [5120, 17408] from 19.1 /
+// 20.3 / 22.7 to 16.9 / 18.0 / 20.4 us; with four consecutive lanes per row
+// segment (instead of lanes 16 apart) to 14.9 / 15.4 / 17.6 us; the gate
+// [17408, 5120] from 14.7 / 15.2 / 15.9 to 12.2 / 12.5 / 13.2 us and the
+// fused gate/up from 27.1 / 27.8 / 28.6 to 24.0 / 24.4 / 25.4 us.  Timing-only
+// copies with whole 128-byte row segments per instruction (8 rows each) ran
+// the gate in 11.1-11.7 us, but the quad-of-groups pipeline they need measured
+// slower than the pair one.
 // The constant part of the codes is removed by four more MFMAs per group with
 // A = -(2^e_j + 2) everywhere: their sum, -sum_k (2^e + 2) a_k for every row,
 // is the accumulator the weight MFMAs start from, so each group's result is
@@ -52,7 +69,8 @@
 // workgroups of 20 rows it measured 2% slower.  There is no barrier in the
 // main loop.  A wave's weight scales are staged once in LDS
 // ([group][row], so one 8-byte read gives the four rows of a lane's
-// outputs).  Loads run P groups ahead, unconditionally from clamped addresses.
+// outputs).  Loads run P pairs of groups ahead, unconditionally from clamped
+// addresses.
 #include <atomic>
 
 #include "gemv_common.h"
@@ -99,20 +117,39 @@ __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint
   const uint8_t *wp[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    const uint32_t row = min(row0 + min(16u * (t % T), rb - 16u) + lr, n - 1u);
-    wp[t] = (t < T ? w : w2) + (uint64_t)row * (k >> 2) + 8u * lg;
+    // loads: lane l takes row l / 4 of the tile, 16-byte chunk l % 4 of the
+    // pair (four consecutive lanes on 64 contiguous bytes of a row)
+    const uint32_t row = min(row0 + min(16u * (t % T), rb - 16u) + (lane >> 2), n - 1u);
+    wp[t] = (t < T ? w : w2) + (uint64_t)row * (k >> 2) + 16u * (G >= 2 ? (lane & 3u) : (lane & 1u));
   }
-  const uint16_t *ap = act + (uint64_t)min(lr, (uint32_t)M - 1u) * k + 8u * lg;
+  // a wave's 1 KB through which each tile's pair load is handed to the lanes
+  // of the MFMA layout: lane s stores at slot s ^ ((s >> 4) & 3) and lane
+  // (lr, lg) loads the slot of lane 4 lr + lg (both conflict-free)
+  v4u *tbuf = reinterpret_cast<v4u *>(reinterpret_cast<uint8_t *>(smem) +
+                                          ((2u * W * NW * kRows * gmax + 15u) & ~15u)) + 64u * wave;
+  const uint32_t wslot = lane ^ ((lane >> 4) & 3u);
+  const uint32_t src = 4u * lr + lg, rslot = src ^ ((src >> 4) & 3u);
+  // activation offset of the lane's eight k in each field: lane group lg
+  // supplies group bytes 16 (lg & 1) + 8 (lg >> 1) .. +7 (see the pair swap)
+  const uint32_t bo = 16u * (lg & 1u) + 8u * (lg >> 1);
+  const uint16_t *ap = act + (uint64_t)min(lr, (uint32_t)M - 1u) * k + bo;
+  const uint32_t npair = (ng + 1u) >> 1;
 
-  uint2 cq[P][TT];
-  uint4 aq[P][4];
-#define BQMM_LOADX(slot, gi)                                                        \
+  uint4 cq[P][TT];
+  uint4 aq[P][8];
+  // slot <- pair pi: groups 2 pi, 2 pi + 1 of the wave (clamped to its last);
+  // the weight load covers the pair of groups starting at ps = min(gA, G - 2)
+#define BQMM_LOADX(slot, pi)                                                        \
   do {                                                                              \
-    const uint32_t g_ = gb + min((uint32_t)(gi), ng - 1u);                          \
+    const uint32_t gA_ = gb + min(2u * (uint32_t)(pi), ng - 1u);                    \
+    const uint32_t gB_ = gb + min(2u * (uint32_t)(pi) + 1u, ng - 1u);               \
+    const uint32_t ps_ = G >= 2 ? min(gA_, G - 2u) : 0u;                            \
     _Pragma("unroll") for (int t = 0; t < TT; ++t)                                  \
-      cq[slot][t] = *reinterpret_cast<const uint2 *>(wp[t] + 32u * g_);             \
+      cq[slot][t] = *reinterpret_cast<const uint4 *>(wp[t] + 32u * ps_);            \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                   \
-      aq[slot][j] = *reinterpret_cast<const uint4 *>(ap + 128u * g_ + 32u * j);     \
+      aq[slot][j] = *reinterpret_cast<const uint4 *>(ap + 128u * gA_ + 32u * j);    \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                   \
+      aq[slot][4 + j] = *reinterpret_cast<const uint4 *>(ap + 128u * gB_ + 32u * j); \
   } while (0)
 
   // Stage this wave's scales in LDS: [weight][group][row] fp16.  A round
@@ -163,49 +200,97 @@ __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint
 
   // bytes of a code word reordered to (b0, b2, b1, b3): b0/b1 then sit in the
   // low bytes of the two halves (fields at bits 2j, 16 + 2j), b2/b3 after >> 8
-#define BQMM_COMPUTEX(slot, gi)                                                     \
+// one group: its A words (x0w, x1w: the lane's eight code bytes), its
+// activation operands aq[slot][ab .. ab + 3] and wave-relative index gi
+#define BQMM_GROUP(x0w, x1w, slot, ab, t, gi)                                       \
   do {                                                                              \
-    v4f nb_ = v4f{0.f, 0.f, 0.f, 0.f};                                              \
+    const uint16_t *srow_ = sc + (((t) / T) * gmax + (uint32_t)(gi)) * kRows + 4u * lg; \
+    const uint32_t x0_ = __builtin_amdgcn_perm((x0w), (x0w), 0x03010200u);          \
+    const uint32_t x1_ = __builtin_amdgcn_perm((x1w), (x1w), 0x03010200u);          \
+    const uint32_t y0_ = x0_ >> 8, y1_ = x1_ >> 8;                                  \
+    const v4u a0_ = {and_or(x0_, M0, G0), and_or(y0_, M0, G0), and_or(x1_, M0, G0), and_or(y1_, M0, G0)}; \
+    const v4u a1_ = {and_or(x0_, M1, G1), and_or(y0_, M1, G1), and_or(x1_, M1, G1), and_or(y1_, M1, G1)}; \
+    const v4u a2_ = {and_or(x0_, M2, G2), and_or(y0_, M2, G2), and_or(x1_, M2, G2), and_or(y1_, M2, G2)}; \
+    const v4u a3_ = {and_or(x0_ >> 1, M3, G3), and_or(y0_ >> 1, M3, G3),          \
+                     and_or(x1_ >> 1, M3, G3), and_or(y1_ >> 1, M3, G3)};         \
+    v4f s_ = mfma(a0_, v4u{aq[slot][ab].x, aq[slot][ab].y, aq[slot][ab].z, aq[slot][ab].w}, nb_); \
+    s_ = mfma(a1_, v4u{aq[slot][ab + 1].x, aq[slot][ab + 1].y, aq[slot][ab + 1].z, aq[slot][ab + 1].w}, s_); \
+    s_ = mfma(a2_, v4u{aq[slot][ab + 2].x, aq[slot][ab + 2].y, aq[slot][ab + 2].z, aq[slot][ab + 2].w}, s_); \
+    s_ = mfma(a3_, v4u{aq[slot][ab + 3].x, aq[slot][ab + 3].y, aq[slot][ab + 3].z, aq[slot][ab + 3].w}, s_); \
+    const uint2 dv_ = *reinterpret_cast<const uint2 *>(srow_ + 16u * ((t) % T));    \
+    acc_out[t][0] = fmaf(f16_bits_to_f32(dv_.x & 0xFFFFu), s_[0], acc_out[t][0]);   \
+    acc_out[t][1] = fmaf(f16_bits_to_f32(dv_.x >> 16), s_[1], acc_out[t][1]);       \
+    acc_out[t][2] = fmaf(f16_bits_to_f32(dv_.y & 0xFFFFu), s_[2], acc_out[t][2]);   \
+    acc_out[t][3] = fmaf(f16_bits_to_f32(dv_.y >> 16), s_[3], acc_out[t][3]);       \
+  } while (0)
+#define BQMM_BIAS(slot, ab)                                                         \
+  do {                                                                              \
+    nb_ = v4f{0.f, 0.f, 0.f, 0.f};                                                  \
     _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                 \
-      const v4u b_ = {aq[slot][j].x, aq[slot][j].y, aq[slot][j].z, aq[slot][j].w};  \
+      const v4u b_ = {aq[slot][ab + j].x, aq[slot][ab + j].y, aq[slot][ab + j].z, aq[slot][ab + j].w}; \
       nb_ = mfma(NK[j], b_, nb_);                                                   \
     }                                                                               \
+  } while (0)
+  // A pair of groups: lane (lr, lg) holds bytes 16 lg .. +15 of the pair's
+  // 64 bytes of row lr.  One v_permlane32_swap per dword (lanes 32..63 of the
+  // first operand trade places with lanes 0..31 of the second) leaves the
+  // first group's bytes 16 (lg & 1) + 8 (lg >> 1) .. +7 in the first result
+  // and the second group's in the second.
+#define BQMM_COMPUTEX(slot, pi)                                                     \
+  do {                                                                              \
+    const uint32_t gi_ = 2u * (uint32_t)(pi);                                       \
+    const uint32_t gA_ = gb + gi_;                                                  \
+    const uint32_t pos_ = G >= 2 ? gA_ - min(gA_, G - 2u) : 0u;                    \
+    v4u tv_[TT];                                                                    \
     _Pragma("unroll") for (int t = 0; t < TT; ++t) {                                \
-      const uint16_t *srow_ = sc + ((t / T) * gmax + (uint32_t)(gi)) * kRows + 4u * lg; \
-      const uint32_t x0_ = __builtin_amdgcn_perm(cq[slot][t].x, cq[slot][t].x, 0x03010200u); \
-      const uint32_t x1_ = __builtin_amdgcn_perm(cq[slot][t].y, cq[slot][t].y, 0x03010200u); \
-      const uint32_t y0_ = x0_ >> 8, y1_ = x1_ >> 8;                                \
-      const v4u a0_ = {and_or(x0_, M0, G0), and_or(y0_, M0, G0), and_or(x1_, M0, G0), and_or(y1_, M0, G0)}; \
-      const v4u a1_ = {and_or(x0_, M1, G1), and_or(y0_, M1, G1), and_or(x1_, M1, G1), and_or(y1_, M1, G1)}; \
-      const v4u a2_ = {and_or(x0_, M2, G2), and_or(y0_, M2, G2), and_or(x1_, M2, G2), and_or(y1_, M2, G2)}; \
-      const v4u a3_ = {and_or(x0_ >> 1, M3, G3), and_or(y0_ >> 1, M3, G3),        \
-                       and_or(x1_ >> 1, M3, G3), and_or(y1_ >> 1, M3, G3)};       \
-      v4f s_ = mfma(a0_, v4u{aq[slot][0].x, aq[slot][0].y, aq[slot][0].z, aq[slot][0].w}, nb_); \
-      s_ = mfma(a1_, v4u{aq[slot][1].x, aq[slot][1].y, aq[slot][1].z, aq[slot][1].w}, s_);      \
-      s_ = mfma(a2_, v4u{aq[slot][2].x, aq[slot][2].y, aq[slot][2].z, aq[slot][2].w}, s_);      \
-      s_ = mfma(a3_, v4u{aq[slot][3].x, aq[slot][3].y, aq[slot][3].z, aq[slot][3].w}, s_);      \
-      const uint2 dv_ = *reinterpret_cast<const uint2 *>(srow_ + 16u * (t % T));    \
-      acc_out[t][0] = fmaf(f16_bits_to_f32(dv_.x & 0xFFFFu), s_[0], acc_out[t][0]); \
-      acc_out[t][1] = fmaf(f16_bits_to_f32(dv_.x >> 16), s_[1], acc_out[t][1]);     \
-      acc_out[t][2] = fmaf(f16_bits_to_f32(dv_.y & 0xFFFFu), s_[2], acc_out[t][2]); \
-      acc_out[t][3] = fmaf(f16_bits_to_f32(dv_.y >> 16), s_[3], acc_out[t][3]);     \
+      tbuf[wslot] = v4u{cq[slot][t].x, cq[slot][t].y, cq[slot][t].z, cq[slot][t].w}; \
+      __builtin_amdgcn_wave_barrier();                                              \
+      tv_[t] = tbuf[rslot];                                                         \
+      __builtin_amdgcn_wave_barrier();                                              \
+    }                                                                               \
+    v4f nb_;                                                                        \
+    if (gi_ + 1u < ng) {                                                            \
+      BQMM_BIAS(slot, 0);                                                           \
+      _Pragma("unroll") for (int t = 0; t < TT; ++t) {                              \
+        const v4u v_ = tv_[t];                                                      \
+        const auto sx_ = __builtin_amdgcn_permlane32_swap(v_.x, v_.z, false, false); \
+        const auto sy_ = __builtin_amdgcn_permlane32_swap(v_.y, v_.w, false, false); \
+        BQMM_GROUP(sx_[0], sy_[0], slot, 0, t, gi_);                                \
+      }                                                                             \
+      BQMM_BIAS(slot, 4);                                                           \
+      _Pragma("unroll") for (int t = 0; t < TT; ++t) {                              \
+        const v4u v_ = tv_[t];                                                      \
+        const auto sx_ = __builtin_amdgcn_permlane32_swap(v_.x, v_.z, false, false); \
+        const auto sy_ = __builtin_amdgcn_permlane32_swap(v_.y, v_.w, false, false); \
+        BQMM_GROUP(sx_[1], sy_[1], slot, 4, t, gi_ + 1u);                           \
+      }                                                                             \
+    } else {                                                                        \
+      BQMM_BIAS(slot, 0);                                                           \
+      _Pragma("unroll") for (int t = 0; t < TT; ++t) {                              \
+        const v4u v_ = tv_[t];                                                      \
+        const auto sx_ = __builtin_amdgcn_permlane32_swap(v_.x, v_.z, false, false); \
+        const auto sy_ = __builtin_amdgcn_permlane32_swap(v_.y, v_.w, false, false); \
+        BQMM_GROUP(pos_ ? sx_[1] : sx_[0], pos_ ? sy_[1] : sy_[0], slot, 0, t, gi_); \
+      }                                                                             \
     }                                                                               \
   } while (0)
 
-  uint32_t gi0 = 0;
-  for (; gi0 + P <= ng; gi0 += P) {
+  uint32_t pi0 = 0;
+  for (; pi0 + P <= npair; pi0 += P) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
-      BQMM_COMPUTEX(u, gi0 + u);
-      BQMM_LOADX(u, gi0 + u + P);
+      BQMM_COMPUTEX(u, pi0 + u);
+      BQMM_LOADX(u, pi0 + u + P);
     }
   }
-  // the last ng - gi0 < P groups are already loaded
+  // the last npair - pi0 < P pairs are already loaded
 #pragma unroll
   for (int u = 0; u < P - 1; ++u)
-    if (gi0 + u < ng) BQMM_COMPUTEX(u, gi0 + u);
+    if (pi0 + u < npair) BQMM_COMPUTEX(u, pi0 + u);
 #undef BQMM_LOADX
 #undef BQMM_COMPUTEX
+#undef BQMM_GROUP
+#undef BQMM_BIAS
 
   // add the W waves' partial sums: red[wave][t][i][lane]
   __syncthreads();  // every wave is done with its scales (the same LDS)
@@ -237,11 +322,12 @@ __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint
 }
 
 // Dynamic LDS of a launch with W waves of T tiles: the staged weight scales
-// of a wave's groups, or the partial sums of the final reduction.
+// of a wave's groups and each wave's 1 KB for the weight loads, or the
+// partial sums of the final reduction.
 inline size_t lds_bytes(int W, int T, int NW, uint32_t k) {
   const uint32_t G = k >> 7;
   const uint32_t gmax = (G + W - 1) / W;
-  const size_t sc_bytes = (size_t)W * NW * 16 * T * gmax * 2;
+  const size_t sc_bytes = (((size_t)W * NW * 16 * T * gmax * 2 + 15) & ~(size_t)15) + (size_t)W * 1024;
   const size_t red_bytes = (size_t)W * NW * T * 4 * 64 * 4;
   return sc_bytes > red_bytes ? sc_bytes : red_bytes;
 }
@@ -307,8 +393,11 @@ inline uint32_t cu_count() {
 #ifndef BQMM_GEMVX_T_FUSED
 #define BQMM_GEMVX_T_FUSED 3
 #endif
+// (The wide launch reaches the plain grid only where it fits the compute units
+// once, one workgroup each, so it no longer needs the 128-VGPR bound that let
+// two of them share a unit.)
 #ifndef BQMM_GEMVX_MINW_WIDE
-#define BQMM_GEMVX_MINW_WIDE 4
+#define BQMM_GEMVX_MINW_WIDE 2
 #endif
 #ifndef BQMM_GEMVX_MINW_NARROW
 #define BQMM_GEMVX_MINW_NARROW 2
@@ -316,20 +405,10 @@ inline uint32_t cu_count() {
 #ifndef BQMM_GEMVX_MINW_FUSED
 #define BQMM_GEMVX_MINW_FUSED 2
 #endif
-// Groups of loads in flight per wave (P): one for the fused and the narrow
-// kernels, two for the wide one.  Measured at m = 4, 6, 8 on the FFN shapes
-// (cold, same-box A/B, identical outputs): one group instead of two made the
-// fused gate/up 2-5% faster and the narrow down 1-1.5% faster, and the wide
-// single-weight kernel 0.5-1% slower.
-#ifndef BQMM_GEMVX_P_WIDE
-#define BQMM_GEMVX_P_WIDE 2
-#endif
-#ifndef BQMM_GEMVX_P_NARROW
-#define BQMM_GEMVX_P_NARROW 1
-#endif
-#ifndef BQMM_GEMVX_P_FUSED
-#define BQMM_GEMVX_P_FUSED 1
-#endif
+// Pairs of groups whose loads are in flight per wave (P): one, for every
+// launch.  (With one group per load, two groups in flight had been the best
+// choice for the wide kernel and one for the others; a pair is two groups.)
+constexpr int kPairsInFlight = 1;
 // The launch shape launch_m picks for (n, k): waves W and tiles per wave T.
 inline void launch_shape(uint32_t n, uint32_t k, int NW, int &W, int &T) {
   if ((k >> 7) >= 8) {
@@ -361,8 +440,7 @@ hipError_t launch_m(const void *act, const void *w, const void *w2, void *out, u
     const int Tp = NW == 2 ? BQMM_GEMVX_T_FUSED : (n >= BQMM_GEMVX_WIDE_N ? BQMM_GEMVX_T_WIDE : BQMM_GEMVX_T_NARROW);
     const uint32_t rb = balanced_rows(n, k, NW, Tp);
     if (rb != 0) {
-      // prefetch depth as in the plain launch: two groups for one weight, one for two
-      constexpr int P = NW == 2 ? 1 : 2;
+      constexpr int P = kPairsInFlight;
       switch ((rb + 15) / 16) {
         case 4: return launch_balanced<M, 4, NW, P>(act, w, w2, out, n, k, rb, s);
         case 5: return launch_balanced<M, 5, NW, P>(act, w, w2, out, n, k, rb, s);
@@ -372,17 +450,17 @@ hipError_t launch_m(const void *act, const void *w, const void *w2, void *out, u
       }
     }
     if constexpr (NW == 2) {
-      return launch_w<M, 8, BQMM_GEMVX_T_FUSED, NW, BQMM_GEMVX_MINW_FUSED, BQMM_GEMVX_P_FUSED>(act, w, w2, out, n,
-                                                                                              k, s);
+      return launch_w<M, 8, BQMM_GEMVX_T_FUSED, NW, BQMM_GEMVX_MINW_FUSED, kPairsInFlight>(act, w, w2, out, n, k,
+                                                                                          s);
     } else {
       if (n >= BQMM_GEMVX_WIDE_N)
-        return launch_w<M, 8, BQMM_GEMVX_T_WIDE, NW, BQMM_GEMVX_MINW_WIDE, BQMM_GEMVX_P_WIDE>(act, w, w2, out, n, k,
-                                                                                           s);
-      return launch_w<M, 8, BQMM_GEMVX_T_NARROW, NW, BQMM_GEMVX_MINW_NARROW, BQMM_GEMVX_P_NARROW>(act, w, w2, out,
-                                                                                                n, k, s);
+        return launch_w<M, 8, BQMM_GEMVX_T_WIDE, NW, BQMM_GEMVX_MINW_WIDE, kPairsInFlight>(act, w, w2, out, n, k,
+                                                                                        s);
+      return launch_w<M, 8, BQMM_GEMVX_T_NARROW, NW, BQMM_GEMVX_MINW_NARROW, kPairsInFlight>(act, w, w2, out, n, k,
+                                                                                            s);
     }
   }
-  return launch_w<M, 1, 2, NW, 1, 2>(act, w, w2, out, n, k, s);
+  return launch_w<M, 1, 2, NW, 1, kPairsInFlight>(act, w, w2, out, n, k, s);
 }
 
 

@@ -165,8 +165,9 @@ int q2_0_gemv_vec(const void *act_bf16, const void *w_q2, void *out_bf16,
  * (v_mfma_f32_16x16x32_bf16, codes and activations exact in bf16, fp32
  * accumulation): a deliberate exception to keeping the GEMV a pure
  * bandwidth kernel, taken because it measured faster at these m.  Where the
- * matrix-core kernel's staged weight scales would exceed 64 KB of LDS in the
- * fused gate/up launch (k above 43008), both calls use the vector kernel. */
+ * matrix-core kernel's LDS (staged weight scales and 1 KB per wave for the
+ * weight loads) would exceed 64 KB in the fused gate/up launch (k above
+ * 37888), both calls use the vector kernel. */
 int q2_0_gemv_vec_batchm(const void *act_bf16, const void *w_q2, void *out_bf16,
                          uint32_t m, uint32_t n, uint32_t k, void *stream);
 

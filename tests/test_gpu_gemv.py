@@ -65,7 +65,7 @@ def test_decode_qkvz_full(gpu):
                                         (1, 300, 30720, 53), (1, 17, 32768, 54),
                                         # m >= 4: the largest k of the matrix-core kernel, and one group
                                         # past it (the vector kernel)
-                                        (4, 300, 43008, 55), (5, 40, 43136, 56), (4, 33, 49152, 57),
+                                        (4, 300, 37888, 55), (5, 40, 38016, 56), (4, 33, 49152, 57),
                                         # m >= 4, balanced rows (one workgroup per compute unit, used
                                         # where the plain grid has more workgroups than units): 4, 5
                                         # and 6 tiles per workgroup, the last tile overlapping the one
@@ -73,7 +73,11 @@ def test_decode_qkvz_full(gpu):
                                         # (the plain launch in more than one round)
                                         (4, 12288 + 1, 1152, 58), (8, 16384 + 77, 1024, 59),
                                         (5, 20480 + 1, 1152, 60), (6, 24576, 1024, 61),
-                                        (7, 24576 + 100, 1152, 62)])
+                                        (7, 24576 + 100, 1152, 62),
+                                        # m >= 4 with one wave (fewer than eight groups): one group
+                                        # (its pair load reads the group twice), two, and three (a
+                                        # pair and a single group)
+                                        (4, 20, 128, 63), (5, 17, 256, 64), (8, 9, 384, 65)])
 def test_ragged(gpu, m, n, k, seed):
     g = inputs.rng(seed)
     w = inputs.q2_0_weight(g, n, k)
@@ -229,7 +233,7 @@ def _chain_bits(gpu, act, wg, wu, m, n, k):
                                         (4, 33, 17408, 44), (8, 17408, 5120, 46), (6, 300, 1152, 47),
                                         (7, 40, 512, 48), (3, 33, 9216, 49), (2, 5, 128, 50),
                                         # the matrix-core kernel's largest k, and the vector kernel past it
-                                        (4, 40, 43008, 51), (4, 40, 49152, 52), (8, 20, 43136, 53),
+                                        (4, 40, 37888, 51), (4, 40, 49152, 52), (8, 20, 38016, 53),
                                         # balanced rows: four tiles for both kernels; then six tiles
                                         # for the single GEMV and the plain launch for the fused one
                                         (4, 12288 + 1, 1152, 54), (6, 20480 + 1, 1024, 55)])

@@ -217,7 +217,7 @@ def verify_leg(bq, dev, Wcopies, act, m, H, I):
 
     wg, wu, wd = Wcopies[0]
     work = wg.numel() + wu.numel() + wd.numel() + m * (6 * H + 12 * I)
-    kname = (f"q2_0_gemv_mfma_kernel<{m}> x3 + silu_mul" if m >= 4 else
+    kname = (f"q2_0_gemv_mfma_kernel<{m}> x3 + silu_mul" if m >= 3 else
              f"q2_0_gemvp_kernel<{m}> gate, up + silu_mul + q2_0_gemvm_kernel<{m}> down")
     keep = [t for c in Wcopies for t in c] + [x, g_, u_, o_]
     return Leg(f"verify_ffn_m{m}", fn, keep, 4, work, "GB/s", kname, HBM_PEAK_GBS, "hbm")
@@ -238,7 +238,7 @@ def verify_fused_leg(bq, dev, Wcopies, act, m, H, I):
 
     wg, wu, wd = Wcopies[0]
     work = wg.numel() + wu.numel() + wd.numel() + m * (2 * H + 4 * I)
-    kname = (f"q2_0_gemv_mfma_kernel<{m}> gate+up+silu, q2_0_gemv_mfma_kernel<{m}> down" if m >= 4 else
+    kname = (f"q2_0_gemv_mfma_kernel<{m}> gate+up+silu, q2_0_gemv_mfma_kernel<{m}> down" if m >= 3 else
              f"q2_0_gemvp_kernel<{m}> gate+up+silu, q2_0_gemvm_kernel<{m}> down")
     keep = [t for c in Wcopies for t in c] + [x, h_, o_]
     return Leg(f"verify_ffn_fused_m{m}", fn, keep, 2, work, "GB/s", kname, HBM_PEAK_GBS, "hbm")

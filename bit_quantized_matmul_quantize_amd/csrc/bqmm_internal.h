@@ -93,7 +93,7 @@ inline hipError_t device_cu_count(int *cus) {
 // Batch size from which the batched Q2_0 GEMV (single and fused gate/up) runs
 // on matrix cores rather than on the vector ALU; both sources dispatch on it.
 #ifndef BQMM_GEMV_MIN_M_MFMA
-#define BQMM_GEMV_MIN_M_MFMA 4
+#define BQMM_GEMV_MIN_M_MFMA 3
 #endif
 
 // ---- launchers (one per kernel source) ------------------------------------

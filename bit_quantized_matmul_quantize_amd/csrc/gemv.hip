@@ -796,10 +796,11 @@ hipError_t launch_gemvm_gate_up(const void *act, const void *wg, const void *wu,
 #define BQMM_GEMVP_M1_MIN_K 4096
 #endif
 
-// The whole-vector kernel serves m <= 3 where its LDS fits (and m = 1 from
-// BQMM_GEMVP_M1_MIN_K on); the single and fused dispatch make the same choice.
+// The whole-vector kernel serves m <= 3 below the matrix-core threshold where
+// its LDS fits (and m = 1 from BQMM_GEMVP_M1_MIN_K on); the single and fused
+// dispatch make the same choice.
 inline bool use_gemvp(uint32_t m, uint32_t k) {
-  if (!BQMM_GEMVP_ENABLE || m > 3) return false;
+  if (!BQMM_GEMVP_ENABLE || m > 3 || m >= kMinMMfma) return false;
   if (m == 1 && k < BQMM_GEMVP_M1_MIN_K) return false;
   return gemvp_lds_bytes(m, k) <= kMaxLdsP;
 }
@@ -817,7 +818,11 @@ hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t 
     switch (m) {
       case 1: return launch_gemvp<1, 1>(act, w, nullptr, out, n, k, s);
       case 2: return launch_gemvp<2, 1>(act, w, nullptr, out, n, k, s);
+#if BQMM_GEMV_MIN_M_MFMA > 3
       default: return launch_gemvp<3, 1>(act, w, nullptr, out, n, k, s);
+#else
+      default: return hipErrorInvalidValue;  // m = 3 runs on the matrix-core kernel
+#endif
     }
   }
   if (m == 1 && k <= kMaxK1) {
@@ -832,10 +837,13 @@ hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t 
                        static_cast<uint16_t *>(out), n, k);
     return hipGetLastError();
   }
-  // From m = 4 on the per-code multiply-adds outweigh the code unpacking and
-  // the matrix-core kernel is faster (its staged scales bound k); measured on
-  // the FFN shapes, m = 4 is about even on gate/up and 7% faster on down,
-  // m = 5 20-30% faster.
+  // From m = 3 on the per-code multiply-adds outweigh the code unpacking and
+  // the matrix-core kernel is faster (its LDS bounds k).  Measured on the FFN
+  // shapes (same-box A/B, cold): at m = 3 down [5120, 17408] 20.9 -> 15.0 us
+  // and gate [17408, 5120] 14.0 -> 12.0 us, the fused gate/up 23.0 -> 23.5 us
+  // (2% slower, but it has to take the single call's kernel); at m = 2 the
+  // vector kernels stay ahead (gate 11.4 against 11.8 us, down 13.4 against
+  // 14.5, fused 17.3 against 23.1).
   if (use_gemv_mfma(m, n, k)) return launch_q2_0_gemv_mfma(act, w, out, m, n, k, s);
   switch (m) {
     case 1: return launch_gemvm<1>(act, w, out, n, k, s);
@@ -859,7 +867,11 @@ hipError_t launch_q2_0_gemv_gate_up_silu(const void *act, const void *w_gate, co
     switch (m) {
       case 1: return launch_gemvp<1, 2>(act, w_gate, w_up, out, n, k, s);
       case 2: return launch_gemvp<2, 2>(act, w_gate, w_up, out, n, k, s);
+#if BQMM_GEMV_MIN_M_MFMA > 3
       default: return launch_gemvp<3, 2>(act, w_gate, w_up, out, n, k, s);
+#else
+      default: return hipErrorInvalidValue;  // m = 3 runs on the matrix-core kernel
+#endif
     }
   }
   if (use_gemv_mfma(m, n, k))

@@ -71,8 +71,6 @@
 // ([group][row], so one 8-byte read gives the four rows of a lane's
 // outputs).  Loads run P pairs of groups ahead, unconditionally from clamped
 // addresses.
-#include <atomic>
-
 #include "gemv_common.h"
 
 namespace bqmm {
@@ -366,19 +364,6 @@ hipError_t launch_balanced(const void *act, const void *w, const void *w2, void 
   return hipGetLastError();
 }
 
-// Compute units of the current device (queried once per device).
-inline uint32_t cu_count() {
-  static std::atomic<int> cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int v = cus[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 0) v = 0;
-    cus[dev].store(v, std::memory_order_relaxed);
-  }
-  return (uint32_t)v;
-}
-
 // Eight waves split k when it has at least eight groups (W <= G is required).
 // The tiles per wave and the register bound (minimum waves per SIMD) are set
 // per case below.  The fused gate/up kernel takes T tiles of each weight (the
@@ -425,8 +410,10 @@ inline void launch_shape(uint32_t n, uint32_t k, int NW, int &W, int &T) {
 // or the balanced tile count is outside 4..6 (4..5 for two weights: six tiles
 // of each spill registers), or its LDS does not fit.
 inline uint32_t balanced_rows(uint32_t n, uint32_t k, int NW, int T) {
-  const uint32_t ncu = cu_count();
-  if (ncu == 0 || (n + 16u * T - 1) / (16u * T) <= ncu) return 0;
+  int cus = 0;
+  if (device_cu_count(&cus) != hipSuccess || cus <= 0) return 0;
+  const uint32_t ncu = (uint32_t)cus;
+  if ((n + 16u * T - 1) / (16u * T) <= ncu) return 0;
   const uint32_t rb = (n + ncu - 1) / ncu, tb = (rb + 15) / 16;
   if (tb < 4 || tb > (NW == 2 ? 5u : 6u) || lds_bytes(8, (int)tb, NW, k) > kMaxLds) return 0;
   return rb;
@@ -471,6 +458,12 @@ hipError_t launch_any_m(const void *act, const void *w, const void *w2, void *ou
                         uint32_t k, hipStream_t s) {
   if (m < (uint32_t)BQMM_GEMV_MIN_M_MFMA) return hipErrorInvalidValue;
   switch (m) {
+#if BQMM_GEMV_MIN_M_MFMA <= 2
+    case 2: return launch_m<2, NW>(act, w, w2, out, n, k, s);
+#endif
+#if BQMM_GEMV_MIN_M_MFMA <= 3
+    case 3: return launch_m<3, NW>(act, w, w2, out, n, k, s);
+#endif
 #if BQMM_GEMV_MIN_M_MFMA <= 4
     case 4: return launch_m<4, NW>(act, w, w2, out, n, k, s);
 #endif

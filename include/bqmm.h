@@ -159,8 +159,8 @@ int q2_0_gemv_vec(const void *act_bf16, const void *w_q2, void *out_bf16,
  * out [m][n] bf16.  [page layers/dense_ffn_decode_batch.rs, fn forward_km_q2:
  *  q2_0_gemv_vec_batchm(inp, w, out, m).]  m > 8 -> BQ_EUNSUPPORTED.
  * Group 128; k % 128 == 0.
- * Kernels: m = 1..3 run on the vector ALU only (packed bf16 dot products, no
- * matrix cores).  From m = 4 on, where the per-code multiply-adds outweigh
+ * Kernels: m = 1, 2 run on the vector ALU only (packed bf16 dot products, no
+ * matrix cores).  From m = 3 on, where the per-code multiply-adds outweigh
  * the code unpacking, the products run on bf16 matrix cores
  * (v_mfma_f32_16x16x32_bf16, codes and activations exact in bf16, fp32
  * accumulation): a deliberate exception to keeping the GEMV a pure

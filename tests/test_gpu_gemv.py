@@ -41,19 +41,20 @@ def test_decode_qkvz_full(gpu):
                                         (1, 100, 17408, 30),    # m=1: prep loop over 1088 items
                                         (1, 3, 33792, 31),      # m=1 beyond the LDS-staged kernel's k
                                         (1, 4096 + 37, 2048, 32),
-                                        # vector batched kernel (m <= 3), wide launch shape (n >= 8192):
+                                        # m = 2, 3 on wide outputs (n >= 8192; m = 3 on matrix cores):
                                         (2, 8192 + 45, 1152, 33),   # two slices, the second ragged
                                         (3, 9000, 384, 34),         # one slice, fewer than the prefetch depth
                                         (3, 8192, 4096, 35),        # one full prefetch round plus one slice
                                         (1, 8192 + 5, 36864, 36),   # m=1 beyond the decode kernel's k
-                                        (4, 9, 65536 + 1024, 37),   # m >= 4 beyond the matrix-core kernel's k
-                                        # matrix-core kernel (m >= 4): one wave per group range
+                                        (4, 9, 65536 + 1024, 37),   # m >= 3 beyond the matrix-core kernel's k
+                                        # matrix-core kernel (m >= 3): one wave per group range
                                         (6, 100, 512, 39), (6, 8192 + 16, 2048, 40),
                                         (4, 8192 + 16, 2048, 41),   # wide: 3 tiles per wave, last workgroup ragged
                                         (5, 1000, 1024, 42),        # narrow: 2 tiles per wave, ragged
                                         (4, 151, 1152, 43),
-                                        # whole-vector kernel (m <= 3): shortest k, and the largest
+                                        # whole-vector kernel (m = 1, 2): shortest k, and the largest
                                         # k whose activations fit its LDS for each m, and one past it
+                                        # (m = 3 at those shapes runs on the matrix-core kernel)
                                         (2, 5, 128, 44), (3, 49, 256, 45), (1, 77, 28672, 46),
                                         (2, 65, 13312, 47), (3, 33, 9216, 48), (2, 33, 13440, 49),
                                         (1, 4096 + 16, 4096, 50),
@@ -63,10 +64,11 @@ def test_decode_qkvz_full(gpu):
                                         # m=1 decode kernel with more than 64 KB of staged activations
                                         # (k past the whole-vector kernel's LDS, up to its own limit)
                                         (1, 300, 30720, 53), (1, 17, 32768, 54),
-                                        # m >= 4: the largest k of the matrix-core kernel, and one group
+                                        # m >= 3: the largest k of the matrix-core kernel, and one group
                                         # past it (the vector kernel)
                                         (4, 300, 37888, 55), (5, 40, 38016, 56), (4, 33, 49152, 57),
-                                        # m >= 4, balanced rows (one workgroup per compute unit, used
+                                        (3, 40, 37888, 66), (3, 40, 38016, 67),
+                                        # m >= 3, balanced rows (one workgroup per compute unit, used
                                         # where the plain grid has more workgroups than units): 4, 5
                                         # and 6 tiles per workgroup, the last tile overlapping the one
                                         # before it, the last workgroup ragged; then past six tiles
@@ -74,10 +76,11 @@ def test_decode_qkvz_full(gpu):
                                         (4, 12288 + 1, 1152, 58), (8, 16384 + 77, 1024, 59),
                                         (5, 20480 + 1, 1152, 60), (6, 24576, 1024, 61),
                                         (7, 24576 + 100, 1152, 62),
-                                        # m >= 4 with one wave (fewer than eight groups): one group
+                                        # m >= 3 with one wave (fewer than eight groups): one group
                                         # (its pair load reads the group twice), two, and three (a
                                         # pair and a single group)
-                                        (4, 20, 128, 63), (5, 17, 256, 64), (8, 9, 384, 65)])
+                                        (4, 20, 128, 63), (5, 17, 256, 64), (8, 9, 384, 65),
+                                        (3, 20, 128, 68), (3, 12288 + 1, 1152, 69)])
 def test_ragged(gpu, m, n, k, seed):
     g = inputs.rng(seed)
     w = inputs.q2_0_weight(g, n, k)

@@ -48,10 +48,13 @@
 // Work split: a wave owns T tiles of 16 rows and a contiguous range of the
 // 128-groups; the W waves of a workgroup split k between them and add their
 // partial sums through LDS at the end.  The T tiles share each activation
-// load, which is what limits this kernel, so T is as large as the launch
-// allows: the grid must fit the compute units in one round (a second, partial
-// round of these latency-bound waves nearly doubles the time).  Measured on
-// the FFN shapes at m = 8: wide single (n = 17408) T = 3 within 128 VGPRs, so
+// load (four per group and lane; with two tiles, on the down projection, a
+// timing copy that issued half of them ran 13% faster at m = 8, with five no
+// faster), so T is as large as the launch allows: the grid must fit the
+// compute units in one round (a second, partial round of these
+// latency-bound waves nearly doubles the time).  Measured on the FFN shapes
+// at m = 8 with the one-group loads: wide single (n = 17408) T = 3 within
+// 128 VGPRs, so
 // two 8-wave workgroups share a CU and all 363 fit at once (20.4 us, was 25.4
 // with T = 2 at 134 VGPRs, one workgroup per CU and 544 of them); narrow
 // (n = 5120) T = 2, 160 workgroups (24.7 us, was 31.2 with T = 1); fused
@@ -63,7 +66,8 @@
 // tiles, the last one starting at row rb - 16 so that it overlaps its
 // neighbour inside the workgroup (no row is loaded by two workgroups; the
 // overlapped rows are stored once).  Same-box A/B, m = 4 / 6 / 8, identical
-// outputs: gate 17.0 / 17.7 / 19.2 -> 14.7 / 15.2 / 15.9 us, fused gate/up
+// outputs (with the one-group loads of that time): gate 17.0 / 17.7 / 19.2 ->
+// 14.7 / 15.2 / 15.9 us, fused gate/up
 // 29.8 / 30.9 / 32.5 -> 27.1 / 27.8 / 28.6 us.  The narrow down projection
 // (160 workgroups, one per unit) gains nothing from it: split into 256
 // workgroups of 20 rows it measured 2% slower.  There is no barrier in the
@@ -110,13 +114,13 @@ __global__ __launch_bounds__(64 * W, MINW) void q2_0_gemv_mfma_kernel(const uint
   // rb rows per workgroup (16 <= rb <= 16 T); tile t starts at row min(16 t, rb - 16)
   const uint32_t row0 = blockIdx.x * rb;
 
-  // weight bytes 8 lg .. +7 of each 128-group of this lane's rows (rows past n
-  // read row n - 1 and are not stored); slots T .. 2T-1 are the up rows
+  // Weight loads: lane l takes row l / 4 of each tile and 16-byte chunk l % 4
+  // of a pair of groups (four consecutive lanes on 64 contiguous bytes of a
+  // row; with a single group per row, chunk l % 2 of it).  Rows past n read
+  // row n - 1 and are not stored; slots T .. 2T-1 are the up rows.
   const uint8_t *wp[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    // loads: lane l takes row l / 4 of the tile, 16-byte chunk l % 4 of the
-    // pair (four consecutive lanes on 64 contiguous bytes of a row)
     const uint32_t row = min(row0 + min(16u * (t % T), rb - 16u) + (lane >> 2), n - 1u);
     wp[t] = (t < T ? w : w2) + (uint64_t)row * (k >> 2) + 16u * (G >= 2 ? (lane & 3u) : (lane & 1u));
   }

@@ -839,7 +839,7 @@ hipError_t launch_q2_0_gemv(const void *act, const void *w, void *out, uint32_t 
   }
   // From m = 3 on the per-code multiply-adds outweigh the code unpacking and
   // the matrix-core kernel is faster (its LDS bounds k).  Measured on the FFN
-  // shapes (same-box A/B, cold): at m = 3 down [5120, 17408] 20.9 -> 15.0 us
+  // shapes (A/B on one machine, cold): at m = 3 down [5120, 17408] 20.9 -> 15.0 us
   // and gate [17408, 5120] 14.0 -> 12.0 us, the fused gate/up 23.0 -> 23.5 us
   // (2% slower, but it has to take the single call's kernel); at m = 2 the
   // vector kernels stay ahead (gate 11.4 against 11.8 us, down 13.4 against

@@ -28,8 +28,8 @@
 // load to the MFMA layout through 1 KB of LDS (one 16-byte store and one load
 // per lane, conflict-free) and then one v_permlane32_swap per dword splits
 // the pair into the two groups' A words.  Against the earlier loads of one
-// group per instruction, 8 bytes per lane on 16 rows x 32 bytes (same-box
-// A/B at m = 4 / 6 / 8, identical results between the two new versions):
+// group per instruction, 8 bytes per lane on 16 rows x 32 bytes (A/B on one
+// machine at m = 4 / 6 / 8, identical results between the two new versions):
 // the pair loads alone took the down projection [5120, 17408] from 19.1 /
 // 20.3 / 22.7 to 16.9 / 18.0 / 20.4 us; with four consecutive lanes per row
 // segment (instead of lanes 16 apart) to 14.9 / 15.4 / 17.6 us; the gate
@@ -65,7 +65,7 @@
 // rb = ceil(n / CUs) rows (68 for n = 17408 on 256 units) in T = ceil(rb / 16)
 // tiles, the last one starting at row rb - 16 so that it overlaps its
 // neighbour inside the workgroup (no row is loaded by two workgroups; the
-// overlapped rows are stored once).  Same-box A/B, m = 4 / 6 / 8, identical
+// overlapped rows are stored once).  A/B on one machine, m = 4 / 6 / 8, identical
 // outputs (with the one-group loads of that time): gate 17.0 / 17.7 / 19.2 ->
 // 14.7 / 15.2 / 15.9 us, fused gate/up
 // 29.8 / 30.9 / 32.5 -> 27.1 / 27.8 / 28.6 us.  The narrow down projection

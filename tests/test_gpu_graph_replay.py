@@ -146,3 +146,41 @@ def test_concurrent_streams_match_eager(gpu):
         a = v.view(torch.uint8) if v.dtype != torch.uint8 else v
         b = eager[key].view(torch.uint8) if eager[key].dtype != torch.uint8 else eager[key]
         assert torch.equal(a, b), f"{key} differs from the eager result"
+
+
+def test_graph_replays_balanced_gemv(gpu):
+    # The batched GEMV's balanced launch (one workgroup of ceil(n / units) rows
+    # per compute unit, its LDS attribute set on first use), single and fused,
+    # captured after an eager run and replayed three times.
+    g = inputs.rng(93)
+    m, n, k = 8, 12288 + 1, 1024
+    x = dev_bf16(inputs.activations(g, m, k, outliers=True), gpu)
+    wg, wu = dev_u8(inputs.q2_0_weight(g, n, k), gpu), dev_u8(inputs.q2_0_weight(g, n, k), gpu)
+    single, fused = empty_bf16((m, n), gpu), empty_bf16((m, n), gpu)
+
+    def run():
+        bq.q2_0_gemv_vec_batchm(x, wg, single, m, n, k)
+        bq.q2_0_gemv_gate_up_silu(x, wg, wu, fused, m, n, k)
+
+    run()
+    torch.cuda.synchronize()
+    eager = (single.clone(), fused.clone())
+    assert torch.count_nonzero(eager[0].view(torch.int16)) > 0
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        single.zero_()
+        fused.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(single.view(torch.int16), eager[0].view(torch.int16)), f"replay {rep}: single"
+        assert torch.equal(fused.view(torch.int16), eager[1].view(torch.int16)), f"replay {rep}: fused"

@@ -249,7 +249,7 @@ def test_fused_gate_up_equals_chain(gpu, m, n, k, seed):
     assert np.array_equal(_fused(gpu, act, wg, wu, m, n, k), _chain_bits(gpu, act, wg, wu, m, n, k))
 
 
-@pytest.mark.parametrize("m", [1, 2, 6, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 6, 8])
 def test_fused_gate_up_ffn_chain(gpu, ffn, m):
     # the verify FFN with the fused first stage, end to end against the oracle's
     # chain (bf16 roundings at the same points)

@@ -394,10 +394,14 @@ hipError_t launch_balanced(const void *act, const void *w, const void *w2, void 
 #ifndef BQMM_GEMVX_MINW_FUSED
 #define BQMM_GEMVX_MINW_FUSED 2
 #endif
-// Pairs of groups whose loads are in flight per wave (P): one, for every
-// launch.  (With one group per load, two groups in flight had been the best
-// choice for the wide kernel and one for the others; a pair is two groups.)
+// Pairs of groups whose loads are in flight per wave (P): one, except on the
+// narrow launch (two tiles per wave), where two pairs measured 1-4% faster at
+// m = 3, 4, 8 on the down projection; on the five-tile gate two pairs were 8%
+// slower and the fused kernel spills with them.  (With one group per load, two
+// groups in flight had been the best choice for the wide kernel.)  The depth
+// does not change the order of any sum.
 constexpr int kPairsInFlight = 1;
+constexpr int kPairsInFlightNarrow = 2;
 // The launch shape launch_m picks for (n, k): waves W and tiles per wave T.
 inline void launch_shape(uint32_t n, uint32_t k, int NW, int &W, int &T) {
   if ((k >> 7) >= 8) {
@@ -447,8 +451,8 @@ hipError_t launch_m(const void *act, const void *w, const void *w2, void *out, u
       if (n >= BQMM_GEMVX_WIDE_N)
         return launch_w<M, 8, BQMM_GEMVX_T_WIDE, NW, BQMM_GEMVX_MINW_WIDE, kPairsInFlight>(act, w, w2, out, n, k,
                                                                                         s);
-      return launch_w<M, 8, BQMM_GEMVX_T_NARROW, NW, BQMM_GEMVX_MINW_NARROW, kPairsInFlight>(act, w, w2, out, n, k,
-                                                                                            s);
+      return launch_w<M, 8, BQMM_GEMVX_T_NARROW, NW, BQMM_GEMVX_MINW_NARROW, kPairsInFlightNarrow>(act, w, w2, out,
+                                                                                                  n, k, s);
     }
   }
   return launch_w<M, 1, 2, NW, 1, kPairsInFlight>(act, w, w2, out, n, k, s);
